@@ -1,0 +1,164 @@
+"""Budget allocation and selection (oracle; exact integer budgets; test infrastructure only).
+
+Ordering rule used everywhere: a larger score ranks first; equal scores rank by
+the smaller flat index g*p + k (within one head: the smaller token index).
+-0.0 equals +0.0.  The pages leave ties open; this is the deterministic reading.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+
+def rank_order(x: np.ndarray) -> np.ndarray:
+    """Indices of a 1-D score vector from best to worst: by (-score, index)."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    return np.lexsort((np.arange(x.size), -x))
+
+
+def top_indices(x: np.ndarray, k: int) -> np.ndarray:
+    return rank_order(x)[:k]
+
+
+def safeguard_budgets(counts: Sequence[int], total: int, alpha: Tuple[int, int]) -> np.ndarray:
+    """Ada-KV safeguard, integer form.
+
+    Ada-KV notes, Algorithm 2, step 8: the final budget of head i is
+    alpha * B_i* + (1 - alpha) * B / h, with B the prefix budget and h the
+    number of KV heads.  With alpha = a/b every head's real budget is
+    N_g / Den, N_g = a*h*f_g + (b - a)*B, Den = b*h.  The integer budgets are
+    the floors plus one extra unit for the heads with the largest remainders
+    (equal remainders: the lower head first), so they sum to B exactly.
+    """
+    a, b = int(alpha[0]), int(alpha[1])
+    if not (0 <= a <= b and b > 0):
+        raise ValueError("alpha must be a/b with 0 <= a <= b, b > 0")
+    h = len(counts)
+    den = b * h
+    num = [a * h * int(f) + (b - a) * int(total) for f in counts]
+    q = [x // den for x in num]
+    r = [x % den for x in num]
+    deficit = int(total) - sum(q)
+    assert 0 <= deficit < max(h, 1) or h == 0
+    for g in sorted(range(h), key=lambda g: (-r[g], g))[:deficit]:
+        q[g] += 1
+    return np.asarray(q, dtype=np.int64)
+
+
+def ada_allocate(score: np.ndarray, budget: int, w: int, alpha: Tuple[int, int] = (1, 5)) -> Dict:
+    """Ada-KV allocation and per-head top-k for one layer instance.
+
+    Ada-KV notes, Algorithm 1 (concatenate all heads' weights, take the top B,
+    count per head) inside Algorithm 2: step 6 removes the window from the
+    budget (B - winsize * h, h = KV heads because entries are stored per KV
+    head), step 7 runs Algorithm 1, step 8 applies the safeguard, step 9 takes
+    each head's top-B_i (Theorem 3.2), steps 10-11 keep those entries, in
+    ascending token order, followed by the window.
+    score: [Hkv, p] float (>= 0).  Returns dict with P, counts f, budgets, sel.
+    """
+    score = np.asarray(score, dtype=np.float64)
+    hkv, p = score.shape
+    P = int(budget) - w * hkv
+    if P < 0 or P > hkv * p:
+        raise ValueError("budget outside [w*Hkv, n*Hkv]")
+    top = top_indices(score.ravel(), P)
+    counts = np.bincount(top // p, minlength=hkv).astype(np.int64)
+    budgets = safeguard_budgets(counts, P, alpha)
+    sel = [np.sort(top_indices(score[g], int(budgets[g]))) for g in range(hkv)]
+    return {"P": P, "counts": counts, "budgets": budgets, "sel": sel}
+
+
+def layer_entropy(s: np.ndarray) -> float:
+    """LAVa layer uncertainty: entropy of the normalised scores divided by the
+    number of entries (LAVa notes, "基于不确定性的层预算分配"), natural log,
+    0 * log 0 = 0.  An all-zero layer has entropy 0."""
+    s = np.asarray(s, dtype=np.float64).ravel()
+    tot = s.sum()
+    if tot <= 0:
+        return 0.0
+    sh = s / tot
+    nz = sh > 0
+    return float(-(sh[nz] * np.log(sh[nz])).sum() / s.size)
+
+
+def largest_remainder(x: np.ndarray, total: int) -> np.ndarray:
+    """Integers summing to `total`: floors of x plus one for the largest
+    fractional parts (equal parts: lower index first)."""
+    x = np.asarray(x, dtype=np.float64)
+    fl = np.floor(x).astype(np.int64)
+    deficit = int(total) - int(fl.sum())
+    rem = x - fl
+    order = np.lexsort((np.arange(x.size), -rem))
+    fl[order[:deficit]] += 1
+    return fl
+
+
+def lava_layer_budgets(scores: np.ndarray, total: int, w: int) -> Tuple[np.ndarray, np.ndarray]:
+    """LAVa dynamic layer budgets.
+
+    LAVa notes, "基于不确定性的层预算分配" and the quick summary: the total
+    budget is split across layers in proportion to e_l.  Windows are kept
+    outside the split: B' = total - L * w * Hkv is what the layers share.  If
+    every layer has zero entropy the split is uniform.  B' must not exceed one
+    layer's prefix entries (Hkv * p): then no layer's share can overflow it.
+    scores: [L, Hkv, p] pooled prefix scores.  Returns (budgets [L], e [L]).
+    """
+    L, hkv, p = scores.shape
+    Bp = int(total) - L * w * hkv
+    if Bp < 0 or Bp > hkv * p:
+        raise ValueError("LAVa total budget out of range")
+    e = np.array([layer_entropy(scores[l]) for l in range(L)])
+    E = e.sum()
+    x = Bp * e / E if E > 0 else np.full(L, Bp / L)
+    return largest_remainder(x, Bp), e
+
+
+def lava_allocate(scores: np.ndarray, total: int, w: int) -> Dict:
+    """LAVa layer-wise eviction with dynamic head budgets.
+
+    LAVa notes, "动态头预算的逐层缓存驱逐": the scores of all heads in a layer
+    are flattened into one array and the layer's B_l best entries are kept, so
+    head budgets follow from the ranking; no safeguard is applied.
+    Returns dict with layer budgets, e, per-layer head budgets [L, Hkv], sel[l][g].
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    L, hkv, p = scores.shape
+    bl, e = lava_layer_budgets(scores, total, w)
+    budgets = np.zeros((L, hkv), dtype=np.int64)
+    sel: List[List[np.ndarray]] = []
+    for l in range(L):
+        top = top_indices(scores[l].ravel(), int(bl[l]))
+        budgets[l] = np.bincount(top // p, minlength=hkv)
+        sel.append([np.sort(top[top // p == g] % p) for g in range(hkv)])
+    return {"layer_budgets": bl, "entropy": e, "budgets": budgets, "sel": sel}
+
+
+def criticalkv_allocate(score: np.ndarray, composite: np.ndarray, budget: int, w: int,
+                        alpha: Tuple[int, int] = (1, 5), ck: Tuple[int, int] = (1, 2)) -> Dict:
+    """CriticalKV two-stage selection on Ada-KV budgets.
+
+    CriticalKV notes, "两阶段贪心选择算法": per head, stage 1 keeps the top
+    b' = alpha_ck * b entries by attention, stage 2 keeps the top
+    b'' = (1 - alpha_ck) * b of the remaining entries by the composite score.
+    "作为通用插件融入现有驱逐流水线": only the selection changes; the budgets are
+    Ada-KV's, computed on the attention score.  b' is rounded down.
+    """
+    base = ada_allocate(score, budget, w, alpha)
+    hkv, p = score.shape
+    c0, c1 = int(ck[0]), int(ck[1])
+    sel, s1, s2 = [], [], []
+    for g in range(hkv):
+        b = int(base["budgets"][g])
+        b1 = (b * c0) // c1
+        b2 = b - b1
+        first = top_indices(score[g], b1)
+        rest = np.setdiff1d(np.arange(p), first, assume_unique=True)   # ascending
+        second = rest[top_indices(np.asarray(composite[g])[rest], b2)]
+        s1.append(np.sort(first))
+        s2.append(np.sort(second))
+        sel.append(np.sort(np.concatenate([first, second])))
+    out = dict(base)
+    out.update({"sel": sel, "stage1": s1, "stage2": s2})
+    return out

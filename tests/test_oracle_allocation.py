@@ -1,0 +1,277 @@
+"""Pins for the oracle's allocation and selection (CPU): hand-worked fixtures,
+exact rational arithmetic, Theorem 3.2 and Theorem 3.3 of the Ada-KV notes by
+brute force, closed forms and invariants."""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.stats
+
+from oracle import allocation
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _parse_sel(tokens):
+    heads, cur = [], []
+    for t in tokens:
+        if t == "|":
+            heads.append(cur)
+            cur = []
+        else:
+            cur.append(int(t))
+    heads.append(cur)
+    return heads
+
+
+def load_alg1():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "alg1_hand_example.txt")) if l.strip() and not l.startswith("#")]
+    d = {"cases": []}
+    for r in rows:
+        if r[0] == "scores":
+            d["scores"] = np.array([float(x) for x in r[1:]])
+        elif r[0] in ("heads", "w", "budget"):
+            d[r[0]] = int(r[1])
+        elif r[0] == "counts":
+            d["counts"] = [int(x) for x in r[1:]]
+        elif r[0] == "alpha":
+            a, b = int(r[1]), int(r[2])
+            i = r.index("budgets")
+            j = r.index("sel")
+            d["cases"].append(((a, b), [int(x) for x in r[i + 1:j]], _parse_sel(r[j + 1:])))
+    return d
+
+
+def check_alg1_fixture(fn) -> bool:
+    g = load_alg1()
+    s = g["scores"].reshape(g["heads"], -1)
+    for alpha, budgets, sel in g["cases"]:
+        out = fn(s, g["budget"], g["w"], alpha)
+        if list(out["counts"]) != g["counts"] or list(out["budgets"]) != budgets:
+            return False
+        if [list(x) for x in out["sel"]] != sel:
+            return False
+    return True
+
+
+def test_alg1_hand_example():
+    assert check_alg1_fixture(allocation.ada_allocate)
+
+
+def test_ck_hand_example():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "ck_hand_example.txt")) if l.strip() and not l.startswith("#")]
+    att = comp = None
+    for r in rows:
+        if r[0] == "attention":
+            att = np.array([float(x) for x in r[1:]])[None]
+        elif r[0] == "composite":
+            comp = np.array([float(x) for x in r[1:]])[None]
+        elif r[0] == "w":
+            w = int(r[1])
+        elif r[0] == "budget":
+            budget = int(r[1])
+        elif r[0] == "ck":
+            ck = (int(r[1]), int(r[2]))
+            want = [int(x) for x in r[4:]]
+            out = allocation.criticalkv_allocate(att, comp, budget, w, (1, 5), ck)
+            assert list(out["sel"][0]) == want, ck
+
+
+def safeguard_fraction(counts, total, alpha):
+    """alpha*f + (1-alpha)*P/h in exact rationals, then largest remainder."""
+    a = Fraction(alpha[0], alpha[1])
+    h = len(counts)
+    x = [a * f + (1 - a) * Fraction(total, h) for f in counts]
+    fl = [math.floor(v) for v in x]
+    rem = [v - f for v, f in zip(x, fl)]
+    for g in sorted(range(h), key=lambda g: (-rem[g], g))[:total - sum(fl)]:
+        fl[g] += 1
+    return fl
+
+
+def check_safeguard(fn) -> bool:
+    r = np.random.default_rng(11)
+    for _ in range(300):
+        h = int(r.integers(1, 9))
+        p = int(r.integers(1, 50))
+        f = r.multinomial(int(r.integers(0, h * p + 1)), np.ones(h) / h)
+        f = np.minimum(f, p)
+        P = int(f.sum())
+        alpha = [(1, 5), (0, 1), (1, 1), (1, 2), (3, 7)][int(r.integers(0, 5))]
+        if list(fn(f, P, alpha)) != safeguard_fraction(list(f), P, alpha):
+            return False
+    return True
+
+
+def test_safeguard_matches_exact_rationals():
+    assert check_safeguard(allocation.safeguard_budgets)
+
+
+def test_budget_invariants_random():
+    r = np.random.default_rng(12)
+    for t in range(60):
+        hkv, p, w = int(r.integers(1, 9)), int(r.integers(1, 40)), int(r.integers(0, 4))
+        s = r.random((hkv, p)) ** int(r.integers(1, 8))
+        if t % 5 == 0:
+            s = np.round(s, 1)                       # many ties
+        P = int(r.integers(0, hkv * p + 1))
+        out = allocation.ada_allocate(s, P + w * hkv, w, (1, 5))
+        b = out["budgets"]
+        assert b.sum() == P and np.all(b >= 0) and np.all(b <= p)
+        assert out["counts"].sum() == P
+        for g in range(hkv):
+            assert len(out["sel"][g]) == b[g] and np.all(np.diff(out["sel"][g]) > 0)
+
+
+def test_alpha_zero_is_uniform_and_alpha_one_is_counts():
+    r = np.random.default_rng(13)
+    s = r.random((5, 30)) ** 4
+    P = 47
+    u = allocation.ada_allocate(s, P, 0, (0, 1))["budgets"]
+    assert list(u) == [10, 10, 9, 9, 9]
+    o = allocation.ada_allocate(s, P, 0, (1, 1))
+    assert list(o["budgets"]) == list(o["counts"])
+
+
+def test_all_equal_scores_take_first_flat_indices():
+    s = np.full((4, 10), 0.25)
+    out = allocation.ada_allocate(s, 23, 0, (1, 1))
+    assert list(out["counts"]) == [10, 10, 3, 0]
+    assert list(out["sel"][2]) == [0, 1, 2]
+
+
+def topsum(row_sorted_cum, b):
+    return row_sorted_cum[b]
+
+
+def test_theorem33_brute_force_tiny_config_shape():
+    """Ada-KV notes, Theorem 3.3: Algorithm 1's split attains the largest retained
+    mass over every split of the budget.  Tiny config shape: 4 heads, p = 60,
+    prefix budget 48 -> 20,825 compositions."""
+    r = np.random.default_rng(14)
+    hkv, p, P = 4, 60, 48
+    temps = [0.2, 0.5, 1.0, 3.0]
+    s = np.stack([np.exp(r.standard_normal(p) / t) for t in temps])
+    s /= s.sum(axis=1, keepdims=True)
+    out = allocation.ada_allocate(s, P, 0, (1, 1))
+    cums = [np.concatenate([[0.0], np.cumsum(np.sort(s[g])[::-1])]) for g in range(hkv)]
+    best, n_comp = -1.0, 0
+    for b0 in range(P + 1):
+        for b1 in range(P - b0 + 1):
+            for b2 in range(P - b0 - b1 + 1):
+                b3 = P - b0 - b1 - b2
+                n_comp += 1
+                val = cums[0][b0] + cums[1][b1] + cums[2][b2] + cums[3][b3]
+                best = max(best, val)
+    assert n_comp == 20825
+    got = sum(cums[g][out["budgets"][g]] for g in range(hkv))
+    assert got >= best * (1 - 1e-12)
+    # the adaptive split is not the uniform one here, and beats it
+    uni = sum(cums[g][P // hkv] for g in range(hkv))
+    assert got > uni
+
+
+def test_theorem32_brute_force_subsets():
+    """Ada-KV notes, Theorem 3.2: given B_i, per-head top-k maximises the
+    retained mass; checked over every subset of a 12-token head."""
+    r = np.random.default_rng(15)
+    p = 12
+    for trial in range(6):
+        s = r.random(p) ** 3
+        if trial == 5:
+            s = np.round(s, 1)
+        for b in range(p + 1):
+            best = max(s[list(c)].sum() for c in itertools.combinations(range(p), b)) if b else 0.0
+            sel = allocation.top_indices(s, b)
+            assert math.isclose(s[sel].sum(), best, rel_tol=1e-12, abs_tol=1e-15)
+
+
+def test_tie_break_prefers_lower_index():
+    s = np.array([[0.5, 0.2, 0.2, 0.2, 0.1]])
+    out = allocation.ada_allocate(s, 3, 0, (1, 1))
+    assert list(out["sel"][0]) == [0, 1, 2]
+    z = np.array([[0.0, -0.0, 0.0]])
+    assert list(allocation.ada_allocate(z, 2, 0, (1, 1))["sel"][0]) == [0, 1]
+
+
+# ---------------------------------------------------------------- LAVa budgets
+def test_entropy_uniform_closed_form_and_scipy():
+    hkv, p = 8, 100
+    s = np.full((hkv, p), 0.3)
+    e = allocation.layer_entropy(s)
+    assert math.isclose(e, math.log(hkv * p) / (hkv * p), rel_tol=1e-13)
+    r = np.random.default_rng(16)
+    x = r.random((3, 17)) ** 5
+    assert math.isclose(allocation.layer_entropy(x), scipy.stats.entropy(x.ravel()) / x.size, rel_tol=1e-12)
+
+
+def test_lava_budgets_sum_and_symmetry():
+    r = np.random.default_rng(17)
+    L, hkv, p, w = 6, 4, 50, 3
+    layer = r.random((hkv, p)) ** 3
+    same = np.stack([layer] * L)
+    bl, e = allocation.lava_layer_budgets(same, 150 + L * w * hkv, w)
+    assert bl.sum() == 150 and bl.max() - bl.min() <= 1
+    mixed = np.stack([r.random((hkv, p)) ** (1 + 2 * l) for l in range(L)])
+    bl2, e2 = allocation.lava_layer_budgets(mixed, 150 + L * w * hkv, w)
+    assert bl2.sum() == 150
+    # lower entropy (sharper layer) -> no larger budget
+    order = np.argsort(-e2)
+    assert np.all(np.diff(bl2[order]) <= 1)
+
+
+def test_lava_allocate_is_flattened_top():
+    r = np.random.default_rng(18)
+    L, hkv, p, w = 3, 4, 30, 2
+    s = r.random((L, hkv, p)) ** 4
+    out = allocation.lava_allocate(s, 100 + L * w * hkv, w)
+    assert out["layer_budgets"].sum() == 100
+    for l in range(L):
+        flat = s[l].ravel()
+        thr = np.sort(flat)[::-1][out["layer_budgets"][l] - 1] if out["layer_budgets"][l] else np.inf
+        kept = np.concatenate([g * p + out["sel"][l][g] for g in range(hkv)])
+        assert kept.size == out["layer_budgets"][l]
+        assert np.all(flat[kept] >= thr)
+        assert list(out["budgets"][l]) == [len(x) for x in out["sel"][l]]
+
+
+# ---------------------------------------------------------------- CriticalKV selection
+def test_criticalkv_limits_and_partition():
+    r = np.random.default_rng(19)
+    hkv, p, w = 4, 40, 2
+    a = r.random((hkv, p)) ** 3
+    c = r.random((hkv, p))
+    budget = 70 + w * hkv
+    same = allocation.criticalkv_allocate(a, c, budget, w, (1, 5), (1, 1))
+    base = allocation.ada_allocate(a, budget, w, (1, 5))
+    assert [list(x) for x in same["sel"]] == [list(x) for x in base["sel"]]
+    only2 = allocation.criticalkv_allocate(a, c, budget, w, (1, 5), (0, 1))
+    for g in range(hkv):
+        assert list(only2["sel"][g]) == sorted(allocation.top_indices(c[g], base["budgets"][g]))
+    half = allocation.criticalkv_allocate(a, c, budget, w, (1, 5), (1, 2))
+    for g in range(hkv):
+        s1, s2 = set(half["stage1"][g]), set(half["stage2"][g])
+        assert not (s1 & s2)
+        assert len(s1) == base["budgets"][g] // 2 and len(s1) + len(s2) == base["budgets"][g]
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _reversed_alpha(f, P, alpha):
+    a, b = alpha
+    return allocation.safeguard_budgets(f, P, (b - a, b))
+
+
+def _index_tie_reversed(score, budget, w, alpha):
+    flipped = np.asarray(score)[:, ::-1]
+    out = allocation.ada_allocate(flipped, budget, w, alpha)
+    p = flipped.shape[1]
+    out["sel"] = [np.sort(p - 1 - s) for s in out["sel"]]
+    return out
+
+
+def test_pins_catch_planted_mistakes():
+    assert not check_safeguard(_reversed_alpha)
+    assert not check_alg1_fixture(_index_tie_reversed)

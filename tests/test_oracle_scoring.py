@@ -1,0 +1,202 @@
+"""Pins for the oracle's scoring (CPU).  Each check compares the oracle with
+something other than itself: a library routine (SciPy's 1-D maximum filter,
+PyTorch's scaled-dot-product attention used as the definition of softmax
+attention), a closed form, or an invariant the mathematics fixes."""
+import math
+
+import numpy as np
+import pytest
+import scipy.ndimage
+import torch
+
+from oracle import scoring
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def sdpa_weights(q, k, mask=None):
+    """Attention weights from torch's SDPA: value = identity returns the weights."""
+    qt = torch.from_numpy(np.ascontiguousarray(q))[None, None]          # [1,1,r,d]
+    kt = torch.from_numpy(np.ascontiguousarray(k))[None, None]          # [1,1,n,d]
+    eye = torch.eye(k.shape[0], dtype=torch.float64)[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, eye, attn_mask=m)[0, 0].numpy()
+
+
+# ---------------------------------------------------------------- max pooling
+@pytest.mark.parametrize("kernel", [1, 3, 5, 7, 9])
+@pytest.mark.parametrize("length", [1, 2, 3, 7, 50])
+def test_maxpool_matches_scipy(kernel, length):
+    x = rng(kernel * 100 + length).random((3, length))
+    ref = scipy.ndimage.maximum_filter1d(x, size=kernel, axis=-1, mode="nearest")
+    np.testing.assert_array_equal(scoring.maxpool_same(x, kernel), ref)
+
+
+def test_maxpool_rejects_even_kernel():
+    with pytest.raises(ValueError):
+        scoring.maxpool_same(np.zeros(4), 4)
+
+
+# ---------------------------------------------------------------- Ada-KV / SnapKV
+def check_single_row_is_softmax_attention(fn) -> bool:
+    """w = 1, pool = 1, G = 1: the score is one row of scaled softmax attention."""
+    r = rng(1)
+    d, n = 16, 40
+    q = r.standard_normal((1, 1, d)) * 2.0
+    k = r.standard_normal((1, n, d))
+    got = fn(q, k, 1)[0]
+    ref = sdpa_weights(q[0], k[0, :n - 1])[0]
+    return np.allclose(got, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_single_row_is_softmax_attention():
+    assert check_single_row_is_softmax_attention(scoring.snapkv_head_scores)
+
+
+def test_window_mean_and_group_mean():
+    r = rng(2)
+    hq, hkv, w, d, n = 4, 2, 3, 8, 30
+    q = r.standard_normal((hq, w, d))
+    k = r.standard_normal((hkv, n, d))
+    p = n - w
+    heads = scoring.snapkv_head_scores(q, k, 1)
+    for i in range(hq):
+        ref = sdpa_weights(q[i], k[i // 2, :p]).mean(axis=0)
+        np.testing.assert_allclose(heads[i], ref, rtol=1e-12, atol=1e-15)
+    grp = scoring.snapkv_scores(q, k, 1)
+    np.testing.assert_allclose(grp[1], 0.5 * (heads[2] + heads[3]), rtol=1e-14)
+
+
+def check_pool_each_row_then_mean(fn) -> bool:
+    """Algorithm 2 step 4 pools every window row, then averages the rows."""
+    r = rng(3)
+    w, d, n, pool = 4, 8, 24, 5
+    q = r.standard_normal((1, w, d)) * 3
+    k = r.standard_normal((1, n, d))
+    P = sdpa_weights(q[0], k[0, :n - w])
+    ref = scipy.ndimage.maximum_filter1d(P, size=pool, axis=-1, mode="nearest").mean(axis=0)
+    return np.allclose(fn(q, k, pool)[0], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_pool_each_row_then_mean():
+    assert check_pool_each_row_then_mean(scoring.snapkv_head_scores)
+
+
+def test_constant_keys_give_uniform_scores():
+    r = rng(4)
+    hq, hkv, w, d, n = 4, 2, 5, 8, 37
+    q = r.standard_normal((hq, w, d))
+    k = np.broadcast_to(r.standard_normal(d), (hkv, n, d)).copy()
+    for pool in (1, 3, 7):
+        s = scoring.snapkv_scores(q, k, pool)
+        np.testing.assert_allclose(s, 1.0 / (n - w), rtol=1e-13)
+
+
+def test_mass_conservation_without_pooling():
+    r = rng(5)
+    q = r.standard_normal((6, 4, 8)) * 4
+    k = r.standard_normal((3, 50, 8))
+    s = scoring.snapkv_scores(q, k, 1)
+    np.testing.assert_allclose(s.sum(axis=1), 1.0, rtol=1e-13)
+
+
+def test_pooling_only_raises_scores():
+    r = rng(6)
+    q = r.standard_normal((4, 4, 8)) * 3
+    k = r.standard_normal((2, 40, 8))
+    base = scoring.snapkv_scores(q, k, 1)
+    for pool in (3, 7):
+        assert np.all(scoring.snapkv_scores(q, k, pool) >= base)
+
+
+# ---------------------------------------------------------------- LAVa
+def test_lava_causal_rows_and_vbar():
+    r = rng(7)
+    hq, hkv, w, d, n = 2, 2, 4, 8, 21
+    q = r.standard_normal((hq, w, d)) * 2
+    k = r.standard_normal((hkv, n, d))
+    v = r.standard_normal((hkv, n, d))
+    p = n - w
+    allowed = np.arange(n)[None, :] <= (p + np.arange(w))[:, None]
+    s_pre, vbar, s_full, pooled_full = scoring.lava_scores(q, k, v, 1, full=True)
+    for g in range(hkv):
+        vb = max(sum(abs(v[g, t, e]) for e in range(d)) for t in range(n))
+        assert math.isclose(vbar[g], vb, rel_tol=1e-13)
+        S = sdpa_weights(q[g], k[g], mask=allowed).sum(axis=0)
+        np.testing.assert_allclose(s_full[g], vb / w * S, rtol=1e-12, atol=1e-15)
+        # each window row sums to one, so the unpooled vector sums to V-bar
+        assert math.isclose(s_full[g].sum(), vb, rel_tol=1e-12)
+    np.testing.assert_array_equal(s_pre, s_full[:, :p])
+
+
+def test_lava_group_max_and_pool_order():
+    r = rng(8)
+    hq, hkv, w, d, n, pool = 4, 2, 3, 8, 26, 7
+    q = r.standard_normal((hq, w, d)) * 2
+    k = r.standard_normal((hkv, n, d))
+    v = r.standard_normal((hkv, n, d))
+    p = n - w
+    s_pre, vbar, s_full, pooled_full = scoring.lava_scores(q, k, v, pool, full=True)
+    single = [scoring.lava_scores(q[i:i + 1], k[i // 2:i // 2 + 1], v[i // 2:i // 2 + 1], 1, full=True)[2][0]
+              for i in range(hq)]
+    for g in range(hkv):
+        np.testing.assert_allclose(s_full[g], np.maximum(single[2 * g], single[2 * g + 1]), rtol=1e-14)
+    ref = scipy.ndimage.maximum_filter1d(s_full, size=pool, axis=-1, mode="nearest")
+    np.testing.assert_array_equal(pooled_full, ref)
+    np.testing.assert_array_equal(s_pre, ref[:, :p])
+
+
+# ---------------------------------------------------------------- CriticalKV
+def test_projected_norm_identity_projection():
+    """W^O made of identity blocks (D = d): ||V W^O_i||_1 = ||V||_1 row-wise."""
+    r = rng(9)
+    hq, hkv, d, n = 4, 2, 8, 12
+    v = r.standard_normal((hkv, n, d))
+    w_o = np.concatenate([np.eye(d)] * hq, axis=0)                       # [hq*d, d]
+    nrm = scoring.projected_value_norms(v, w_o, hq)
+    for i in range(hq):
+        np.testing.assert_allclose(nrm[i], np.abs(v[i // 2]).sum(axis=1), rtol=1e-14)
+    # a signed permutation and a scale change nothing but the scale
+    perm = np.eye(d)[r.permutation(d)] * np.where(r.random(d) < 0.5, -1.0, 1.0)
+    w2 = np.concatenate([3.0 * perm] * hq, axis=0)
+    np.testing.assert_allclose(scoring.projected_value_norms(v, w2, hq), 3.0 * nrm, rtol=1e-13)
+
+
+def test_criticalkv_group_rule_and_epsilon():
+    r = rng(10)
+    hq, hkv, w, d, n, D = 4, 2, 3, 8, 20, 12
+    q = r.standard_normal((hq, w, d))
+    k = r.standard_normal((hkv, n, d))
+    v = r.standard_normal((hkv, n, d))
+    w_o = r.standard_normal((hq * d, D))
+    score, comp, a, nrm = scoring.criticalkv_scores(q, k, v, w_o, 3, 1e-6)
+    np.testing.assert_allclose(score, scoring.snapkv_scores(q, k, 3), rtol=1e-14)
+    for g in range(hkv):
+        parts = []
+        for i in (2 * g, 2 * g + 1):
+            _, c1, _, _ = scoring.criticalkv_scores(q[i:i + 1], k[g:g + 1], v[g:g + 1],
+                                                    w_o[i * d:(i + 1) * d], 3, 1e-6)
+            parts.append(c1[0])
+        np.testing.assert_allclose(comp[g], 0.5 * (parts[0] + parts[1]), rtol=1e-13)
+    assert np.all(comp > 0)
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _no_sqrt_d(q_win, k, pool):
+    return scoring.snapkv_head_scores(q_win * math.sqrt(q_win.shape[-1]), k, pool)
+
+
+def _mean_then_pool(q_win, k, pool):
+    p = k.shape[1] - q_win.shape[1]
+    out = []
+    for i in range(q_win.shape[0]):
+        z = q_win[i] @ k[0, :p].T / math.sqrt(q_win.shape[-1])
+        out.append(scoring.maxpool_same(scoring.softmax_rows(z).mean(axis=0), pool))
+    return np.asarray(out)
+
+
+def test_pins_catch_planted_mistakes():
+    assert not check_single_row_is_softmax_attention(_no_sqrt_d)
+    assert not check_pool_each_row_then_mean(_mean_then_pool)
