@@ -1,0 +1,147 @@
+// Compaction of the retained rows into the flat cache on gfx950.
+//
+// Ada-KV notes, Algorithm 2 steps 10-11: keep the selected prefix rows and
+// append the window rows; the Ada-KV paper ("Variable-length Attention with
+// Variable-sized Cache Elements") stores all heads' retained caches in one
+// tensor.  Segment s = i*hkv + g occupies rows seg_start[s] .. seg_start[s+1]-1:
+// B_g selected rows (ascending token order), w window rows, then `reserve`
+// rows kept free for decode appends.  The copy is a pure byte move: every row
+// is moved by 16-byte lanes, consecutive lanes covering consecutive bytes.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace adakv {
+namespace {
+
+constexpr int LT = 1024;
+
+// Exclusive prefix sum (int64) over the workgroup in thread order.
+__device__ __forceinline__ int64_t block_excl_i64(int64_t x, int64_t* wsum, int64_t& total) {
+  int64_t inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(inc, off);
+    if ((int)__lane_id() >= off) inc += y;
+  }
+  const int wv = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
+  if ((int)__lane_id() == 63) wsum[wv] = inc;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+  for (int i = 0; i < nw; ++i) {
+    before += (i < wv) ? wsum[i] : 0;
+    all += wsum[i];
+  }
+  __syncthreads();
+  total = all;
+  return before + inc - x;
+}
+
+__global__ __launch_bounds__(LT) void compact_layout_kernel(const int32_t* __restrict__ budgets, int S, int w,
+                                                            int reserve, int64_t* __restrict__ seg_start,
+                                                            int32_t* __restrict__ seg_len) {
+  __shared__ int64_t wsum[LT / WAVE];
+  int64_t running = 0;
+  for (int base = 0; base < S; base += LT) {
+    const int s = base + threadIdx.x;
+    const int len = (s < S) ? budgets[s] + w : 0;
+    int64_t tot;
+    const int64_t ex = block_excl_i64((s < S) ? (int64_t)len + reserve : 0, wsum, tot);
+    if (s < S) {
+      seg_start[s] = running + ex;
+      seg_len[s] = len;
+    }
+    running += tot;
+  }
+  if (threadIdx.x == 0) seg_start[S] = running;
+}
+
+constexpr int RPW = 64;   // retained rows per copy workgroup
+
+template <int ROWB>
+__global__ __launch_bounds__(256) void compact_copy_kernel(const char* __restrict__ k, const char* __restrict__ v,
+                                                           const int32_t* __restrict__ budgets,
+                                                           const int32_t* __restrict__ sel,
+                                                           const int64_t* __restrict__ sel_off,
+                                                           const int64_t* __restrict__ seg_start, int S, int hkv,
+                                                           int n, int w, int p, int reserve, int64_t total_rows,
+                                                           int64_t flat_rows, char* __restrict__ kf,
+                                                           char* __restrict__ vf) {
+  __shared__ int64_t src_row[RPW], dst_row[RPW];
+  const int64_t r0 = (int64_t)blockIdx.x * RPW;
+  if (threadIdx.x < RPW) {
+    const int64_t r = r0 + threadIdx.x;
+    int64_t src = -1, dst = -1;
+    if (r < total_rows) {
+      // largest s with packed(s) <= r, packed(s) = seg_start[s] - s * reserve
+      int lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg_start[mid] - (int64_t)mid * reserve <= r) lo = mid;
+        else hi = mid - 1;
+      }
+      const int s = lo, inst = s / hkv, g = s % hkv;
+      const int64_t packed_s = seg_start[s] - (int64_t)s * reserve;
+      const int64_t j = r - packed_s;
+      const int B = budgets[s];
+      int64_t tok;
+      if (j < B) {
+        const int s0 = inst * hkv;
+        const int64_t head_off = packed_s - (seg_start[s0] - (int64_t)s0 * reserve) - (int64_t)g * w;
+        tok = sel[sel_off[inst] + head_off + j];
+      } else {
+        tok = (int64_t)p + (j - B);
+      }
+      dst = seg_start[s] + j;
+      // rows outside the caller's flat buffer or the source head are never touched
+      if (dst < flat_rows && tok >= 0 && tok < n) src = ((int64_t)inst * hkv + g) * n + tok;
+      else dst = -1;
+    }
+    src_row[threadIdx.x] = src;
+    dst_row[threadIdx.x] = dst;
+  }
+  __syncthreads();
+  constexpr int LPR = ROWB / 16;          // lanes per row
+  constexpr int RPP = 256 / LPR;          // rows per pass
+  const int rr0 = threadIdx.x / LPR, ch = threadIdx.x % LPR;
+#pragma unroll
+  for (int rr = rr0; rr < RPW; rr += RPP) {
+    const int64_t src = src_row[rr];
+    if (src < 0) continue;
+    const int64_t dst = dst_row[rr];
+    const u32x4 a = ld16(k + src * ROWB + ch * 16);
+    const u32x4 b = ld16(v + src * ROWB + ch * 16);
+    st16(kf + dst * ROWB + ch * 16, a);
+    st16(vf + dst * ROWB + ch * 16, b);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compact(const Geo& g, int64_t retained_rows, const void* k, const void* v,
+                          const int32_t* budgets, const int32_t* sel, const int64_t* sel_off, int reserve,
+                          void* k_flat, void* v_flat, int64_t* seg_start, int32_t* seg_len, hipStream_t st) {
+  const int S = g.I * g.hkv;
+  compact_layout_kernel<<<1, LT, 0, st>>>(budgets, S, g.w, reserve, seg_start, seg_len);
+  const int rowb = g.d * (g.dtype == ADAKV_BF16 ? 2 : 4);
+  const int64_t blocks = (retained_rows + RPW - 1) / RPW;
+  const int64_t flat_rows = retained_rows + (int64_t)S * reserve;
+  if (blocks == 0) return hipGetLastError();
+  const char* kc = static_cast<const char*>(k);
+  const char* vc = static_cast<const char*>(v);
+  char* kfc = static_cast<char*>(k_flat);
+  char* vfc = static_cast<char*>(v_flat);
+#define COPY(RB)                                                                                                  \
+  compact_copy_kernel<RB><<<(unsigned)blocks, 256, 0, st>>>(kc, vc, budgets, sel, sel_off, seg_start, S, g.hkv, g.n, \
+                                                            g.w, g.p, reserve, retained_rows, flat_rows, kfc, vfc)
+  switch (rowb) {
+    case 64: COPY(64); break;
+    case 128: COPY(128); break;
+    case 256: COPY(256); break;
+    case 512: COPY(512); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef COPY
+  return hipGetLastError();
+}
+
+}  // namespace adakv

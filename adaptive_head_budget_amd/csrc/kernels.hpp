@@ -1,0 +1,43 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "adakv.h"
+
+namespace adakv {
+
+// Validated geometry of a call.
+struct Geo {
+  int I, hq, hkv, G, d, n, w, p, pool, dtype, scorer, hidden;
+  float eps;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- scoring (score.hip, vwo.hip)
+size_t score_ws_bytes(const Geo& g);
+hipError_t launch_score(const Geo& g, const void* q, const void* k, const void* v, const void* w_o,
+                        float* score, float* score2, char* ws, hipStream_t st);
+hipError_t launch_vwo(const Geo& g, int inst0, int ni, const void* v, const void* w_o,
+                      const float* head_scores, float* score2, hipStream_t st);
+
+// ---- allocation (select.hip)
+size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a);
+hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* score, const float* score2,
+                           int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st);
+
+// ---- compaction (compact.hip)
+hipError_t launch_compact(const Geo& g, int64_t retained_rows, const void* k, const void* v,
+                          const int32_t* budgets, const int32_t* sel, const int64_t* sel_off, int reserve,
+                          void* k_flat, void* v_flat, int64_t* seg_start, int32_t* seg_len, hipStream_t st);
+
+// ---- decode (decode.hip)
+constexpr int DECODE_ROWS = 256;   // rows of one split-K chunk
+size_t decode_ws_bytes(const Geo& g, int64_t max_rows);
+hipError_t launch_decode(const Geo& g, int64_t max_rows, const void* q, const void* k_new, const void* v_new,
+                         void* k_flat, void* v_flat, const int64_t* seg_start, int32_t* seg_len,
+                         float* out, char* ws, hipStream_t st);
+
+}  // namespace adakv

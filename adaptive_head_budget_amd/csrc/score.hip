@@ -1,0 +1,573 @@
+// Observation-window scoring on gfx950.
+//
+// Pass 1 (score_stats_kernel): per window row, the softmax normaliser over the
+// row's key domain, as (row max, sum of exp) partials over key chunks.
+// Pass 2 (score_emit_kernel): the pooled, normalised weights reduced to one
+// score per key.  Both passes form Q_win K^T with 16x16 MFMA tiles: keys are the
+// M side (A operand, staged through LDS), window rows the N side (B operand,
+// held in registers).  The A rows are permuted so that every lane ends up with
+// 32 consecutive keys of one window row, which makes the max pooling a
+// register-local sliding maximum.
+//
+// Definitions followed:
+//  * Ada-KV notes, Algorithm 2 ("Ada-KV Integration") steps 2-4: softmax of the
+//    window queries against the cache outside the window, max pooling of every
+//    row, mean over the rows; GQA groups average their query heads ("与分组查询
+//    注意力（GQA）的兼容性").  Logits carry the 1/sqrt(d_h) of the Ada-KV paper,
+//    Section 3.1, footnote 5.
+//  * LAVa notes, Definition 1, "适配GQA架构" and "实验环境": causal window rows,
+//    row weights summed, group maximum, times max_k ||V[k]||_1 / w, max pooled.
+//  * CriticalKV notes, "作为通用插件融入现有驱逐流水线": the per-query-head Ada-KV
+//    score is kept for the composite score.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace adakv {
+namespace {
+
+constexpr int TILE = 128;          // keys per tile (8 M-blocks of 16)
+constexpr int HALO = 4;            // extra keys on each side of an emit tile
+constexpr int TROWS = TILE + 2 * HALO;
+constexpr int STATS_KEYS = 1024;   // keys per stats workgroup
+
+template <typename T, int D>
+struct Lay {
+  static constexpr int ROWB = D * (int)sizeof(T);
+  static constexpr int STRIDE = ROWB + 16;           // odd count of 16-B units per LDS row
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  static constexpr int EPC = 16 / (int)sizeof(T);    // elements per chunk
+  static constexpr int KSTEPS = D / Mma<T>::KSTEP;
+};
+
+// LDS row of key offset koff in [0, TILE): the 16 M-rows an A-operand read
+// touches map to 16 consecutive LDS rows.  Halo keys take rows TILE.. TILE+7.
+__device__ __forceinline__ int tile_row(int koff) {
+  if (koff < 0) return TILE + (koff + HALO);
+  if (koff >= TILE) return TILE + HALO + (koff - TILE);
+  return ((koff & 31) << 2) | (koff >> 5);
+}
+
+// LDS row read by lane m (= lane % 16) of M-block mb.  Main blocks hold keys
+// 32*(m/4) + 4*mb + (m%4); the halo block (mb == 8) holds keys -4..-1 in lane
+// group 0 and TILE..TILE+3 in lane group 3 (groups 1, 2 read duplicates).
+__device__ __forceinline__ int a_row(int mb, int m) {
+  if (mb < 8) return 16 * mb + 4 * (m & 3) + (m >> 2);
+  return ((m >> 2) == 3) ? TILE + HALO + (m & 3) : TILE + (m & 3);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void stage_tile(char* lds, const T* kb, int n, int k0, int koff_lo, int koff_hi) {
+  using L = Lay<T, D>;
+  const int cnt = (koff_hi - koff_lo) * L::CPR;
+  for (int idx = threadIdx.x; idx < cnt; idx += blockDim.x) {
+    const int koff = koff_lo + idx / L::CPR, ch = idx % L::CPR;
+    const int key = k0 + koff;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (key >= 0 && key < n) v = ld16(kb + (size_t)key * D + ch * L::EPC);
+    st16(lds + tile_row(koff) * L::STRIDE + ch * 16, v);
+  }
+}
+
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2, float c2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  l = l * fast_exp2((m - M) * c2) + l2 * fast_exp2((m2 - M) * c2);
+  m = M;
+}
+
+// Sum 32 per-lane values across the 16 lanes of a lane group (lanes sharing
+// lane/16); afterwards lane c of the group holds the totals of entries 2c, 2c+1.
+__device__ __forceinline__ void reduce_scatter16(float (&x)[32], int c, float& o0, float& o1) {
+  float y[16], z[8], u[4], t[2];
+  {
+    const bool b = (c >> 3) & 1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float send = b ? x[i] : x[i + 16];
+      const float keep = b ? x[i + 16] : x[i];
+      y[i] = keep + shfl_xor(send, 8);
+    }
+  }
+  {
+    const bool b = (c >> 2) & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float send = b ? y[i] : y[i + 8];
+      const float keep = b ? y[i + 8] : y[i];
+      z[i] = keep + shfl_xor(send, 4);
+    }
+  }
+  {
+    const bool b = (c >> 1) & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float send = b ? z[i] : z[i + 4];
+      const float keep = b ? z[i + 4] : z[i];
+      u[i] = keep + shfl_xor(send, 2);
+    }
+  }
+  {
+    const bool b = c & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float send = b ? u[i] : u[i + 2];
+      const float keep = b ? u[i + 2] : u[i];
+      t[i] = keep + shfl_xor(send, 1);
+    }
+  }
+  o0 = t[0];
+  o1 = t[1];
+}
+
+__device__ __forceinline__ float allsum16(float x) {
+  x += shfl_xor(x, 8);
+  x += shfl_xor(x, 4);
+  x += shfl_xor(x, 2);
+  x += shfl_xor(x, 1);
+  return x;
+}
+
+// ---------------------------------------------------------------- pass 1
+template <typename T, int D, int NB, bool CAUSAL>
+__global__ __launch_bounds__(512) void score_stats_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, float2* __restrict__ part, int inst0, int hq,
+    int hkv, int G, int n, int w, int p, int kend, int nchunk, float c2) {
+  using L = Lay<T, D>;
+  using M = Mma<T>;
+  extern __shared__ __align__(16) char lds[];
+  const int chunk = blockIdx.x, g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
+  const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+  const int gq = lane >> 4, c = lane & 15;
+  const T* kb = k + ((size_t)inst * hkv + g) * (size_t)n * D;
+  const T* qb = q + ((size_t)inst * hq + (size_t)g * G + h) * (size_t)w * D;
+
+  typename M::op_t qop[NB][L::KSTEPS];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = 16 * nb + c;
+#pragma unroll
+    for (int ks = 0; ks < L::KSTEPS; ++ks)
+      qop[nb][ks] = (r < w) ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
+  }
+  float rm[NB], rl[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) { rm[nb] = -INFINITY; rl[nb] = 0.f; }
+
+  const int kbeg = chunk * STATS_KEYS;
+  const int kfin = min(kbeg + STATS_KEYS, kend);
+  for (int k0 = kbeg; k0 < kfin; k0 += TILE) {
+    __syncthreads();
+    stage_tile<T, D>(lds, kb, n, k0, 0, TILE);
+    __syncthreads();
+    f32x4 acc[8][NB];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
+      const T* arow = reinterpret_cast<const T*>(lds + a_row(mb, c) * L::STRIDE);
+#pragma unroll
+      for (int ks = 0; ks < L::KSTEPS; ++ks) {
+        const typename M::op_t a = M::load(arow + ks * M::KSTEP + M::KPL * gq);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = 16 * nb + c;
+      const int lim = CAUSAL ? min(kend - 1, p + r) : kend - 1;   // last key of this row's domain
+      float lm = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = k0 + 32 * gq + 4 * mb + j;
+          if (key <= lim) lm = fmaxf(lm, acc[mb][nb][j]);
+        }
+      if (lm != -INFINITY) {
+        float ls = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = k0 + 32 * gq + 4 * mb + j;
+            const float e = fast_exp2((acc[mb][nb][j] - lm) * c2);
+            ls += (key <= lim) ? e : 0.f;
+          }
+        merge_ml(rm[nb], rl[nb], lm, ls, c2);
+      }
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const float om = shfl_xor(rm[nb], mask), ol = shfl_xor(rl[nb], mask);
+      merge_ml(rm[nb], rl[nb], om, ol, c2);
+    }
+    const int r = 16 * nb + c;
+    if (gq == 0 && r < w)
+      part[(((size_t)il * hkv + g) * nchunk + chunk) * (size_t)(G * w) + h * w + r] = make_float2(rm[nb], rl[nb]);
+  }
+}
+
+__global__ void score_stats_merge_kernel(const float2* __restrict__ part, float2* __restrict__ stats, int nrows,
+                                         int Gw, int nchunk, float c2) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nrows) return;
+  const int seg = t / Gw, row = t % Gw;
+  float m = -INFINITY, l = 0.f;
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const float2 v = part[((size_t)seg * nchunk + ch) * Gw + row];
+    merge_ml(m, l, v.x, v.y, c2);
+  }
+  stats[t] = make_float2(m, 1.0f / l);
+}
+
+// ---------------------------------------------------------------- pass 2
+enum { EMIT_SNAP = 0, EMIT_LAVA = 1 };
+
+template <typename T, int D, int NB, int POOL, int KIND>
+__global__ __launch_bounds__(512) void score_emit_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float2* __restrict__ stats,
+    const uint32_t* __restrict__ vbar_bits, float* __restrict__ score, float* __restrict__ head_scores,
+    int inst0, int hq, int hkv, int G, int n, int w, int p, int tiles_per_wg, float c2) {
+  using L = Lay<T, D>;
+  using M = Mma<T>;
+  constexpr int RHO = (POOL - 1) / 2;
+  extern __shared__ __align__(16) char lds[];
+  float* hs = reinterpret_cast<float*>(lds + TROWS * L::STRIDE);   // [G][TROWS]
+  float* gmx = hs + G * TROWS;                                      // [TROWS]
+  const int g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
+  const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+  const int gq = lane >> 4, c = lane & 15;
+  const int Gw = G * w;
+  const T* kb = k + ((size_t)inst * hkv + g) * (size_t)n * D;
+  const T* qb = q + ((size_t)inst * hq + (size_t)g * G + h) * (size_t)w * D;
+
+  typename M::op_t qop[NB][L::KSTEPS];
+  float sm[NB], sil[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = 16 * nb + c;
+#pragma unroll
+    for (int ks = 0; ks < L::KSTEPS; ++ks)
+      qop[nb][ks] = (r < w) ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
+    if (r < w) {
+      const float2 st = stats[((size_t)il * hkv + g) * Gw + h * w + r];
+      sm[nb] = st.x;
+      sil[nb] = st.y;
+    } else {
+      sm[nb] = 0.f;     // padding rows: q = 0, weight 0
+      sil[nb] = 0.f;
+    }
+  }
+  const float vscale = (KIND == EMIT_LAVA) ? __uint_as_float(vbar_bits[(size_t)inst * hkv + g]) / (float)w : 0.f;
+  const float inv_gw = 1.0f / (float)Gw, inv_w = 1.0f / (float)w;
+
+  for (int t = 0; t < tiles_per_wg; ++t) {
+    const int k0 = (blockIdx.x * tiles_per_wg + t) * TILE;
+    if (k0 >= p) break;
+    __syncthreads();
+    stage_tile<T, D>(lds, kb, n, k0, -HALO, TILE + HALO);
+    __syncthreads();
+
+    f32x4 acc[9][NB];
+#pragma unroll
+    for (int mb = 0; mb < 9; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
+      const T* arow = reinterpret_cast<const T*>(lds + a_row(mb, c) * L::STRIDE);
+#pragma unroll
+      for (int ks = 0; ks < L::KSTEPS; ++ks) {
+        const typename M::op_t a = M::load(arow + ks * M::KSTEP + M::KPL * gq);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
+      }
+    }
+    const int kbase = k0 + 32 * gq;   // first key of this lane group
+
+    if (KIND == EMIT_SNAP) {
+      float ks[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) ks[i] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        // x[t] <-> key kbase - 3 + t, t in [0, 38); outside the prefix -> -inf
+        float x[38];
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[3 + 4 * mb + j] = acc[mb][nb][j];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const float lft = shfl_lane(acc[7][nb][1 + j], (lane - 16) & 63);
+          const float rgt = shfl_lane(acc[0][nb][j], (lane + 16) & 63);
+          x[j] = (gq == 0) ? acc[8][nb][1 + j] : lft;
+          x[35 + j] = (gq == 3) ? acc[8][nb][j] : rgt;
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 38; ++t2) {
+          const int key = kbase - 3 + t2;
+          if (key < 0 || key >= p) x[t2] = -INFINITY;
+        }
+        const float mrow = sm[nb], il_row = sil[nb];
+        if (RHO == 3) {
+          float a[36];
+#pragma unroll
+          for (int t2 = 0; t2 < 36; ++t2) a[t2] = fmax3(x[t2], x[t2 + 1], x[t2 + 2]);
+#pragma unroll
+          for (int kk = 0; kk < 32; ++kk) {
+            const float pooled = fmax3(a[kk], a[kk + 2], a[kk + 4]);
+            ks[kk] += fast_exp2((pooled - mrow) * c2) * il_row;
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < 32; ++kk) {
+            float pooled = x[kk + 3];
+            if (RHO >= 1) pooled = fmax3(pooled, x[kk + 2], x[kk + 4]);
+            if (RHO >= 2) pooled = fmax3(pooled, x[kk + 1], x[kk + 5]);
+            ks[kk] += fast_exp2((pooled - mrow) * c2) * il_row;
+          }
+        }
+      }
+      float s0, s1;
+      reduce_scatter16(ks, c, s0, s1);
+      hs[h * TILE + 32 * gq + 2 * c] = s0;
+      hs[h * TILE + 32 * gq + 2 * c + 1] = s1;
+      __syncthreads();
+      for (int t2 = threadIdx.x; t2 < TILE; t2 += blockDim.x) {
+        const int key = k0 + t2;
+        if (key < p) {
+          float s = 0.f;
+          for (int hh = 0; hh < G; ++hh) s += hs[hh * TILE + t2];
+          score[((size_t)inst * hkv + g) * p + key] = s * inv_gw;
+        }
+      }
+      if (head_scores != nullptr) {
+        for (int idx = threadIdx.x; idx < G * TILE; idx += blockDim.x) {
+          const int hh = idx / TILE, t2 = idx % TILE, key = k0 + t2;
+          if (key < p)
+            head_scores[(((size_t)il * hq) + (size_t)g * G + hh) * p + key] = hs[hh * TILE + t2] * inv_w;
+        }
+      }
+    } else {
+      // LAVa: causal weights summed over the head's rows, before pooling.
+      float ks[32], hsum[4];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) ks[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hsum[j] = 0.f;
+      const int hkey0 = (gq == 0) ? k0 - HALO : ((gq == 3) ? k0 + TILE : -1);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int r = 16 * nb + c;
+        const int lim = min(n - 1, p + r);
+        const float mrow = sm[nb], il_row = sil[nb];
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = kbase + 4 * mb + j;
+            const float e = fast_exp2((acc[mb][nb][j] - mrow) * c2) * il_row;
+            ks[4 * mb + j] += (key <= lim) ? e : 0.f;
+          }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = hkey0 + j;
+          const float e = fast_exp2((acc[8][nb][j] - mrow) * c2) * il_row;
+          hsum[j] += (hkey0 >= 0 && key >= 0 && key <= lim) ? e : 0.f;
+        }
+      }
+      float s0, s1;
+      reduce_scatter16(ks, c, s0, s1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hsum[j] = allsum16(hsum[j]);
+      float* hrow = hs + h * TROWS;
+      hrow[HALO + 32 * gq + 2 * c] = s0;
+      hrow[HALO + 32 * gq + 2 * c + 1] = s1;
+      if (c == 0 && gq == 0)
+        for (int j = 0; j < 4; ++j) hrow[j] = hsum[j];
+      if (c == 0 && gq == 3)
+        for (int j = 0; j < 4; ++j) hrow[HALO + TILE + j] = hsum[j];
+      __syncthreads();
+      for (int t2 = threadIdx.x; t2 < TROWS; t2 += blockDim.x) {
+        float m = hs[t2];
+        for (int hh = 1; hh < G; ++hh) m = fmaxf(m, hs[hh * TROWS + t2]);
+        gmx[t2] = m;
+      }
+      __syncthreads();
+      for (int t2 = threadIdx.x; t2 < TILE; t2 += blockDim.x) {
+        const int key = k0 + t2;
+        if (key < p) {
+          float m = gmx[HALO + t2];
+#pragma unroll
+          for (int o = 1; o <= RHO; ++o) m = fmax3(m, gmx[HALO + t2 - o], gmx[HALO + t2 + o]);
+          score[((size_t)inst * hkv + g) * p + key] = vscale * m;
+        }
+      }
+    }
+  }
+}
+
+// LAVa value-norm maximum: vbar[i, g] = max_t sum_e |v[i, g, t, e]| (row sums in
+// a fixed order; the maximum is taken with an integer atomic on the bit
+// pattern, exact and order independent for non-negative floats).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vbar_kernel(const T* __restrict__ v, uint32_t* __restrict__ vbar_bits,
+                                                   int inst0, int hkv, int n, int rows_per_wg) {
+  using L = Lay<T, D>;
+  constexpr int LPR = L::CPR;              // lanes per row
+  constexpr int RPP = 256 / LPR;           // rows per pass of the workgroup
+  const int g = blockIdx.y, inst = inst0 + blockIdx.z;
+  const T* vb = v + ((size_t)inst * hkv + g) * (size_t)n * D;
+  const int lr = threadIdx.x / LPR, ch = threadIdx.x % LPR;
+  const int r0 = blockIdx.x * rows_per_wg, r1 = min(n, r0 + rows_per_wg);
+  float best = 0.f;
+  for (int base = r0; base < r1; base += RPP) {   // same trip count for every lane
+    const int r = base + lr;
+    float s = 0.f;
+    if (r < r1) {
+      const u32x4 x = ld16(vb + (size_t)r * D + ch * L::EPC);
+      if (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s += fabsf(bf16_bits_to_f32(x[e] & 0xffffu)) + fabsf(bf16_bits_to_f32(x[e] >> 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += fabsf(__uint_as_float(x[e]));
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) s += shfl_xor(s, m);
+    best = fmaxf(best, s);
+  }
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1) best = fmaxf(best, shfl_xor(best, m));
+  if ((threadIdx.x & 63) == 0) atomicMax(vbar_bits + (size_t)inst * hkv + g, __float_as_uint(best));
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int cnt) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < cnt) p[t] = v;
+}
+
+// ---------------------------------------------------------------- host side
+struct ScorePlan {
+  int ib;        // instances per batch
+  int nchunk;    // stats chunks per head
+  int kend;      // end of the widest row domain
+  size_t off_part, off_stats, off_heads, off_vbar, total;
+};
+
+ScorePlan plan_score(const Geo& g) {
+  ScorePlan P{};
+  const size_t inst_k_bytes = (size_t)g.hkv * g.n * g.d * (g.dtype == ADAKV_BF16 ? 2 : 4);
+  size_t ib = (size_t)(128u << 20) / (inst_k_bytes ? inst_k_bytes : 1);
+  if (ib < 1) ib = 1;
+  if (ib > (size_t)g.I) ib = g.I;
+  P.ib = (int)ib;
+  P.kend = (g.scorer == ADAKV_SCORE_LAVA) ? g.n : g.p;
+  P.nchunk = (P.kend + STATS_KEYS - 1) / STATS_KEYS;
+  const size_t Gw = (size_t)g.G * g.w;
+  size_t off = 0;
+  P.off_part = off;  off = align_up(off + (size_t)P.ib * g.hkv * P.nchunk * Gw * sizeof(float2), 256);
+  P.off_stats = off; off = align_up(off + (size_t)P.ib * g.hkv * Gw * sizeof(float2), 256);
+  P.off_heads = off;
+  if (g.scorer == ADAKV_SCORE_CRITICALKV) off = align_up(off + (size_t)P.ib * g.hq * g.p * sizeof(float), 256);
+  P.off_vbar = off;
+  off = align_up(off + (size_t)g.I * g.hkv * sizeof(uint32_t), 256);
+  P.total = off;
+  return P;
+}
+
+template <typename T, int D, int NB>
+hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void* k, const void* v,
+                     const void* w_o, float* score, float* score2, char* ws, hipStream_t st) {
+  using L = Lay<T, D>;
+  const float c2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
+  float2* part = reinterpret_cast<float2*>(ws + P.off_part);
+  float2* stats = reinterpret_cast<float2*>(ws + P.off_stats);
+  float* heads = (g.scorer == ADAKV_SCORE_CRITICALKV) ? reinterpret_cast<float*>(ws + P.off_heads) : nullptr;
+  uint32_t* vbar = reinterpret_cast<uint32_t*>(ws + P.off_vbar);
+  const T* qt = static_cast<const T*>(q);
+  const T* kt = static_cast<const T*>(k);
+  const bool lava = g.scorer == ADAKV_SCORE_LAVA;
+  const int threads = g.G * WAVE;
+  const int Gw = g.G * g.w;
+  const size_t lds_stats = (size_t)TILE * L::STRIDE;
+  const size_t lds_emit = (size_t)TROWS * L::STRIDE + (size_t)(g.G + 1) * TROWS * sizeof(float);
+  const int ntiles = (g.p + TILE - 1) / TILE;
+
+  if (lava) {
+    const int cnt = g.I * g.hkv;
+    fill_u32_kernel<<<(cnt + 255) / 256, 256, 0, st>>>(vbar, 0u, cnt);
+    const int rows_per_wg = 2048;
+    dim3 grid((g.n + rows_per_wg - 1) / rows_per_wg, g.hkv, g.I);
+    vbar_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(v), vbar, 0, g.hkv, g.n, rows_per_wg);
+  }
+  for (int i0 = 0; i0 < g.I; i0 += P.ib) {
+    const int ni = std::min(P.ib, g.I - i0);
+    dim3 g1(P.nchunk, g.hkv, ni);
+    if (lava)
+      score_stats_kernel<T, D, NB, true><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
+                                                                         g.w, g.p, P.kend, P.nchunk, c2);
+    else
+      score_stats_kernel<T, D, NB, false><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
+                                                                          g.w, g.p, P.kend, P.nchunk, c2);
+    const int nrows = ni * g.hkv * Gw;
+    score_stats_merge_kernel<<<(nrows + 255) / 256, 256, 0, st>>>(part, stats, nrows, Gw, P.nchunk, c2);
+    const long tiles_total = (long)ntiles * g.hkv * ni;
+    int tpw = (int)std::max<long>(1, tiles_total / 2048);
+    if (tpw > ntiles) tpw = ntiles;
+    dim3 g2((ntiles + tpw - 1) / tpw, g.hkv, ni);
+#define EMIT(POOLV)                                                                                          \
+  do {                                                                                                       \
+    if (lava)                                                                                                \
+      score_emit_kernel<T, D, NB, POOLV, EMIT_LAVA><<<g2, threads, lds_emit, st>>>(                          \
+          qt, kt, stats, vbar, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, tpw, c2);                \
+    else                                                                                                     \
+      score_emit_kernel<T, D, NB, POOLV, EMIT_SNAP><<<g2, threads, lds_emit, st>>>(                          \
+          qt, kt, stats, vbar, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, tpw, c2);                  \
+  } while (0)
+    switch (g.pool) {
+      case 1: EMIT(1); break;
+      case 3: EMIT(3); break;
+      case 5: EMIT(5); break;
+      default: EMIT(7); break;
+    }
+#undef EMIT
+    if (g.scorer == ADAKV_SCORE_CRITICALKV) {
+      hipError_t e = launch_vwo(g, i0, ni, v, w_o, heads, score2, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t run_score_nb(const Geo& g, const ScorePlan& P, const void* q, const void* k, const void* v,
+                        const void* w_o, float* score, float* score2, char* ws, hipStream_t st) {
+  if (g.w <= 16) return run_score<T, D, 1>(g, P, q, k, v, w_o, score, score2, ws, st);
+  if (g.w <= 32) return run_score<T, D, 2>(g, P, q, k, v, w_o, score, score2, ws, st);
+  return run_score<T, D, 4>(g, P, q, k, v, w_o, score, score2, ws, st);
+}
+
+}  // namespace
+
+size_t score_ws_bytes(const Geo& g) { return plan_score(g).total; }
+
+hipError_t launch_score(const Geo& g, const void* q, const void* k, const void* v, const void* w_o,
+                        float* score, float* score2, char* ws, hipStream_t st) {
+  const ScorePlan P = plan_score(g);
+  if (g.dtype == ADAKV_BF16) {
+    if (g.d == 128) return run_score_nb<uint16_t, 128>(g, P, q, k, v, w_o, score, score2, ws, st);
+    if (g.d == 64) return run_score_nb<uint16_t, 64>(g, P, q, k, v, w_o, score, score2, ws, st);
+  } else {
+    if (g.d == 16) return run_score_nb<float, 16>(g, P, q, k, v, w_o, score, score2, ws, st);
+    if (g.d == 64) return run_score_nb<float, 64>(g, P, q, k, v, w_o, score, score2, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace adakv

@@ -1,0 +1,125 @@
+"""Device buffers for one eviction pass and the four library calls in order.
+
+PyTorch only provides device memory and the stream; every step runs in
+libadakv's kernels through the ctypes binding.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import lib
+from .configs import Workload
+
+_SCORERS = {"snapkv": lib.ADAKV_SCORE_SNAPKV, "lava": lib.ADAKV_SCORE_LAVA, "criticalkv": lib.ADAKV_SCORE_CRITICALKV}
+
+
+def make_shape(cfg: Workload, n_inst: Optional[int] = None, n: Optional[int] = None) -> lib.AdakvShape:
+    return lib.AdakvShape(
+        n_inst=cfg.instances if n_inst is None else n_inst, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d,
+        n=cfg.n if n is None else n, w=cfg.w, pool=cfg.pool,
+        dtype=lib.ADAKV_BF16 if cfg.dtype == "bf16" else lib.ADAKV_F32, scorer=_SCORERS[cfg.scorer],
+        hidden=cfg.hidden, eps=cfg.eps, reserved0=0)
+
+
+def make_alloc(cfg: Workload, budget: Optional[int] = None) -> lib.AdakvAlloc:
+    mode = {"snapkv": lib.ADAKV_ALLOC_ADA, "lava": lib.ADAKV_ALLOC_LAVA_LAYERS,
+            "criticalkv": lib.ADAKV_ALLOC_ADA_CRITICALKV}[cfg.scorer]
+    return lib.AdakvAlloc(mode=mode, alpha_num=cfg.alpha[0], alpha_den=cfg.alpha[1], ck_num=cfg.ck[0],
+                          ck_den=cfg.ck[1], reserved0=0, budget=cfg.budget if budget is None else budget)
+
+
+def selected_rows(shape: lib.AdakvShape, alloc: lib.AdakvAlloc) -> int:
+    if alloc.mode == lib.ADAKV_ALLOC_LAVA_LAYERS:
+        return alloc.budget - shape.n_inst * shape.w * shape.hkv
+    return shape.n_inst * (alloc.budget - shape.w * shape.hkv)
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda"):
+    """Storage array (bf16 bits as uint16, or float32) -> device tensor."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def to_host_f64(t) -> np.ndarray:
+    """Device tensor (bf16 or f32) -> float64 values, exactly."""
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+class Eviction:
+    """Output buffers and workspace for one call sequence score -> allocate ->
+    compact -> decode over I instances."""
+
+    def __init__(self, cfg: Workload, n_inst: Optional[int] = None, n: Optional[int] = None,
+                 budget: Optional[int] = None, reserve: Optional[int] = None, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.shape = make_shape(cfg, n_inst, n)
+        self.alloc = make_alloc(cfg, budget)
+        self.reserve = cfg.reserve if reserve is None else reserve
+        s = self.shape
+        I, hkv, p = s.n_inst, s.hkv, s.n - s.w
+        self.tdtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        ws_bytes = lib.adakv_workspace_bytes(s, self.alloc, self.reserve)
+        if ws_bytes == 0:
+            raise ValueError("invalid shape or allocation settings")
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        self.score = torch.empty((I, hkv, p), dtype=torch.float32, device=device)
+        self.score2 = (torch.empty((I, hkv, p), dtype=torch.float32, device=device)
+                       if cfg.scorer == "criticalkv" else None)
+        self.budgets = torch.empty((I, hkv), dtype=torch.int32, device=device)
+        self.n_sel = selected_rows(s, self.alloc)
+        self.sel = torch.empty((max(self.n_sel, 4),), dtype=torch.int32, device=device)
+        self.sel_off = torch.empty((I + 1,), dtype=torch.int64, device=device)
+        self.rows = self.n_sel + I * hkv * (s.w + self.reserve)
+        self.k_flat = torch.empty((self.rows, s.d), dtype=self.tdtype, device=device)
+        self.v_flat = torch.empty((self.rows, s.d), dtype=self.tdtype, device=device)
+        self.seg_start = torch.empty((I * hkv + 1,), dtype=torch.int64, device=device)
+        self.seg_len = torch.empty((I * hkv,), dtype=torch.int32, device=device)
+        self.out = torch.empty((I, s.hq, s.d), dtype=torch.float32, device=device)
+        self.step = 0
+
+    def run_score(self, q_win, k, v=None, w_o=None, stream=None):
+        lib.adakv_score(self.shape, q_win, k, v, w_o, self.score, self.score2, self.ws, stream)
+
+    def run_allocate(self, stream=None):
+        lib.adakv_allocate(self.shape, self.alloc, self.score, self.score2, self.budgets, self.sel, self.sel_off,
+                           self.ws, stream)
+
+    def run_compact(self, k, v, stream=None):
+        lib.adakv_compact(self.shape, self.alloc, k, v, self.budgets, self.sel, self.sel_off, self.reserve,
+                          self.k_flat, self.v_flat, self.seg_start, self.seg_len, stream)
+        self.step = 0
+
+    def run_decode(self, q, k_new=None, v_new=None, stream=None):
+        lib.adakv_decode_attn(self.shape, self.alloc, q, k_new, v_new, self.k_flat, self.v_flat, self.seg_start,
+                              self.seg_len, self.reserve, self.step, self.out, self.ws, stream)
+        if k_new is not None:
+            self.step += 1
+
+    def evict(self, q_win, k, v=None, w_o=None, stream=None):
+        self.run_score(q_win, k, v, w_o, stream)
+        self.run_allocate(stream)
+        self.run_compact(k, v, stream)
+
+    # host views -------------------------------------------------------------
+    def host_selection(self):
+        """Per instance, per head: the selected token indices (numpy)."""
+        b = self.budgets.cpu().numpy().astype(np.int64)
+        sel = self.sel.cpu().numpy().astype(np.int64)
+        off = self.sel_off.cpu().numpy()
+        res = []
+        for i in range(b.shape[0]):
+            pos = int(off[i])
+            heads = []
+            for g in range(b.shape[1]):
+                heads.append(sel[pos:pos + b[i, g]])
+                pos += int(b[i, g])
+            res.append(heads)
+        return b, off, res

@@ -1,0 +1,185 @@
+"""Benchmark of the eviction hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+score -> allocate -> compact for every instance, then the workload's decode
+steps (append + varlen attention over the flat cache).  Default workload:
+Llama-3.1-8B geometry, 32 layers x batch 4 (128 instances), 32768 cached tokens,
+budget 1024 per KV head, 128 decode steps.
+
+Prints one JSON line.  `value` is the evicted-layer KV token rate (tokens of
+all instances / stream time of score+allocate+compact); the flat-cache decode
+HBM rate is reported next to it, with the phase times that make up ms_per_step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def decode_bytes(cfg, rows_before: int, append: bool) -> int:
+    """Algorithmic HBM bytes of one decode call: every retained K and V row
+    once (after the append), the queries, the outputs and the appended rows."""
+    el = 2 if cfg.dtype == "bf16" else 4
+    I, hkv, hq, d = cfg.instances, cfg.hkv, cfg.hq, cfg.d
+    rows = rows_before + (I * hkv if append else 0)
+    b = rows * 2 * d * el + I * hq * d * el + I * hq * d * 4
+    if append:
+        b += 2 * I * hkv * d * el     # k_new, v_new read (their flat-cache write is part of `rows`)
+    return b
+
+
+def evict_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one eviction pass: K read once for the window
+    scores (V too for LAVa/CriticalKV), the window queries, the scores written
+    and read back by the selection, and the retained rows copied (read + write)."""
+    el = 2 if cfg.dtype == "bf16" else 4
+    I, hkv, hq, d, n, w, p = cfg.instances, cfg.hkv, cfg.hq, cfg.d, cfg.n, cfg.w, cfg.p
+    kv = I * hkv * n * d * el
+    b = kv + I * hq * w * d * el
+    if cfg.scorer != "snapkv":
+        b += kv
+    b += 2 * I * hkv * p * 4
+    retained = (cfg.budget if cfg.scorer == "lava" else I * cfg.budget)
+    b += retained * 2 * d * el * 2
+    return b
+
+
+def cpu_baseline(cfg):
+    """The oracle, untuned, on one instance of the workload on the host cores."""
+    from adaptive_head_budget_amd import synth
+    from oracle import allocation, cache, scoring
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    inst = synth.make_instance(cfg, 0)
+    dt = cfg.dtype
+    q = synth.widen(inst["q_win"], dt)
+    k = synth.widen(inst["k"], dt)
+    t0 = time.perf_counter()
+    s = scoring.snapkv_scores(q, k, cfg.pool)
+    r = allocation.ada_allocate(s, cfg.budget, cfg.w, cfg.alpha)
+    v = synth.widen(inst["v"], dt)
+    kh, vh = cache.compact(k, r["sel"], cfg.w), cache.compact(v, r["sel"], cfg.w)
+    t1 = time.perf_counter()
+    if cfg.decode_steps:
+        kh, vh = cache.append(kh, vh, synth.widen(inst["k_new"][0], dt), synth.widen(inst["v_new"][0], dt))
+        cache.decode(synth.widen(inst["q_dec"][0], dt), kh, vh)
+    t2 = time.perf_counter()
+    return {"value": cfg.n / (t1 - t0), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {cfg.instances} instances ({cfg.n} tokens x {cfg.hkv} KV heads): score+allocate+"
+                      f"compact {t1 - t0:.2f} s, one decode step {t2 - t1:.3f} s (float64 NumPy)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="llama3.1-8b_32L_b4_n32768")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the eviction path has no multi-GPU "
+              f"leg in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from adaptive_head_budget_amd import configs, lib, pipeline, synth
+
+    lib.load()
+    cfg = configs.BY_NAME[args.config]
+    dev = "cuda"
+    print(f"[bench] {cfg.name}: drawing inputs", file=sys.stderr, flush=True)
+    data = synth.make_batch_torch(cfg, dev)
+    ev = pipeline.Eviction(cfg, device=dev)
+    stream = torch.cuda.current_stream()
+    v_arg = data["v"] if cfg.scorer != "snapkv" else None
+    w_o = data.get("w_o")
+    steps_dec = cfg.decode_steps
+    rows_base = ev.n_sel + cfg.instances * cfg.hkv * cfg.w
+
+    def one_step(rec):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        ev.run_score(data["q_win"], data["k"], v_arg, w_o)
+        e[1].record(stream)
+        ev.run_allocate()
+        e[2].record(stream)
+        ev.run_compact(data["k"], data["v"])
+        e[3].record(stream)
+        dec = []
+        for t in range(steps_dec):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            if cfg.append:
+                ev.run_decode(data["q_dec"][t], data["k_new"][t], data["v_new"][t])
+            else:
+                ev.run_decode(data["q_dec"][t])
+            b.record(stream)
+            dec.append((a, b))
+        if rec is not None:
+            rec.append((e, dec))
+
+    for _ in range(args.warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(recs)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    sc = np.mean([r[0][0].elapsed_time(r[0][1]) for r in recs])
+    al = np.mean([r[0][1].elapsed_time(r[0][2]) for r in recs])
+    co = np.mean([r[0][2].elapsed_time(r[0][3]) for r in recs])
+    evict_ms = sc + al + co
+    dec_launch_ms = [a.elapsed_time(b) for r in recs for (a, b) in r[1]]
+    dec_ms_step = float(np.sum(dec_launch_ms)) / args.steps if dec_launch_ms else 0.0
+    tokens = cfg.instances * cfg.n
+    value = tokens / (evict_ms * 1e-3)
+
+    dec_bytes_total = sum(decode_bytes(cfg, rows_base + cfg.instances * cfg.hkv * (t if cfg.append else 0),
+                                       cfg.append) for t in range(steps_dec))
+    out = {
+        "metric": "evicted-layer KV tokens/s + flat-cache decode HBM GB/s, Llama-3.1-8B shape",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic (seeded device draws; shapes of the named model, no weights)",
+        "config": {"workload": cfg.name, "instances": cfg.instances, "layers": cfg.layers, "batch": cfg.batch,
+                   "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d, "n": cfg.n, "w": cfg.w, "pool": cfg.pool,
+                   "budget": cfg.budget, "alpha": list(cfg.alpha), "decode_steps": steps_dec,
+                   "scorer": cfg.scorer},
+        "phases_ms": {"score": sc, "allocate": al, "compact": co, "evict": evict_ms, "decode_total": dec_ms_step},
+        "evict_hbm_gbps": evict_bytes(cfg) / (evict_ms * 1e-3) / 1e9,
+    }
+    if steps_dec:
+        avg_launch_s = float(np.mean(dec_launch_ms)) * 1e-3
+        per_launch_bytes = dec_bytes_total / steps_dec
+        achieved = per_launch_bytes / avg_launch_s / 1e9
+        out["decode_hbm_gbps"] = achieved
+        out["roofline"] = {"kernel": "adakv_decode_attn", "bound": "hbm", "achieved": achieved,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                           "traffic": None, "algorithmic_bytes_per_launch": per_launch_bytes,
+                           "avg_launch_ms": avg_launch_s * 1e3}
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

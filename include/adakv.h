@@ -1,0 +1,217 @@
+/*
+ * adakv.h -- C ABI of libadakv.so: head-wise adaptive KV-cache eviction on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path, per layer instance (one layer of one sequence):
+ *   adakv_score        observation-window scores of every prefix token
+ *   adakv_allocate     layer-wide top-B -> per-head budgets -> per-head selection
+ *   adakv_compact      selected rows + window rows -> one flat variable-length cache
+ *   adakv_decode_attn  decode attention over the flat cache (optional append)
+ *
+ * Conventions shared by every call
+ *   - Every buffer argument is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or keeps pointers after a call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting: the host is never synchronised.
+ *   - Arguments are checked on the host before anything is launched.  A bad
+ *     argument returns its status code and launches nothing.  ADAKV_EHIP means
+ *     the HIP runtime reported an error when a kernel was launched.
+ *   - Every pointer must be 16-byte aligned.  Arrays are dense, row-major, in
+ *     the shapes given below, with I = shape.n_inst, p = n - w, G = hq / hkv.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Calls are stateless and may run concurrently on different streams with
+ *     different workspaces.
+ *
+ * Sources (page title, then section / equation / algorithm):
+ *   [AdaKV-notes]  "Ada-KV: Optimizing KV Cache Eviction by Adaptive Budget
+ *                  Allocation for Efficient LLM Inference" (papercache.org notes)
+ *   [AdaKV-paper]  the same paper, arXiv 2407.11550 HTML, Sections 3-4
+ *   [LAVa-notes]   "LAVa: Layer-wise KV Cache Eviction with Dynamic Budget
+ *                  Allocation" (papercache.org notes)
+ *   [CKV-notes]    "CriticalKV: Optimizing KV Cache Eviction from an Output
+ *                  Perturbation Perspective" (papernotes.org)
+ */
+#ifndef ADAKV_H
+#define ADAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ADAKV_OK = 0,
+  ADAKV_EINVAL = 1,        /* a NULL pointer, a bad size or a bad combination   */
+  ADAKV_EUNSUPPORTED = 2,  /* valid but not built: head dim, dtype, window, ... */
+  ADAKV_ECAPACITY = 3,     /* an append would pass the reserved rows            */
+  ADAKV_EWORKSPACE = 4,    /* ws_bytes smaller than adakv_workspace_bytes()     */
+  ADAKV_EHIP = 5           /* the HIP runtime reported an error on launch       */
+} adakv_status;
+
+typedef enum { ADAKV_BF16 = 0, ADAKV_F32 = 1 } adakv_dtype;
+
+typedef enum {
+  ADAKV_SCORE_SNAPKV = 0,      /* Ada-KV / SnapKV window attention            */
+  ADAKV_SCORE_LAVA = 1,        /* LAVa score (attention x value-norm maximum) */
+  ADAKV_SCORE_CRITICALKV = 2   /* Ada-KV score + CriticalKV composite         */
+} adakv_scorer;
+
+typedef enum {
+  ADAKV_ALLOC_ADA = 0,          /* Ada-KV budgets with safeguard, per-head top-k   */
+  ADAKV_ALLOC_LAVA_LAYERS = 1,  /* LAVa entropy layer budgets, flattened top-k    */
+  ADAKV_ALLOC_ADA_CRITICALKV = 2/* Ada-KV budgets, CriticalKV two-stage selection */
+} adakv_alloc_mode;
+
+/* Geometry of one call.  Enumerations are carried as int32_t fields. */
+typedef struct {
+  int32_t n_inst;  /* I: independent instances (layer x sequence)            */
+  int32_t hq;      /* query heads                                             */
+  int32_t hkv;     /* KV heads; hq % hkv == 0                                 */
+  int32_t d;       /* head dimension                                          */
+  int32_t n;       /* cached tokens per head, window included                 */
+  int32_t w;       /* observation window: the last w tokens of every head     */
+  int32_t pool;    /* max-pool kernel, odd, 1 = off                           */
+  int32_t dtype;   /* adakv_dtype of q, k, v, w_o and the flat cache           */
+  int32_t scorer;  /* adakv_scorer                                            */
+  int32_t hidden;  /* CriticalKV: model hidden size D (columns of W^O)         */
+  float eps;       /* CriticalKV: additive epsilon of the composite            */
+  int32_t reserved0;
+} adakv_shape;
+
+/* Budget allocation settings. */
+typedef struct {
+  int32_t mode;       /* adakv_alloc_mode                                          */
+  int32_t alpha_num;  /* Ada-KV safeguard alpha = alpha_num / alpha_den (0..1)     */
+  int32_t alpha_den;
+  int32_t ck_num;     /* CriticalKV stage-1 share = ck_num / ck_den (0..1)        */
+  int32_t ck_den;
+  int32_t reserved0;
+  int64_t budget;     /* ADA / CRITICALKV: budget B of every instance, window
+                         included (w*hkv <= B <= n*hkv).
+                         LAVA_LAYERS: total budget over all I instances (the
+                         layers of one sequence), windows included; the part
+                         B' = budget - I*w*hkv must satisfy 0 <= B' <= hkv*p.  */
+} adakv_alloc;
+
+/* Bytes of workspace every call below needs for this geometry (the maximum
+ * over the calls).  `reserve` is the number of empty rows kept per head in the
+ * flat cache (see adakv_compact).  Returns 0 for an invalid description. */
+size_t adakv_workspace_bytes(const adakv_shape* shape, const adakv_alloc* alloc, int32_t reserve);
+
+/* Observation-window scoring of every prefix token (the first p tokens).
+ *
+ *   SNAPKV      [AdaKV-notes] Algorithm 2 ("Ada-KV Integration"), steps 2-4:
+ *               for query head i and window row r the logits
+ *               q_win[i,r] . k[g,t] / sqrt(d) over the prefix t < p are
+ *               softmaxed, every row is max pooled (stride 1, window cut at the
+ *               ends), and the rows are averaged; GQA groups take the mean
+ *               over their query heads ([AdaKV-paper] "Compatibility with Group
+ *               Query Attention").  score[i,g,t] = that group mean.
+ *   LAVA        [LAVa-notes] Definition 1 and "适配GQA架构": window row r attends
+ *               causally to keys 0..p+r; the rows' weights are summed, the group
+ *               takes the maximum over its heads, the result is scaled by
+ *               max_t ||v[g,t]||_1 / w and max pooled over all n tokens; score
+ *               holds the prefix part.
+ *   CRITICALKV  score = the SNAPKV score (for the budgets); score2 = the
+ *               composite of [CKV-notes] "两阶段贪心选择算法", under GQA the mean
+ *               over the group's query heads of (A_i[t] + eps) * ||(v W^O_i)[t]||_1.
+ *
+ *   q_win  [I, hq, w, d]   dtype         the window queries
+ *   k      [I, hkv, n, d]  dtype
+ *   v      [I, hkv, n, d]  dtype         LAVA and CRITICALKV only, else NULL
+ *   w_o    [hidden, hq*d]  dtype         CRITICALKV only, else NULL: the output
+ *                                        projection in the nn.Linear layout
+ *                                        (row c holds output feature c, so
+ *                                        W^O_i of the pages is columns i*d..i*d+d-1
+ *                                        transposed)
+ *   score  [I, hkv, p]     float32 out
+ *   score2 [I, hkv, p]     float32 out   CRITICALKV only, else NULL
+ *   ws     >= adakv_workspace_bytes() bytes of device scratch
+ *
+ * Supported: bf16 with d in {64, 128}; f32 with d in {16, 64}; w <= 64;
+ * pool in {1, 3, 5, 7}; G <= 8; CRITICALKV needs bf16, d = 128 and hidden a
+ * multiple of 64.  Other valid shapes return ADAKV_EUNSUPPORTED. */
+adakv_status adakv_score(const adakv_shape* shape, const void* q_win, const void* k, const void* v,
+                         const void* w_o, float* score, float* score2, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Budget allocation and selection.  Scores must be finite and >= 0 (-0.0 is
+ * treated as +0.0).  Ranking: a larger score first; equal scores by the smaller
+ * flat index g*p + t.
+ *
+ *   ADA         [AdaKV-notes] Algorithm 1 inside Algorithm 2: P = B - w*hkv;
+ *               the top P of all hkv*p scores give counts f_g; the safeguard
+ *               (Algorithm 2, step 8) alpha*f_g + (1-alpha)*P/hkv is made
+ *               integer exactly (floors, then one extra unit to the largest
+ *               remainders, lower head first on equal remainders) so the
+ *               budgets sum to P; then each head keeps its top B_g.
+ *   LAVA_LAYERS [LAVa-notes] "基于不确定性的层预算分配": instance l is layer l;
+ *               e_l = entropy of the layer's normalised scores / (hkv*p);
+ *               B' = budget - I*w*hkv is split in proportion to e_l (largest
+ *               remainder, lower layer first); "动态头预算的逐层缓存驱逐": each
+ *               layer keeps its top B'_l of the flattened scores (no safeguard).
+ *   ADA_CRITICALKV  budgets as ADA on `score`; per head stage 1 keeps the top
+ *               floor(B_g*ck_num/ck_den) by `score`, stage 2 the top rest by
+ *               `score2` among the others ([CKV-notes] "两阶段贪心选择算法").
+ *
+ *   score   [I, hkv, p] float32         score2 [I, hkv, p] float32 (CK only, else NULL)
+ *   budgets [I, hkv]    int32 out       prefix budget B_g of every head
+ *   sel     int32 out, sum of all budgets entries: instance i starts at
+ *           sel_off[i]; inside it head g's selected token indices (in [0,p))
+ *           follow head g-1's, each head ascending.  Its length is
+ *           I*(budget - w*hkv) for ADA / CK and budget - I*w*hkv for LAVA.
+ *   sel_off [I+1] int64 out
+ */
+adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, const float* score,
+                            const float* score2, int32_t* budgets, int32_t* sel, int64_t* sel_off,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Compaction into the flat cache ([AdaKV-notes] Algorithm 2 steps 10-11 and
+ * [AdaKV-paper] "Variable-length Attention with Variable-sized Cache
+ * Elements": all heads' retained caches concatenated into one tensor).
+ * Segment s = i*hkv + g holds the selected prefix rows of (i, g) in ascending
+ * token order, then its w window rows, then `reserve` rows left untouched for
+ * decode appends.  The copy is bit-exact.
+ *
+ *   k, v        [I, hkv, n, d] dtype         as given to adakv_score
+ *   budgets, sel, sel_off                    as written by adakv_allocate
+ *   k_flat, v_flat [rows, d] dtype out       rows = (sum of budgets) + I*hkv*(w + reserve)
+ *   seg_start   [I*hkv + 1] int64 out        first row of every segment
+ *   seg_len     [I*hkv]     int32 out        B_g + w (rows in use)
+ */
+adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, const void* k, const void* v,
+                           const int32_t* budgets, const int32_t* sel, const int64_t* sel_off,
+                           int32_t reserve, void* k_flat, void* v_flat, int64_t* seg_start,
+                           int32_t* seg_len, void* stream);
+
+/* Decode attention over the flat cache.  If k_new and v_new are given, first
+ * every segment gets one more row at seg_start[s] + seg_len[s] and seg_len[s]
+ * grows by one ([AdaKV-notes] the cache update before the output formula).
+ * Then out[i, j] = softmax(q[i,j] . K_s / sqrt(d)) V_s over the seg_len[s] rows of
+ * segment s = i*hkv + j/G.
+ *
+ *   q          [I, hq, d]    dtype
+ *   k_new, v_new [I, hkv, d] dtype, both or neither (NULL = no append)
+ *   k_flat, v_flat, seg_start, seg_len       from adakv_compact (seg_len updated in place)
+ *   reserve    the reserve given to adakv_compact
+ *   step       appends already made since adakv_compact (0 for the first decode);
+ *              an append with step >= reserve returns ADAKV_ECAPACITY
+ *   out        [I, hq, d] float32 out
+ * Needs G <= 8. */
+adakv_status adakv_decode_attn(const adakv_shape* shape, const adakv_alloc* alloc, const void* q,
+                               const void* k_new, const void* v_new, void* k_flat, void* v_flat,
+                               const int64_t* seg_start, int32_t* seg_len, int32_t reserve, int32_t step,
+                               float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* A short, static description of a status code. */
+const char* adakv_strerror(adakv_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t adakv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ADAKV_H */
