@@ -157,7 +157,7 @@ adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, c
 
 adakv_status adakv_decode_attn(const adakv_shape* shape, const adakv_alloc* alloc, const void* q, const void* k_new,
                                const void* v_new, void* k_flat, void* v_flat, const int64_t* seg_start,
-                               int32_t* seg_len, int32_t reserve, int32_t step, float* out, void* ws,
+                               const int32_t* seg_len, int32_t reserve, int32_t step, float* out, void* ws,
                                size_t ws_bytes, void* stream) {
   Geo g{};
   adakv_status st = check_shape(shape, g);
@@ -176,8 +176,8 @@ adakv_status adakv_decode_attn(const adakv_shape* shape, const adakv_alloc* allo
   if (!append && step > reserve) return ADAKV_EINVAL;
   const int64_t rows = selected_rows(*alloc, g) + (int64_t)g.I * g.hkv * ((int64_t)g.w + step + (append ? 1 : 0));
   if (ws_bytes < decode_ws_bytes(g, rows)) return ADAKV_EWORKSPACE;
-  return hip_status(launch_decode(g, rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out,
-                                  static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+  return hip_status(launch_decode(g, rows, step + (append ? 1 : 0), q, k_new, v_new, k_flat, v_flat, seg_start,
+                                  seg_len, out, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

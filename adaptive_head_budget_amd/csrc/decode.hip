@@ -1,194 +1,160 @@
 // Decode attention over the flat variable-length cache on gfx950.
 //
-// Ada-KV notes, "多头自注意力层的形式化描述": append the new key/value, then
-// A_i = softmax(q_i K^T) (scaled by 1/sqrt(d_h), LAVa notes "解码过程的残差流视角")
-// and the head output A_i V.  The varlen design follows the Ada-KV paper's
-// "Variable-length Attention with Variable-sized Cache Elements": every
-// segment (instance, KV head) has its own length, and the G query heads of a
-// GQA group share every row read.
+// Ada-KV notes, "多头自注意力层的形式化描述": the new key/value is appended to
+// the cache, then A_i = softmax(q_i K^T) (scaled by 1/sqrt(d_h), LAVa notes
+// "解码过程的残差流视角") and the head output A_i V.  The varlen design follows
+// the Ada-KV paper's "Variable-length Attention with Variable-sized Cache
+// Elements": every segment (instance, KV head) has its own length, and the G
+// query heads of a GQA group share every row read.
 //
-// Work is split into chunks of DECODE_ROWS rows.  A prep kernel appends the new
-// rows and lays out the chunk list; the attention kernel turns one chunk into a
-// partial (row max, sum, weighted value sum) per query head, with q.K^T on
-// 16x16 MFMA tiles (rows on M, query heads on N) and the value sum on the
-// vector units reading V with 16-byte coalesced loads; the merge kernel
-// combines the partials of each head in chunk order.
+// One workgroup streams one segment (or one of `nsplit` row ranges of it when
+// segments are too few to fill the chip).  Each of its 4 waves takes 64 rows of
+// every 256-row chunk: q.K^T on 16x16 MFMA tiles (rows on M, query heads on N),
+// an online softmax per wave, and the value sum on the vector units with
+// 16-byte coalesced V loads.  The new row of an append is read straight from
+// k_new/v_new and also stored into the segment's reserved rows for later steps;
+// seg_len is never modified (a call attends over seg_len + step (+1) rows), so
+// a decode call carries no state from the previous one.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace adakv {
 namespace {
 
-constexpr int PT = 1024;
-constexpr int R = DECODE_ROWS;
+constexpr int CH = 256;   // rows per chunk (4 waves x 64)
 
-template <typename T, int D>
-__global__ __launch_bounds__(PT) void decode_prep_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
-                                                         T* __restrict__ kf, T* __restrict__ vf,
-                                                         const int64_t* __restrict__ seg_start,
-                                                         int32_t* __restrict__ seg_len, int S,
-                                                         int32_t* __restrict__ chunk_start) {
-  __shared__ int32_t wsum[PT / WAVE];
-  constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int CPR = D / EPC;
-  int running = 0;
-  for (int base = 0; base < S; base += PT) {
-    const int s = base + threadIdx.x;
-    int nch = 0;
-    if (s < S) {
-      int len = seg_len[s];
-      // append only inside the segment's own rows (its reserve)
-      if (k_new != nullptr && seg_start[s] + len < seg_start[s + 1]) {
-        const int64_t row = seg_start[s] + len;
-        for (int c = 0; c < CPR; ++c) {
-          st16(kf + row * D + c * EPC, ld16(k_new + (size_t)s * D + c * EPC));
-          st16(vf + row * D + c * EPC, ld16(v_new + (size_t)s * D + c * EPC));
-        }
-        len += 1;
-        seg_len[s] = len;
-      }
-      nch = (len + R - 1) / R;
-    }
-    // exclusive scan of nch
-    int inc = nch;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(inc, off);
-      if ((int)__lane_id() >= off) inc += y;
-    }
-    const int wv = threadIdx.x / WAVE;
-    if ((int)__lane_id() == 63) wsum[wv] = inc;
-    __syncthreads();
-    int before = 0, all = 0;
-    for (int i = 0; i < PT / WAVE; ++i) {
-      before += (i < wv) ? wsum[i] : 0;
-      all += wsum[i];
-    }
-    __syncthreads();
-    if (s < S) chunk_start[s] = running + before + inc - nch;
-    running += all;
-  }
-  if (threadIdx.x == 0) chunk_start[S] = running;
-}
-
-// One chunk of up to R rows of one segment.  4 waves x 64 rows.
 template <typename T, int D, int GT>
-__global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ q, const T* __restrict__ kf,
-                                                          const T* __restrict__ vf,
-                                                          const int64_t* __restrict__ seg_start,
-                                                          const int32_t* __restrict__ seg_len,
-                                                          const int32_t* __restrict__ chunk_start, int S, int hq,
-                                                          int hkv, int G, float c2, float* __restrict__ part) {
+__global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
+                                                     const T* __restrict__ v_new, T* __restrict__ kf,
+                                                     T* __restrict__ vf, const int64_t* __restrict__ seg_start,
+                                                     const int32_t* __restrict__ seg_len, int hq, int hkv, int G,
+                                                     int nsplit, int extra, int append, float c2,
+                                                     float* __restrict__ out, float* __restrict__ part) {
   using M = Mma<T>;
   constexpr int KSTEPS = D / M::KSTEP;
   constexpr int EPL = 16 / (int)sizeof(T);     // value elements per lane
   constexpr int LPR = D / EPL;                 // lanes per value row
   constexpr int RS = WAVE / LPR;               // row slots per wave
-  constexpr int PSTR = D + 2;
-  __shared__ float P[4][64][GT];
+  constexpr int RPL = 64 / RS;                 // value rows per lane per chunk
+  __shared__ float P[2][4][64][GT];
+  __shared__ float Sc[2][4][GT];
   __shared__ float Ow[4][GT][D];
   __shared__ float Mw[4][GT], Lw[4][GT];
-  __shared__ int seg_sh;
 
-  const int b = blockIdx.x;
-  const int total = chunk_start[S];
-  if (b >= total) return;
-  if (threadIdx.x == 0) {
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (chunk_start[mid] <= b) lo = mid;
-      else hi = mid - 1;
-    }
-    seg_sh = lo;
-  }
-  __syncthreads();
-  const int s = seg_sh;
+  const int s = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
   const int inst = s / hkv, g = s % hkv;
-  const int len = seg_len[s];
-  const int row0 = (b - chunk_start[s]) * R;
-  const int64_t base_row = seg_start[s];
+  const int64_t base = seg_start[s];
+  const int cap = (int)(seg_start[s + 1] - base);
+  const int len0 = seg_len[s];
+  int len = len0 + extra;
+  const bool do_append = append && (len0 + extra - 1) < cap;
+  if (len > cap) len = cap;                      // never read past the segment's rows
+  const int newrow = do_append ? len0 + extra - 1 : -1;
+  const int nch = (len + CH - 1) / CH;
+  const int cps = (nch + nsplit - 1) / nsplit;
+  const int r_begin = split * cps * CH;
+  const int r_end = min(len, r_begin + cps * CH);
+
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int gq = lane >> 4, c = lane & 15;
+  const int rs = lane / LPR, cc = lane % LPR;
+  const T* knew_s = k_new + (size_t)s * D;
+  const T* vnew_s = v_new + (size_t)s * D;
 
-  // B operand: q^T, column c = query head of the group (zero beyond G).
+  if (do_append && split == 0 && threadIdx.x < D / (16 / (int)sizeof(T))) {
+    constexpr int EPC = 16 / (int)sizeof(T);
+    st16(kf + (base + newrow) * D + threadIdx.x * EPC, ld16(knew_s + threadIdx.x * EPC));
+    st16(vf + (base + newrow) * D + threadIdx.x * EPC, ld16(vnew_s + threadIdx.x * EPC));
+  }
+
   typename M::op_t qop[KSTEPS];
   const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (c < G ? c : 0)) * D;
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) qop[ks] = (c < G) ? M::load(qb + ks * M::KSTEP + M::KPL * gq) : M::zero();
 
-  const int wrow0 = row0 + 64 * wv;   // first row of this wave
-  f32x4 acc[4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    acc[mb] = zero4();
-    int r = wrow0 + 16 * mb + c;
-    r = (r < len) ? r : 0;
-    const T* krow = kf + (base_row + r) * D;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) acc[mb] = M::mma(M::load(krow + ks * M::KSTEP + M::KPL * gq), qop[ks], acc[mb]);
-  }
-  // acc[mb][j] <-> row wrow0 + 16*mb + 4*gq + j, query head c
-  float m = -INFINITY;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wrow0 + 16 * mb + 4 * gq + j;
-      if (r < len) m = fmaxf(m, acc[mb][j]);
-    }
-  m = fmaxf(m, shfl_xor(m, 16));
-  m = fmaxf(m, shfl_xor(m, 32));
-  float l = 0.f;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wrow0 + 16 * mb + 4 * gq + j;
-      const float e = (r < len && m != -INFINITY) ? fast_exp2((acc[mb][j] - m) * c2) : 0.f;
-      l += e;
-      if (c < GT) P[wv][16 * mb + 4 * gq + j][c] = e;
-    }
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
-  if (gq == 0 && c < GT) {
-    Mw[wv][c] = m;
-    Lw[wv][c] = l;
-  }
-  __syncthreads();
-
-  // value sum: lane (row slot rs, element chunk cc)
-  const int rs = lane / LPR, cc = lane % LPR;
+  float m_run = -INFINITY, l_run = 0.f;   // per query head c (same in the 4 lane groups)
   float o[GT][EPL];
 #pragma unroll
   for (int h = 0; h < GT; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
-#pragma unroll 4
-  for (int t = 0; t < 64 / RS; ++t) {
-    const int rr = t * RS + rs;
-    const int r = wrow0 + rr;
-    if (r < len) {
-      const u32x4 raw = ld16(vf + (base_row + r) * D + cc * EPL);
+
+  int buf = 0;
+  for (int c0 = r_begin; c0 < r_end; c0 += CH, buf ^= 1) {
+    const int wrow0 = c0 + 64 * wv;
+    // issue the value loads first: they do not depend on the scores
+    u32x4 vraw[RPL];
+#pragma unroll
+    for (int t = 0; t < RPL; ++t) {
+      const int r = wrow0 + t * RS + rs;
+      const T* src = (r == newrow) ? vnew_s : vf + (base + (r < r_end ? r : r_begin)) * D;
+      vraw[t] = ld16(src + cc * EPL);
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      acc[mb] = zero4();
+      const int r = wrow0 + 16 * mb + c;
+      const T* krow = (r == newrow) ? knew_s : kf + (base + (r < r_end ? r : r_begin)) * D;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) acc[mb] = M::mma(M::load(krow + ks * M::KSTEP + M::KPL * gq), qop[ks], acc[mb]);
+    }
+    // acc[mb][j] <-> row wrow0 + 16*mb + 4*gq + j, query head c
+    float mc = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (wrow0 + 16 * mb + 4 * gq + j < r_end) mc = fmaxf(mc, acc[mb][j]);
+    mc = fmaxf(mc, shfl_xor(mc, 16));
+    mc = fmaxf(mc, shfl_xor(mc, 32));
+    const float m_new = fmaxf(m_run, mc);
+    const float sc_run = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c2);
+    float lc = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 16 * mb + 4 * gq + j;
+        const float e = (wrow0 + rr < r_end) ? fast_exp2((acc[mb][j] - m_new) * c2) : 0.f;
+        lc += e;
+        if (c < GT) P[buf][wv][rr][c] = e;
+      }
+    lc += shfl_xor(lc, 16);
+    lc += shfl_xor(lc, 32);
+    l_run = l_run * sc_run + lc;
+    m_run = m_new;
+    if (gq == 0 && c < GT) Sc[buf][wv][c] = sc_run;
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float sh = Sc[buf][wv][h];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] *= sh;
+    }
+#pragma unroll
+    for (int t = 0; t < RPL; ++t) {
+      const int rr = t * RS + rs;
       float vv[EPL];
       if (sizeof(T) == 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vv[2 * e] = bf16_bits_to_f32(raw[e] & 0xffffu);
-          vv[2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16);
+        for (int e = 0; e < EPL / 2; ++e) {
+          vv[2 * e] = bf16_bits_to_f32(vraw[t][e] & 0xffffu);
+          vv[2 * e + 1] = bf16_bits_to_f32(vraw[t][e] >> 16);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) vv[e] = __uint_as_float(raw[e]);
+        for (int e = 0; e < EPL; ++e) vv[e] = __uint_as_float(vraw[t][e]);
       }
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float pw = P[wv][rr][h];
+        const float pw = P[buf][wv][rr][h];   // 0 for rows past the end
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[h][e] += pw * vv[e];
       }
     }
   }
+  // sum the row slots of each wave, then combine the waves in order
 #pragma unroll
   for (int msk = LPR; msk < 64; msk <<= 1)
 #pragma unroll
@@ -201,92 +167,108 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const T* __restrict__ 
 #pragma unroll
       for (int e = 0; e < EPL; ++e) Ow[wv][h][cc * EPL + e] = o[h][e];
   }
+  if (gq == 0 && c < GT) {
+    Mw[wv][c] = m_run;
+    Lw[wv][c] = l_run;
+  }
   __syncthreads();
-  // combine the 4 waves in order
   for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
     const int h = idx / (D + 2), e = idx % (D + 2);
     float Mx = -INFINITY;
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) Mx = fmaxf(Mx, Mw[w2][h]);
-    float acc2 = 0.f;
+    float acc2 = 0.f, l2 = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
       const float sc = (Mw[w2][h] == -INFINITY) ? 0.f : fast_exp2((Mw[w2][h] - Mx) * c2);
-      acc2 += sc * ((e < D) ? Ow[w2][h][e] : (e == D ? 0.f : Lw[w2][h]));
+      l2 += sc * Lw[w2][h];
+      if (e < D) acc2 += sc * Ow[w2][h][e];
     }
-    part[((size_t)b * G + h) * PSTR + e] = (e == D) ? Mx : acc2;
+    if (nsplit == 1) {
+      if (e < D) out[((size_t)inst * hq + (size_t)g * G + h) * D + e] = acc2 / l2;
+    } else {
+      part[((size_t)blockIdx.x * G + h) * (D + 2) + e] = (e < D) ? acc2 : (e == D ? Mx : l2);
+    }
   }
 }
 
 template <int D>
-__global__ void decode_merge_kernel(const float* __restrict__ part, const int32_t* __restrict__ chunk_start, int hq,
-                                    int hkv, int G, int max_chunks, float c2, float* __restrict__ out) {
-  constexpr int PSTR = D + 2;
-  const int inst = blockIdx.x / hq, j = blockIdx.x % hq;
-  const int g = j / G, h = j % G;
+__global__ void decode_merge_kernel(const float* __restrict__ part, int hq, int hkv, int G, int nsplit, float c2,
+                                    float* __restrict__ out) {
+  const int inst = blockIdx.x / hq, jq = blockIdx.x % hq;
+  const int g = jq / G, h = jq % G;
   const int s = inst * hkv + g;
-  const int c0 = min(chunk_start[s], max_chunks), c1 = min(chunk_start[s + 1], max_chunks);
   float Mx = -INFINITY;
-  for (int cix = c0; cix < c1; ++cix) Mx = fmaxf(Mx, part[((size_t)cix * G + h) * PSTR + D]);
+  for (int sp = 0; sp < nsplit; ++sp) Mx = fmaxf(Mx, part[(((size_t)s * nsplit + sp) * G + h) * (D + 2) + D]);
   for (int e = threadIdx.x; e < D; e += blockDim.x) {
     float o = 0.f, l = 0.f;
-    for (int cix = c0; cix < c1; ++cix) {
-      const float* pp = part + ((size_t)cix * G + h) * PSTR;
-      const float sc = fast_exp2((pp[D] - Mx) * c2);
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* pp = part + (((size_t)s * nsplit + sp) * G + h) * (D + 2);
+      const float sc = (pp[D] == -INFINITY) ? 0.f : fast_exp2((pp[D] - Mx) * c2);
       o += sc * pp[e];
       l += sc * pp[D + 1];
     }
-    out[((size_t)inst * hq + j) * D + e] = o / l;
+    out[((size_t)inst * hq + jq) * D + e] = o / l;
   }
 }
 
-template <typename T, int D, int GT>
-hipError_t run_decode(const Geo& g, int64_t max_rows, const void* q, const void* k_new, const void* v_new,
-                      void* k_flat, void* v_flat, const int64_t* seg_start, int32_t* seg_len, float* out, char* ws,
-                      hipStream_t st) {
+// Splits per segment: one workgroup per segment when there are enough
+// segments to fill the chip, else enough splits of >= 2 chunks each.
+int choose_splits(const Geo& g, int64_t max_rows) {
   const int S = g.I * g.hkv;
-  int32_t* chunk_start = reinterpret_cast<int32_t*>(ws);
-  float* part = reinterpret_cast<float*>(ws + align_up((size_t)(S + 1) * 4, 256));
+  if (S >= 512) return 1;
+  const int64_t avg = max_rows / S;
+  int want = (1024 + S - 1) / S;
+  const int64_t lim = avg / (2 * CH);
+  if (want > lim) want = (int)lim;
+  return want < 1 ? 1 : want;
+}
+
+template <typename T, int D, int GT>
+hipError_t run_decode(const Geo& g, int64_t max_rows, int extra, const void* q, const void* k_new, const void* v_new,
+                      void* k_flat, void* v_flat, const int64_t* seg_start, const int32_t* seg_len, float* out,
+                      char* ws, hipStream_t st) {
+  const int S = g.I * g.hkv;
+  const int nsplit = choose_splits(g, max_rows);
   const float c2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
-  decode_prep_kernel<T, D><<<1, PT, 0, st>>>(static_cast<const T*>(k_new), static_cast<const T*>(v_new),
-                                             static_cast<T*>(k_flat), static_cast<T*>(v_flat), seg_start, seg_len, S,
-                                             chunk_start);
-  const int64_t max_chunks = max_rows / R + S;
-  decode_attn_kernel<T, D, GT><<<(unsigned)max_chunks, 256, 0, st>>>(
-      static_cast<const T*>(q), static_cast<const T*>(k_flat), static_cast<const T*>(v_flat), seg_start, seg_len,
-      chunk_start, S, g.hq, g.hkv, g.G, c2, part);
-  decode_merge_kernel<D><<<g.I * g.hq, D < 64 ? 64 : D, 0, st>>>(part, chunk_start, g.hq, g.hkv, g.G, (int)max_chunks,
-                                                                c2, out);
+  float* part = reinterpret_cast<float*>(ws);
+  const int append = k_new != nullptr;
+  decode_kernel<T, D, GT><<<(unsigned)(S * nsplit), 256, 0, st>>>(
+      static_cast<const T*>(q), static_cast<const T*>(k_new), static_cast<const T*>(v_new), static_cast<T*>(k_flat),
+      static_cast<T*>(v_flat), seg_start, seg_len, g.hq, g.hkv, g.G, nsplit, extra, append, c2, out, part);
+  if (nsplit > 1)
+    decode_merge_kernel<D><<<g.I * g.hq, D < 64 ? 64 : D, 0, st>>>(part, g.hq, g.hkv, g.G, nsplit, c2, out);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t run_decode_g(const Geo& g, int64_t max_rows, const void* q, const void* k_new, const void* v_new,
-                        void* k_flat, void* v_flat, const int64_t* seg_start, int32_t* seg_len, float* out, char* ws,
-                        hipStream_t st) {
-  if (g.G <= 1) return run_decode<T, D, 1>(g, max_rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
-  if (g.G <= 2) return run_decode<T, D, 2>(g, max_rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
-  if (g.G <= 4) return run_decode<T, D, 4>(g, max_rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
-  return run_decode<T, D, 8>(g, max_rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
+hipError_t run_decode_g(const Geo& g, int64_t max_rows, int extra, const void* q, const void* k_new,
+                        const void* v_new, void* k_flat, void* v_flat, const int64_t* seg_start,
+                        const int32_t* seg_len, float* out, char* ws, hipStream_t st) {
+#define RUN(GTV) run_decode<T, D, GTV>(g, max_rows, extra, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st)
+  if (g.G <= 1) return RUN(1);
+  if (g.G <= 2) return RUN(2);
+  if (g.G <= 4) return RUN(4);
+  return RUN(8);
+#undef RUN
 }
 
 }  // namespace
 
 size_t decode_ws_bytes(const Geo& g, int64_t max_rows) {
   const int S = g.I * g.hkv;
-  const int64_t max_chunks = max_rows / R + S;
-  return align_up((size_t)(S + 1) * 4, 256) + (size_t)max_chunks * g.G * (g.d + 2) * sizeof(float);
+  return (size_t)S * choose_splits(g, max_rows) * g.G * (g.d + 2) * sizeof(float);
 }
 
-hipError_t launch_decode(const Geo& g, int64_t max_rows, const void* q, const void* k_new, const void* v_new,
-                         void* k_flat, void* v_flat, const int64_t* seg_start, int32_t* seg_len, float* out,
-                         char* ws, hipStream_t st) {
+hipError_t launch_decode(const Geo& g, int64_t max_rows, int extra, const void* q, const void* k_new,
+                         const void* v_new, void* k_flat, void* v_flat, const int64_t* seg_start,
+                         const int32_t* seg_len, float* out, char* ws, hipStream_t st) {
   if (g.dtype == ADAKV_BF16) {
-    if (g.d == 128) return run_decode_g<uint16_t, 128>(g, max_rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
-    if (g.d == 64) return run_decode_g<uint16_t, 64>(g, max_rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
+    if (g.d == 128) return run_decode_g<uint16_t, 128>(g, max_rows, extra, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
+    if (g.d == 64) return run_decode_g<uint16_t, 64>(g, max_rows, extra, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
   } else {
-    if (g.d == 16) return run_decode_g<float, 16>(g, max_rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
-    if (g.d == 64) return run_decode_g<float, 64>(g, max_rows, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
+    if (g.d == 16) return run_decode_g<float, 16>(g, max_rows, extra, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
+    if (g.d == 64) return run_decode_g<float, 64>(g, max_rows, extra, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, out, ws, st);
   }
   return hipErrorInvalidValue;
 }

@@ -34,10 +34,10 @@ hipError_t launch_compact(const Geo& g, int64_t retained_rows, const void* k, co
                           void* k_flat, void* v_flat, int64_t* seg_start, int32_t* seg_len, hipStream_t st);
 
 // ---- decode (decode.hip)
-constexpr int DECODE_ROWS = 256;   // rows of one split-K chunk
 size_t decode_ws_bytes(const Geo& g, int64_t max_rows);
-hipError_t launch_decode(const Geo& g, int64_t max_rows, const void* q, const void* k_new, const void* v_new,
-                         void* k_flat, void* v_flat, const int64_t* seg_start, int32_t* seg_len,
-                         float* out, char* ws, hipStream_t st);
+// extra = appends made before this call + 1 if this call appends
+hipError_t launch_decode(const Geo& g, int64_t max_rows, int extra, const void* q, const void* k_new,
+                         const void* v_new, void* k_flat, void* v_flat, const int64_t* seg_start,
+                         const int32_t* seg_len, float* out, char* ws, hipStream_t st);
 
 }  // namespace adakv

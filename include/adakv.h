@@ -179,30 +179,34 @@ adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, 
  *   budgets, sel, sel_off                    as written by adakv_allocate
  *   k_flat, v_flat [rows, d] dtype out       rows = (sum of budgets) + I*hkv*(w + reserve)
  *   seg_start   [I*hkv + 1] int64 out        first row of every segment
- *   seg_len     [I*hkv]     int32 out        B_g + w (rows in use)
+ *   seg_len     [I*hkv]     int32 out        B_g + w (rows written here)
  */
 adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, const void* k, const void* v,
                            const int32_t* budgets, const int32_t* sel, const int64_t* sel_off,
                            int32_t reserve, void* k_flat, void* v_flat, int64_t* seg_start,
                            int32_t* seg_len, void* stream);
 
-/* Decode attention over the flat cache.  If k_new and v_new are given, first
- * every segment gets one more row at seg_start[s] + seg_len[s] and seg_len[s]
- * grows by one ([AdaKV-notes] the cache update before the output formula).
- * Then out[i, j] = softmax(q[i,j] . K_s / sqrt(d)) V_s over the seg_len[s] rows of
- * segment s = i*hkv + j/G.
+/* Decode attention over the flat cache.  Segment s holds seg_len[s] rows from
+ * adakv_compact plus the `step` rows appended by earlier decode calls.  If
+ * k_new and v_new are given, this call appends one more row to every segment
+ * (stored at seg_start[s] + seg_len[s] + step) before attending ([AdaKV-notes]
+ * the cache update before the output formula).  Then
+ *   out[i, j] = softmax(q[i,j] . K_s / sqrt(d)) V_s
+ * over the rows of segment s = i*hkv + j/G.  seg_len is read only: a call
+ * carries no state besides the appended rows, so the caller counts `step`.
  *
  *   q          [I, hq, d]    dtype
  *   k_new, v_new [I, hkv, d] dtype, both or neither (NULL = no append)
- *   k_flat, v_flat, seg_start, seg_len       from adakv_compact (seg_len updated in place)
+ *   k_flat, v_flat, seg_start, seg_len       from adakv_compact
  *   reserve    the reserve given to adakv_compact
- *   step       appends already made since adakv_compact (0 for the first decode);
- *              an append with step >= reserve returns ADAKV_ECAPACITY
+ *   step       rows appended since adakv_compact (0 for the first decode);
+ *              an append with step >= reserve returns ADAKV_ECAPACITY, and
+ *              step > reserve returns ADAKV_EINVAL
  *   out        [I, hq, d] float32 out
  * Needs G <= 8. */
 adakv_status adakv_decode_attn(const adakv_shape* shape, const adakv_alloc* alloc, const void* q,
                                const void* k_new, const void* v_new, void* k_flat, void* v_flat,
-                               const int64_t* seg_start, int32_t* seg_len, int32_t reserve, int32_t step,
+                               const int64_t* seg_start, const int32_t* seg_len, int32_t reserve, int32_t step,
                                float* out, void* ws, size_t ws_bytes, void* stream);
 
 /* A short, static description of a status code. */

@@ -232,7 +232,7 @@ def test_llama_model_full_sampled(gpu_lib):
     out = ev.out.cpu().numpy()
     P = cfg.budget - cfg.w * cfg.hkv
     assert int(off[-1]) == cfg.instances * P
-    assert np.all(sl == b.reshape(-1) + cfg.w + steps)
+    assert np.all(sl == b.reshape(-1) + cfg.w)        # decode leaves seg_len as compaction wrote it
     for i in (0, 77):
         q64 = pipeline.to_host_f64(data["q_win"][i])
         k64 = pipeline.to_host_f64(data["k"][i])
@@ -250,7 +250,7 @@ def test_llama_model_full_sampled(gpu_lib):
         vn = pipeline.to_host_f64(data["v_new"][:, i])
         for g in range(cfg.hkv):
             s = i * cfg.hkv + g
-            st0, ln = int(ss[s]), int(sl[s])
+            st0, ln = int(ss[s]), int(sl[s]) + steps
             kseg = pipeline.to_host_f64(kf_all[st0:st0 + ln])
             vseg = pipeline.to_host_f64(vf_all[st0:st0 + ln])
             assert np.array_equal(kseg, np.concatenate([kh[g], kn[:, g]])), f"K segment {s}"
