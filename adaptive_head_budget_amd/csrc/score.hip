@@ -19,6 +19,9 @@
 //    row weights summed, group maximum, times max_k ||V[k]||_1 / w, max pooled.
 //  * CriticalKV notes, "作为通用插件融入现有驱逐流水线": the per-query-head Ada-KV
 //    score is kept for the composite score.
+#include <algorithm>
+#include <cmath>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,7 +31,6 @@ namespace {
 constexpr int TILE = 128;          // keys per tile (8 M-blocks of 16)
 constexpr int HALO = 4;            // extra keys on each side of an emit tile
 constexpr int TROWS = TILE + 2 * HALO;
-constexpr int STATS_KEYS = 1024;   // keys per stats workgroup
 
 template <typename T, int D>
 struct Lay {
@@ -39,34 +41,71 @@ struct Lay {
   static constexpr int KSTEPS = D / Mma<T>::KSTEP;
 };
 
-// LDS row of key offset koff in [0, TILE): the 16 M-rows an A-operand read
-// touches map to 16 consecutive LDS rows.  Halo keys take rows TILE.. TILE+7.
+// LDS row of key offset koff in [0, TILE).  M-row m of M-block mb holds key
+// 32*(m/4) + 4*mb + (m%4) (so every lane of the MFMA result owns 32
+// consecutive keys); it is stored at LDS row 16*mb + m, so the lanes of one
+// A-operand read touch 16 consecutive rows (no bank conflicts with the odd
+// 16-byte row pitch).  Halo keys take rows TILE .. TILE+7.
 __device__ __forceinline__ int tile_row(int koff) {
   if (koff < 0) return TILE + (koff + HALO);
   if (koff >= TILE) return TILE + HALO + (koff - TILE);
-  return ((koff & 31) << 2) | (koff >> 5);
+  return (((koff >> 2) & 7) << 4) | ((koff >> 5) << 2) | (koff & 3);
 }
 
-// LDS row read by lane m (= lane % 16) of M-block mb.  Main blocks hold keys
-// 32*(m/4) + 4*mb + (m%4); the halo block (mb == 8) holds keys -4..-1 in lane
-// group 0 and TILE..TILE+3 in lane group 3 (groups 1, 2 read duplicates).
+// LDS row read by lane m (= lane % 16) of M-block mb.  The halo block
+// (mb == 8) holds keys -4..-1 in lane group 0 and TILE..TILE+3 in lane group 3
+// (groups 1, 2 read duplicates).
 __device__ __forceinline__ int a_row(int mb, int m) {
-  if (mb < 8) return 16 * mb + 4 * (m & 3) + (m >> 2);
+  if (mb < 8) return 16 * mb + m;
   return ((m >> 2) == 3) ? TILE + HALO + (m & 3) : TILE + (m & 3);
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void stage_tile(char* lds, const T* kb, int n, int k0, int koff_lo, int koff_hi) {
+// K tile staging in two halves so the global loads of tile t+1 are in
+// flight while tile t is multiplied: load() fills registers, store() moves
+// them to LDS.  Keys [k0 + KLO, k0 + KHI) of one head; keys outside [0, n)
+// become zero rows.  The per-thread chunk -> (source offset, LDS row) map is
+// the same for every tile and is computed once.  Needs >= 256 threads.
+template <typename T, int D, int KLO, int KHI>
+struct TileRegs {
   using L = Lay<T, D>;
-  const int cnt = (koff_hi - koff_lo) * L::CPR;
-  for (int idx = threadIdx.x; idx < cnt; idx += blockDim.x) {
-    const int koff = koff_lo + idx / L::CPR, ch = idx % L::CPR;
-    const int key = k0 + koff;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (key >= 0 && key < n) v = ld16(kb + (size_t)key * D + ch * L::EPC);
-    st16(lds + tile_row(koff) * L::STRIDE + ch * 16, v);
+  static constexpr int CHUNKS = (KHI - KLO) * L::CPR;
+  static constexpr int PER = (CHUNKS + 255) / 256;
+  u32x4 r[PER];
+  int src[PER];   // element offset from row k0 (key offset * D + chunk column)
+  int dst[PER];   // LDS byte offset, -1 when this thread has no chunk
+  int kof[PER];   // key offset of the chunk
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + i * (int)blockDim.x;
+      const int koff = KLO + idx / L::CPR, ch = idx % L::CPR;
+      kof[i] = koff;
+      src[i] = koff * D + ch * L::EPC;
+      dst[i] = (idx < CHUNKS) ? tile_row(koff) * L::STRIDE + ch * 16 : -1;
+    }
   }
-}
+  __device__ __forceinline__ void load(const T* kb, int n, int k0) {
+    const T* base = kb + (ptrdiff_t)k0 * D;
+    if (k0 + KLO >= 0 && k0 + KHI <= n) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (dst[i] >= 0) r[i] = ld16(base + src[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int key = k0 + kof[i];
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (dst[i] >= 0 && key >= 0 && key < n) v = ld16(base + src[i]);
+        r[i] = v;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (dst[i] >= 0) st16(lds + dst[i], r[i]);
+  }
+};
 
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2, float c2) {
   const float M = fmaxf(m, m2);
@@ -128,18 +167,23 @@ __device__ __forceinline__ float allsum16(float x) {
 }
 
 // ---------------------------------------------------------------- pass 1
+// Workgroup = max(G, 4) waves; wave h < G owns query head g*G + h (its w window
+// rows on the N side, NB blocks of 16); the others only help load K.
 template <typename T, int D, int NB, bool CAUSAL>
 __global__ __launch_bounds__(512) void score_stats_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float2* __restrict__ part, int inst0, int hq,
-    int hkv, int G, int n, int w, int p, int kend, int nchunk, float c2) {
+    int hkv, int G, int n, int w, int p, int kend, int nchunk, int keys_per_wg, float c2) {
   using L = Lay<T, D>;
   using M = Mma<T>;
   extern __shared__ __align__(16) char lds[];
   const int chunk = blockIdx.x, g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
   const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
   const int gq = lane >> 4, c = lane & 15;
+  const bool active = h < G;
   const T* kb = k + ((size_t)inst * hkv + g) * (size_t)n * D;
-  const T* qb = q + ((size_t)inst * hq + (size_t)g * G + h) * (size_t)w * D;
+  const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (active ? h : 0)) * (size_t)w * D;
+  // lane's A-operand row in LDS for M-block 0 (block mb adds 16 rows)
+  const char* a_base = lds + a_row(0, c) * L::STRIDE + M::KPL * gq * (int)sizeof(T);
 
   typename M::op_t qop[NB][L::KSTEPS];
 #pragma unroll
@@ -147,57 +191,76 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
     const int r = 16 * nb + c;
 #pragma unroll
     for (int ks = 0; ks < L::KSTEPS; ++ks)
-      qop[nb][ks] = (r < w) ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
+      qop[nb][ks] = (active && r < w) ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
   }
   float rm[NB], rl[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) { rm[nb] = -INFINITY; rl[nb] = 0.f; }
 
-  const int kbeg = chunk * STATS_KEYS;
-  const int kfin = min(kbeg + STATS_KEYS, kend);
+  const int kbeg = chunk * keys_per_wg;
+  const int kfin = min(kbeg + keys_per_wg, kend);
+  TileRegs<T, D, 0, TILE> tr;
+  tr.init();
+  tr.load(kb, n, kbeg);
   for (int k0 = kbeg; k0 < kfin; k0 += TILE) {
     __syncthreads();
-    stage_tile<T, D>(lds, kb, n, k0, 0, TILE);
+    tr.store(lds);
     __syncthreads();
+    if (k0 + TILE < kfin) tr.load(kb, n, k0 + TILE);     // next tile in flight
+    if (!active) continue;
     f32x4 acc[8][NB];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
-      const T* arow = reinterpret_cast<const T*>(lds + a_row(mb, c) * L::STRIDE);
+      const T* arow = reinterpret_cast<const T*>(a_base + mb * 16 * L::STRIDE);
 #pragma unroll
       for (int ks = 0; ks < L::KSTEPS; ++ks) {
-        const typename M::op_t a = M::load(arow + ks * M::KSTEP + M::KPL * gq);
+        const typename M::op_t a = M::load(arow + ks * M::KSTEP);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
       }
     }
+    // every key of the tile inside every row's domain: no per-key test
+    const bool full = k0 + TILE - 1 <= (CAUSAL ? min(kend - 1, p) : kend - 1);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int r = 16 * nb + c;
       const int lim = CAUSAL ? min(kend - 1, p + r) : kend - 1;   // last key of this row's domain
       float lm = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = k0 + 32 * gq + 4 * mb + j;
-          if (key <= lim) lm = fmaxf(lm, acc[mb][nb][j]);
-        }
-      if (lm != -INFINITY) {
-        float ls = 0.f;
+        for (int mb = 0; mb < 8; ++mb)
+          lm = fmax3(lm, fmax3(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2]), acc[mb][nb][3]);
+      } else {
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = k0 + 32 * gq + 4 * mb + j;
-            const float e = fast_exp2((acc[mb][nb][j] - lm) * c2);
-            ls += (key <= lim) ? e : 0.f;
-          }
+          for (int j = 0; j < 4; ++j)
+            if (k0 + 32 * gq + 4 * mb + j <= lim) lm = fmaxf(lm, acc[mb][nb][j]);
+      }
+      if (lm != -INFINITY) {
+        const float lmc = lm * c2;
+        float ls = 0.f;
+        if (full) {
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ls += fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float e = fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
+              ls += (k0 + 32 * gq + 4 * mb + j <= lim) ? e : 0.f;
+            }
+        }
         merge_ml(rm[nb], rl[nb], lm, ls, c2);
       }
     }
   }
+  if (!active) return;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -211,17 +274,26 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
   }
 }
 
-__global__ void score_stats_merge_kernel(const float2* __restrict__ part, float2* __restrict__ stats, int nrows,
-                                         int Gw, int nchunk, float c2) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per window row: merge the chunk partials (chunk order fixed by the
+// lane and the reduction tree) into (row max, 1 / row sum).
+__global__ __launch_bounds__(256) void score_stats_merge_kernel(const float2* __restrict__ part,
+                                                                float2* __restrict__ stats, int nrows, int Gw,
+                                                                int nchunk, float c2) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= nrows) return;
+  const int lane = threadIdx.x & 63;
   const int seg = t / Gw, row = t % Gw;
   float m = -INFINITY, l = 0.f;
-  for (int ch = 0; ch < nchunk; ++ch) {
+  for (int ch = lane; ch < nchunk; ch += 64) {
     const float2 v = part[((size_t)seg * nchunk + ch) * Gw + row];
     merge_ml(m, l, v.x, v.y, c2);
   }
-  stats[t] = make_float2(m, 1.0f / l);
+#pragma unroll
+  for (int mask = 1; mask < 64; mask <<= 1) {
+    const float om = shfl_xor(m, mask), ol = shfl_xor(l, mask);
+    merge_ml(m, l, om, ol, c2);
+  }
+  if (lane == 0) stats[t] = make_float2(m, 1.0f / l);
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -241,107 +313,170 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
   const int g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
   const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
   const int gq = lane >> 4, c = lane & 15;
+  const bool active = h < G;
   const int Gw = G * w;
   const T* kb = k + ((size_t)inst * hkv + g) * (size_t)n * D;
-  const T* qb = q + ((size_t)inst * hq + (size_t)g * G + h) * (size_t)w * D;
+  const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (active ? h : 0)) * (size_t)w * D;
+  const char* a_base = lds + a_row(0, c) * L::STRIDE + M::KPL * gq * (int)sizeof(T);
+  const char* a_halo = lds + a_row(8, c) * L::STRIDE + M::KPL * gq * (int)sizeof(T);
 
   typename M::op_t qop[NB][L::KSTEPS];
-  float sm[NB], sil[NB];
+  float smc[NB], sil[NB];   // row max * c2 and 1 / row sum
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int r = 16 * nb + c;
+    const bool ok = active && r < w;
 #pragma unroll
     for (int ks = 0; ks < L::KSTEPS; ++ks)
-      qop[nb][ks] = (r < w) ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
-    if (r < w) {
+      qop[nb][ks] = ok ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
+    if (ok) {
       const float2 st = stats[((size_t)il * hkv + g) * Gw + h * w + r];
-      sm[nb] = st.x;
+      smc[nb] = st.x * c2;
       sil[nb] = st.y;
     } else {
-      sm[nb] = 0.f;     // padding rows: q = 0, weight 0
+      smc[nb] = 0.f;    // padding rows: q = 0, weight 0
       sil[nb] = 0.f;
     }
   }
   const float vscale = (KIND == EMIT_LAVA) ? __uint_as_float(vbar_bits[(size_t)inst * hkv + g]) / (float)w : 0.f;
   const float inv_gw = 1.0f / (float)Gw, inv_w = 1.0f / (float)w;
 
+  const int t0 = blockIdx.x * tiles_per_wg;
+  TileRegs<T, D, -HALO, TILE + HALO> tr;
+  tr.init();
+  if (t0 * TILE < p) tr.load(kb, n, t0 * TILE);
   for (int t = 0; t < tiles_per_wg; ++t) {
-    const int k0 = (blockIdx.x * tiles_per_wg + t) * TILE;
+    const int k0 = (t0 + t) * TILE;
     if (k0 >= p) break;
     __syncthreads();
-    stage_tile<T, D>(lds, kb, n, k0, -HALO, TILE + HALO);
+    tr.store(lds);
     __syncthreads();
+    if (t + 1 < tiles_per_wg && k0 + TILE < p) tr.load(kb, n, k0 + TILE);   // next tile in flight
 
-    f32x4 acc[9][NB];
+    if (active) {
+      f32x4 acc[9][NB];
 #pragma unroll
-    for (int mb = 0; mb < 9; ++mb) {
+      for (int mb = 0; mb < 9; ++mb) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
-      const T* arow = reinterpret_cast<const T*>(lds + a_row(mb, c) * L::STRIDE);
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
+        const T* arow = reinterpret_cast<const T*>(mb < 8 ? a_base + mb * 16 * L::STRIDE : a_halo);
 #pragma unroll
-      for (int ks = 0; ks < L::KSTEPS; ++ks) {
-        const typename M::op_t a = M::load(arow + ks * M::KSTEP + M::KPL * gq);
+        for (int ks = 0; ks < L::KSTEPS; ++ks) {
+          const typename M::op_t a = M::load(arow + ks * M::KSTEP);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
+        }
+      }
+      const int kbase = k0 + 32 * gq;   // first key of this lane group
+
+      if (KIND == EMIT_SNAP) {
+        const bool interior = k0 >= 3 && k0 + TILE + 3 <= p;   // all pooled keys inside the prefix
+        float ks[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) ks[i] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          // x[t] <-> key kbase - 3 + t, t in [0, 38); outside the prefix -> -inf
+          float x[38];
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[3 + 4 * mb + j] = acc[mb][nb][j];
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            const float lft = shfl_lane(acc[7][nb][1 + j], (lane - 16) & 63);
+            const float rgt = shfl_lane(acc[0][nb][j], (lane + 16) & 63);
+            x[j] = (gq == 0) ? acc[8][nb][1 + j] : lft;
+            x[35 + j] = (gq == 3) ? acc[8][nb][j] : rgt;
+          }
+          if (!interior) {
+#pragma unroll
+            for (int t2 = 0; t2 < 38; ++t2) {
+              const int key = kbase - 3 + t2;
+              if (key < 0 || key >= p) x[t2] = -INFINITY;
+            }
+          }
+          const float mc = smc[nb], il_row = sil[nb];
+          if (RHO == 3) {
+            float a3[36];
+#pragma unroll
+            for (int t2 = 0; t2 < 36; ++t2) a3[t2] = fmax3(x[t2], x[t2 + 1], x[t2 + 2]);
+#pragma unroll
+            for (int kk = 0; kk < 32; ++kk) {
+              const float pooled = fmax3(a3[kk], a3[kk + 2], a3[kk + 4]);
+              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
+            }
+          } else {
+#pragma unroll
+            for (int kk = 0; kk < 32; ++kk) {
+              float pooled = x[kk + 3];
+              if (RHO >= 1) pooled = fmax3(pooled, x[kk + 2], x[kk + 4]);
+              if (RHO >= 2) pooled = fmax3(pooled, x[kk + 1], x[kk + 5]);
+              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
+            }
+          }
+        }
+        float s0, s1;
+        reduce_scatter16(ks, c, s0, s1);
+        hs[h * TILE + 32 * gq + 2 * c] = s0;
+        hs[h * TILE + 32 * gq + 2 * c + 1] = s1;
+      } else {
+        // LAVa: causal weights summed over the head's rows, before pooling.
+        const bool interior = k0 >= HALO && k0 + TILE + HALO <= p;   // every key <= p <= p + r, >= 0
+        float ks[32], hsum[4];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) ks[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hsum[j] = 0.f;
+        const int hkey0 = (gq == 0) ? k0 - HALO : ((gq == 3) ? k0 + TILE : -1);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int r = 16 * nb + c;
+          const int lim = min(n - 1, p + r);
+          const float mc = smc[nb], il_row = sil[nb];
+          if (interior) {
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                ks[4 * mb + j] = fmaf(fast_exp2(fmaf(acc[mb][nb][j], c2, -mc)), il_row, ks[4 * mb + j]);
+          } else {
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float e = fast_exp2(fmaf(acc[mb][nb][j], c2, -mc));
+                ks[4 * mb + j] += (kbase + 4 * mb + j <= lim) ? e * il_row : 0.f;
+              }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = hkey0 + j;
+            const float e = fast_exp2(fmaf(acc[8][nb][j], c2, -mc));
+            hsum[j] += (hkey0 >= 0 && key >= 0 && key <= lim) ? e * il_row : 0.f;
+          }
+        }
+        float s0, s1;
+        reduce_scatter16(ks, c, s0, s1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hsum[j] = allsum16(hsum[j]);
+        float* hrow = hs + h * TROWS;
+        hrow[HALO + 32 * gq + 2 * c] = s0;
+        hrow[HALO + 32 * gq + 2 * c + 1] = s1;
+        if (c == 0 && gq == 0)
+          for (int j = 0; j < 4; ++j) hrow[j] = hsum[j];
+        if (c == 0 && gq == 3)
+          for (int j = 0; j < 4; ++j) hrow[HALO + TILE + j] = hsum[j];
       }
     }
-    const int kbase = k0 + 32 * gq;   // first key of this lane group
-
+    __syncthreads();
     if (KIND == EMIT_SNAP) {
-      float ks[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) ks[i] = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // x[t] <-> key kbase - 3 + t, t in [0, 38); outside the prefix -> -inf
-        float x[38];
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x[3 + 4 * mb + j] = acc[mb][nb][j];
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          const float lft = shfl_lane(acc[7][nb][1 + j], (lane - 16) & 63);
-          const float rgt = shfl_lane(acc[0][nb][j], (lane + 16) & 63);
-          x[j] = (gq == 0) ? acc[8][nb][1 + j] : lft;
-          x[35 + j] = (gq == 3) ? acc[8][nb][j] : rgt;
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 38; ++t2) {
-          const int key = kbase - 3 + t2;
-          if (key < 0 || key >= p) x[t2] = -INFINITY;
-        }
-        const float mrow = sm[nb], il_row = sil[nb];
-        if (RHO == 3) {
-          float a[36];
-#pragma unroll
-          for (int t2 = 0; t2 < 36; ++t2) a[t2] = fmax3(x[t2], x[t2 + 1], x[t2 + 2]);
-#pragma unroll
-          for (int kk = 0; kk < 32; ++kk) {
-            const float pooled = fmax3(a[kk], a[kk + 2], a[kk + 4]);
-            ks[kk] += fast_exp2((pooled - mrow) * c2) * il_row;
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < 32; ++kk) {
-            float pooled = x[kk + 3];
-            if (RHO >= 1) pooled = fmax3(pooled, x[kk + 2], x[kk + 4]);
-            if (RHO >= 2) pooled = fmax3(pooled, x[kk + 1], x[kk + 5]);
-            ks[kk] += fast_exp2((pooled - mrow) * c2) * il_row;
-          }
-        }
-      }
-      float s0, s1;
-      reduce_scatter16(ks, c, s0, s1);
-      hs[h * TILE + 32 * gq + 2 * c] = s0;
-      hs[h * TILE + 32 * gq + 2 * c + 1] = s1;
-      __syncthreads();
       for (int t2 = threadIdx.x; t2 < TILE; t2 += blockDim.x) {
         const int key = k0 + t2;
         if (key < p) {
-          float s = 0.f;
-          for (int hh = 0; hh < G; ++hh) s += hs[hh * TILE + t2];
-          score[((size_t)inst * hkv + g) * p + key] = s * inv_gw;
+          float sum = 0.f;
+          for (int hh = 0; hh < G; ++hh) sum += hs[hh * TILE + t2];
+          score[((size_t)inst * hkv + g) * p + key] = sum * inv_gw;
         }
       }
       if (head_scores != nullptr) {
@@ -352,45 +487,6 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
         }
       }
     } else {
-      // LAVa: causal weights summed over the head's rows, before pooling.
-      float ks[32], hsum[4];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) ks[i] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hsum[j] = 0.f;
-      const int hkey0 = (gq == 0) ? k0 - HALO : ((gq == 3) ? k0 + TILE : -1);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int r = 16 * nb + c;
-        const int lim = min(n - 1, p + r);
-        const float mrow = sm[nb], il_row = sil[nb];
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = kbase + 4 * mb + j;
-            const float e = fast_exp2((acc[mb][nb][j] - mrow) * c2) * il_row;
-            ks[4 * mb + j] += (key <= lim) ? e : 0.f;
-          }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = hkey0 + j;
-          const float e = fast_exp2((acc[8][nb][j] - mrow) * c2) * il_row;
-          hsum[j] += (hkey0 >= 0 && key >= 0 && key <= lim) ? e : 0.f;
-        }
-      }
-      float s0, s1;
-      reduce_scatter16(ks, c, s0, s1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) hsum[j] = allsum16(hsum[j]);
-      float* hrow = hs + h * TROWS;
-      hrow[HALO + 32 * gq + 2 * c] = s0;
-      hrow[HALO + 32 * gq + 2 * c + 1] = s1;
-      if (c == 0 && gq == 0)
-        for (int j = 0; j < 4; ++j) hrow[j] = hsum[j];
-      if (c == 0 && gq == 3)
-        for (int j = 0; j < 4; ++j) hrow[HALO + TILE + j] = hsum[j];
-      __syncthreads();
       for (int t2 = threadIdx.x; t2 < TROWS; t2 += blockDim.x) {
         float m = hs[t2];
         for (int hh = 1; hh < G; ++hh) m = fmaxf(m, hs[hh * TROWS + t2]);
@@ -468,7 +564,7 @@ ScorePlan plan_score(const Geo& g) {
   if (ib > (size_t)g.I) ib = g.I;
   P.ib = (int)ib;
   P.kend = (g.scorer == ADAKV_SCORE_LAVA) ? g.n : g.p;
-  P.nchunk = (P.kend + STATS_KEYS - 1) / STATS_KEYS;
+  P.nchunk = (P.kend + TILE - 1) / TILE;   // the most chunks a launch can use (one tile each)
   const size_t Gw = (size_t)g.G * g.w;
   size_t off = 0;
   P.off_part = off;  off = align_up(off + (size_t)P.ib * g.hkv * P.nchunk * Gw * sizeof(float2), 256);
@@ -493,7 +589,7 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   const T* qt = static_cast<const T*>(q);
   const T* kt = static_cast<const T*>(k);
   const bool lava = g.scorer == ADAKV_SCORE_LAVA;
-  const int threads = g.G * WAVE;
+  const int threads = std::max(g.G, 4) * WAVE;
   const int Gw = g.G * g.w;
   const size_t lds_stats = (size_t)TILE * L::STRIDE;
   const size_t lds_emit = (size_t)TROWS * L::STRIDE + (size_t)(g.G + 1) * TROWS * sizeof(float);
@@ -506,19 +602,29 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
     dim3 grid((g.n + rows_per_wg - 1) / rows_per_wg, g.hkv, g.I);
     vbar_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(v), vbar, 0, g.hkv, g.n, rows_per_wg);
   }
+  // about two resident workgroups per CU, each streaming many tiles
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const long target = 2L * (cus > 0 ? cus : 256);
+  const int ktiles = (P.kend + TILE - 1) / TILE;
   for (int i0 = 0; i0 < g.I; i0 += P.ib) {
     const int ni = std::min(P.ib, g.I - i0);
-    dim3 g1(P.nchunk, g.hkv, ni);
+    const long stiles = (long)ktiles * g.hkv * ni;
+    const int spw = (int)std::min<long>(ktiles, std::max<long>(1, stiles / target));
+    const int kpw = spw * TILE;
+    const int nchunk = (P.kend + kpw - 1) / kpw;
+    dim3 g1(nchunk, g.hkv, ni);
     if (lava)
       score_stats_kernel<T, D, NB, true><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
-                                                                         g.w, g.p, P.kend, P.nchunk, c2);
+                                                                         g.w, g.p, P.kend, nchunk, kpw, c2);
     else
       score_stats_kernel<T, D, NB, false><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
-                                                                          g.w, g.p, P.kend, P.nchunk, c2);
+                                                                          g.w, g.p, P.kend, nchunk, kpw, c2);
     const int nrows = ni * g.hkv * Gw;
-    score_stats_merge_kernel<<<(nrows + 255) / 256, 256, 0, st>>>(part, stats, nrows, Gw, P.nchunk, c2);
+    score_stats_merge_kernel<<<(nrows + 3) / 4, 256, 0, st>>>(part, stats, nrows, Gw, nchunk, c2);
     const long tiles_total = (long)ntiles * g.hkv * ni;
-    int tpw = (int)std::max<long>(1, tiles_total / 2048);
+    int tpw = (int)std::max<long>(1, (tiles_total + target - 1) / target);
     if (tpw > ntiles) tpw = ntiles;
     dim3 g2((ntiles + tpw - 1) / tpw, g.hkv, ni);
 #define EMIT(POOLV)                                                                                          \

@@ -89,6 +89,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="llama3.1-8b_32L_b4_n32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this size once (a plain copy kernel of known size, "
+                         "used to calibrate HBM byte counters in a profiled run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the eviction path has no multi-GPU "
@@ -132,6 +135,12 @@ def main():
         if rec is not None:
             rec.append((e, dec))
 
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         one_step(None)
     torch.cuda.synchronize()
