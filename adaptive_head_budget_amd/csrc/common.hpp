@@ -16,6 +16,11 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 // Raw 16-byte global / LDS moves (callers guarantee 16-byte alignment).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Streaming (nontemporal) forms for data read or written once.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p)); }
 
 // One 16x16 MFMA step per element type.  Lane l supplies A[m = l%16][KPL*(l/16) .. +KPL)
 // and B[KPL*(l/16) .. +KPL)[n = l%16]; the result D[m = 4*(l/16)+j][n = l%16], j < 4,
@@ -27,6 +32,7 @@ template <> struct Mma<uint16_t> {   // bf16 storage
   static constexpr int KPL = 8;      // K elements per lane
   typedef bf16x8 op_t;
   __device__ __forceinline__ static op_t load(const uint16_t* p) { return *reinterpret_cast<const op_t*>(p); }
+  __device__ __forceinline__ static op_t load_nt(const uint16_t* p) { return __builtin_bit_cast(op_t, ld16_nt(p)); }
   __device__ __forceinline__ static op_t zero() { u32x4 z = {0u, 0u, 0u, 0u}; return __builtin_bit_cast(op_t, z); }
   __device__ __forceinline__ static f32x4 mma(op_t a, op_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -38,6 +44,7 @@ template <> struct Mma<float> {
   static constexpr int KPL = 1;
   typedef float op_t;
   __device__ __forceinline__ static op_t load(const float* p) { return *p; }
+  __device__ __forceinline__ static op_t load_nt(const float* p) { return __builtin_nontemporal_load(p); }
   __device__ __forceinline__ static op_t zero() { return 0.f; }
   __device__ __forceinline__ static f32x4 mma(op_t a, op_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

@@ -8,10 +8,12 @@
 // query heads of a GQA group share every row read.
 //
 // One workgroup streams one segment (or one of `nsplit` row ranges of it when
-// segments are too few to fill the chip).  Each of its 4 waves takes 64 rows of
-// every 256-row chunk: q.K^T on 16x16 MFMA tiles (rows on M, query heads on N),
-// an online softmax per wave, and the value sum on the vector units with
-// 16-byte coalesced V loads.  The new row of an append is read straight from
+// segments are too few to fill the chip).  Each of its 4 waves takes 32 rows of
+// every 128-row chunk: keys go straight to LDS with coalesced direct loads,
+// q.K^T runs on 16x16 MFMA tiles (rows on M, query heads on N), an online
+// softmax per wave, and the value sum on the vector units with 16-byte
+// coalesced V loads.  Waves only touch their own LDS, so they never wait for
+// each other inside the chunk loop.  The new row of an append is read straight from
 // k_new/v_new and also stored into the segment's reserved rows for later steps;
 // seg_len is never modified (a call attends over seg_len + step (+1) rows), so
 // a decode call carries no state from the previous one.
@@ -21,8 +23,15 @@
 namespace adakv {
 namespace {
 
-constexpr int CH = 256;   // rows per chunk (4 waves x 64)
+constexpr int WR = 32;          // rows per wave per chunk
+constexpr int CH = 4 * WR;      // rows per chunk (4 waves)
 
+// Keys reach LDS with 16-byte direct-to-LDS loads: lane l of a load writes
+// LDS bytes [16*l, 16*l + 16) of the instruction's 1 KB block (4 rows), so
+// 16 lanes move one full 256-byte row and every load is coalesced.  Lane
+// (row r, slot cs) fetches 16-byte chunk cs ^ (r & 15) of the row; an MFMA
+// read of chunk ch of row r then uses slot ch ^ (r & 15), and the 16 rows of
+// one read land in 16 different bank groups.
 template <typename T, int D, int GT>
 __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                      const T* __restrict__ v_new, T* __restrict__ kf,
@@ -32,12 +41,17 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
                                                      float* __restrict__ out, float* __restrict__ part) {
   using M = Mma<T>;
   constexpr int KSTEPS = D / M::KSTEP;
+  constexpr int ROWB = D * (int)sizeof(T);     // bytes per row
+  constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                // rows per direct load
   constexpr int EPL = 16 / (int)sizeof(T);     // value elements per lane
   constexpr int LPR = D / EPL;                 // lanes per value row
   constexpr int RS = WAVE / LPR;               // row slots per wave
-  constexpr int RPL = 64 / RS;                 // value rows per lane per chunk
-  __shared__ float P[2][4][64][GT];
-  __shared__ float Sc[2][4][GT];
+  constexpr int RPL = WR / RS;                 // value rows per lane per chunk
+  constexpr int MB = WR / 16;                  // M-blocks per wave
+  __shared__ __align__(16) char kbuf[4][WR * ROWB];
+  __shared__ float P[4][WR][GT];
+  __shared__ float Sc[4][GT];
   __shared__ float Ow[4][GT][D];
   __shared__ float Mw[4][GT], Lw[4][GT];
 
@@ -60,18 +74,21 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   const int rs = lane / LPR, cc = lane % LPR;
   const T* knew_s = k_new + (size_t)s * D;
   const T* vnew_s = v_new + (size_t)s * D;
+  char* kb = kbuf[wv];
 
-  if (do_append && split == 0 && threadIdx.x < D / (16 / (int)sizeof(T))) {
-    constexpr int EPC = 16 / (int)sizeof(T);
-    st16(kf + (base + newrow) * D + threadIdx.x * EPC, ld16(knew_s + threadIdx.x * EPC));
-    st16(vf + (base + newrow) * D + threadIdx.x * EPC, ld16(vnew_s + threadIdx.x * EPC));
+  if (do_append && split == 0 && threadIdx.x < CPR) {
+    st16(kf + (base + newrow) * D + threadIdx.x * EPL, ld16(knew_s + threadIdx.x * EPL));
+    st16(vf + (base + newrow) * D + threadIdx.x * EPL, ld16(vnew_s + threadIdx.x * EPL));
   }
 
+  // B operand: q^T, column c = query head of the group (zero beyond G).
   typename M::op_t qop[KSTEPS];
   const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (c < G ? c : 0)) * D;
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) qop[ks] = (c < G) ? M::load(qb + ks * M::KSTEP + M::KPL * gq) : M::zero();
 
+  // this lane's part of every direct key load: row lr of each 4-row block, chunk slot cs
+  const int lr = lane / CPR, cs = lane % CPR;
   float m_run = -INFINITY, l_run = 0.f;   // per query head c (same in the 4 lane groups)
   float o[GT][EPL];
 #pragma unroll
@@ -79,30 +96,43 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
 
-  int buf = 0;
-  for (int c0 = r_begin; c0 < r_end; c0 += CH, buf ^= 1) {
-    const int wrow0 = c0 + 64 * wv;
-    // issue the value loads first: they do not depend on the scores
+  for (int c0 = r_begin; c0 < r_end; c0 += CH) {
+    const int wrow0 = c0 + WR * wv;
+    // keys: direct to LDS, rows wrow0 .. wrow0 + WR - 1
+#pragma unroll
+    for (int i = 0; i < WR / RPI; ++i) {
+      const int rr = i * RPI + lr;
+      const int r = wrow0 + rr;
+      const T* src = (r == newrow) ? knew_s : kf + (base + (r < r_end ? r : r_begin)) * D;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + ((cs ^ (rr & 15)) % CPR) * EPL),
+                                       static_cast<void*>(&kbuf[wv][i * 1024]), 16, 0, 0);
+    }
+    // values: registers
     u32x4 vraw[RPL];
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
       const int r = wrow0 + t * RS + rs;
       const T* src = (r == newrow) ? vnew_s : vf + (base + (r < r_end ? r : r_begin)) * D;
-      vraw[t] = ld16(src + cc * EPL);
+      vraw[t] = ld16_nt(src + cc * EPL);
     }
-    f32x4 acc[4];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // keys in LDS, values in registers
+    f32x4 acc[MB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       acc[mb] = zero4();
-      const int r = wrow0 + 16 * mb + c;
-      const T* krow = (r == newrow) ? knew_s : kf + (base + (r < r_end ? r : r_begin)) * D;
+      const int rr = 16 * mb + c;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) acc[mb] = M::mma(M::load(krow + ks * M::KSTEP + M::KPL * gq), qop[ks], acc[mb]);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int ch = (ks * M::KSTEP + M::KPL * gq) / EPL;     // 16-byte chunk of this operand
+        const T* ap = reinterpret_cast<const T*>(kb + rr * ROWB + (((ch ^ (rr & 15)) % CPR) * 16)) +
+                      (ks * M::KSTEP + M::KPL * gq) % EPL;
+        acc[mb] = M::mma(M::load(ap), qop[ks], acc[mb]);
+      }
     }
     // acc[mb][j] <-> row wrow0 + 16*mb + 4*gq + j, query head c
     float mc = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (wrow0 + 16 * mb + 4 * gq + j < r_end) mc = fmaxf(mc, acc[mb][j]);
@@ -110,25 +140,26 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     mc = fmaxf(mc, shfl_xor(mc, 32));
     const float m_new = fmaxf(m_run, mc);
     const float sc_run = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * c2);
+    const float mnc = m_new * c2;
     float lc = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = 16 * mb + 4 * gq + j;
-        const float e = (wrow0 + rr < r_end) ? fast_exp2((acc[mb][j] - m_new) * c2) : 0.f;
+        const float e = (wrow0 + rr < r_end) ? fast_exp2(fmaf(acc[mb][j], c2, -mnc)) : 0.f;
         lc += e;
-        if (c < GT) P[buf][wv][rr][c] = e;
+        if (c < GT) P[wv][rr][c] = e;
       }
     lc += shfl_xor(lc, 16);
     lc += shfl_xor(lc, 32);
     l_run = l_run * sc_run + lc;
     m_run = m_new;
-    if (gq == 0 && c < GT) Sc[buf][wv][c] = sc_run;
-    __syncthreads();
+    if (gq == 0 && c < GT) Sc[wv][c] = sc_run;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's P / Sc writes are visible to its lanes
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-      const float sh = Sc[buf][wv][h];
+      const float sh = Sc[wv][h];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] *= sh;
     }
@@ -148,11 +179,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
       }
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        const float pw = P[buf][wv][rr][h];   // 0 for rows past the end
+        const float pw = P[wv][rr][h];   // 0 for rows past the end
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[h][e] += pw * vv[e];
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS reads done before the next chunk overwrites kbuf / P
   }
   // sum the row slots of each wave, then combine the waves in order
 #pragma unroll

@@ -164,3 +164,11 @@ def test_decode_rejects(L):
     assert dec(None, None, 2, 3) == lib.ADAKV_EINVAL             # more appends than rows reserved
     assert dec(FAKE, FAKE, 2, 0, ws_bytes=8) == lib.ADAKV_EWORKSPACE
     assert dec(FAKE, FAKE, 2, 0, shape=_shape(hq=80, hkv=8)) == lib.ADAKV_EUNSUPPORTED
+
+
+def test_no_undefined_kernel_stubs(L):
+    """Every kernel launched from host code has its host-side stub in the
+    library (a stub can silently go missing when a device-only construct is
+    rejected by the host compilation pass)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", lib.LIB_PATH], capture_output=True, text=True).stdout
+    assert "device_stub" not in out
