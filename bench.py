@@ -24,6 +24,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+DECODE_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_llama3.1-8b_32L_b4_n32768.md")
+DECODE_SOURCES = [os.path.join(ROOT, "adaptive_head_budget_amd", "csrc", f) for f in ("decode.hip", "common.hpp")]
+
+
+def measured_traffic(cfg_name: str):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when that summary covers another workload or
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    if cfg_name != "llama3.1-8b_32L_b4_n32768" or not os.path.exists(DECODE_PROFILE):
+        return None
+    fields = {}
+    for line in open(DECODE_PROFILE):
+        if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(f, "rb").read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def decode_bytes(cfg, rows_before: int, append: bool) -> int:
@@ -182,7 +204,7 @@ def main():
         out["decode_hbm_gbps"] = achieved
         out["roofline"] = {"kernel": "adakv_decode_attn", "bound": "hbm", "achieved": achieved,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                           "traffic": None, "algorithmic_bytes_per_launch": per_launch_bytes,
+                           "traffic": measured_traffic(cfg.name), "algorithmic_bytes_per_launch": per_launch_bytes,
                            "avg_launch_ms": avg_launch_s * 1e3}
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
