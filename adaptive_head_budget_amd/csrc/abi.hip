@@ -129,7 +129,6 @@ adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, 
   if (!aligned16(score) || !aligned16(budgets) || !aligned16(sel_off) || !aligned16(ws)) return ADAKV_EINVAL;
   if (selected_rows(*alloc, g) > 0 && !aligned16(sel)) return ADAKV_EINVAL;
   if (alloc->mode == ADAKV_ALLOC_ADA_CRITICALKV && !aligned16(score2)) return ADAKV_EINVAL;
-  if (alloc->mode == ADAKV_ALLOC_ADA_CRITICALKV && (size_t)(g.p + 31) / 32 * 4 > 96 * 1024) return ADAKV_EUNSUPPORTED;
   if (alloc->mode == ADAKV_ALLOC_LAVA_LAYERS && g.I > 4096) return ADAKV_EUNSUPPORTED;
   if (ws_bytes < alloc_ws_bytes(g, *alloc)) return ADAKV_EWORKSPACE;
   return hip_status(launch_allocate(g, *alloc, score, score2, budgets, sel, sel_off, static_cast<char*>(ws),

@@ -1,11 +1,20 @@
 // Budget allocation and selection on gfx950.
 //
-// Top-k over non-negative fp32 scores is a radix select on the bit patterns
-// (4 passes of 8 bits, most significant first): it yields a threshold key T and
-// the number of entries equal to T that are kept.  Entries equal to T are kept
-// in index order, so the result is the first k of the order (-score, index)
-// and is exactly reproducible.  One workgroup of 1024 threads owns one segment
-// (an instance for the layer-wide top-B, a head for the per-head top-k).
+// Top-k over non-negative fp32 scores is a radix select on the bit patterns,
+// most significant digit first: bits [30:20], [19:9], [8:0] (bit 31 is zero for
+// every non-negative score).  The select yields a threshold key T and the number
+// of entries equal to T that are kept; entries equal to T are kept in index
+// order, so the result is the first k of the order (-score, index) and is
+// exactly reproducible.
+//
+// Every streaming pass is spread over the whole chip: a score row (one KV head
+// of one instance) is cut into chunks of up to 4096 scores, one workgroup per
+// chunk, each thread holding up to 16 consecutive scores.  A segment is the unit
+// a top-k runs over: an instance (all its heads, for the layer-wide top-B) or a
+// single row (a head's own top-k).  Chunks add their digit histogram into the
+// segment's histogram with global atomics and end; a small kernel with one
+// workgroup per segment then picks the digit and clears the histogram for the
+// next pass.  No workgroup ever waits for another.
 //
 // Definitions followed:
 //  * Ada-KV notes, Algorithm 1 (concatenate the heads, top-B, count per head)
@@ -23,56 +32,34 @@
 namespace adakv {
 namespace {
 
-constexpr int ST = 1024;        // threads of a selection workgroup
-constexpr int NW = ST / WAVE;   // waves
+constexpr int SB = 256;             // threads of a selection workgroup
+constexpr int SW = SB / WAVE;       // waves
+constexpr int TILE = SB * 4;        // scores per chunk for each unit of ntile
+constexpr int MAXT = 4;             // ntile <= MAXT: up to 4 * MAXT consecutive scores per thread
+constexpr int NK = 4 * MAXT;
+constexpr int NBIN = 2048;          // histogram bins (11-bit digits)
 constexpr uint32_t NONE = 0xFFFFFFFFu;
 
-__device__ __forceinline__ uint64_t lanemask_lt() {
-  const int l = (int)__lane_id();
-  return l == 0 ? 0ull : (~0ull >> (64 - l));
-}
-
-// Adds one to arr[key] for every lane with key != NONE.  The most common keys
-// of the wave are added with one atomic each.
-__device__ __forceinline__ void wave_count(uint32_t* arr, uint32_t key) {
-#pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const uint64_t act = __ballot(key != NONE);
-    if (act == 0) return;
-    const int leader = __ffsll((unsigned long long)act) - 1;
-    const uint32_t lk = (uint32_t)__shfl((int)key, leader);
-    const uint64_t same = __ballot(key == lk);
-    if ((int)__lane_id() == leader) atomicAdd(arr + lk, (uint32_t)__popcll(same));
-    if (key == lk) key = NONE;
-  }
-  if (key != NONE) atomicAdd(arr + key, 1u);
-}
-
-struct SelShared {
-  uint32_t hist[NW][256];
-  uint32_t tot[256];
-  uint32_t misc[8];
-  uint32_t wsum[NW];
-  uint32_t wsum2[NW];
+struct RState {                     // radix state of a segment
+  uint32_t prefix;                  // digits fixed so far; after the last pass: T (NONE = take nothing)
+  int32_t krem;                     // entries still to take below the prefix; at the end: ties to keep
 };
 
-// Exclusive count of `pred` over the workgroup in thread order, plus the total.
-__device__ __forceinline__ uint32_t block_excl(SelShared& sh, bool pred, uint32_t& total) {
-  const uint64_t b = __ballot(pred);
-  const int wv = threadIdx.x / WAVE;
-  if (__lane_id() == 0) sh.wsum[wv] = (uint32_t)__popcll(b);
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t s = sh.wsum[i];
-    before += (i < wv) ? s : 0u;
-    all += s;
-  }
-  __syncthreads();
-  total = all;
-  return before + (uint32_t)__popcll(b & lanemask_lt());
+// Keys of the select: the bit pattern of a non-negative float orders like its
+// value.  Negative inputs (outside the scores' domain) count as zero.
+__device__ __forceinline__ uint32_t sel_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u >> 31) ? 0u : u;
 }
+
+__device__ __forceinline__ int digit_shift(int ps) { return ps == 0 ? 20 : (ps == 1 ? 9 : 0); }
+__device__ __forceinline__ uint32_t digit_of(uint32_t u, int ps) {
+  return ps == 0 ? (u >> 20) : (ps == 1 ? ((u >> 9) & 2047u) : (u & 511u));
+}
+__device__ __forceinline__ bool in_prefix(uint32_t u, uint32_t prefix, int ps) {
+  return ps == 0 ? true : (ps == 1 ? ((u >> 20) == (prefix >> 20)) : ((u >> 9) == (prefix >> 9)));
+}
+__device__ __forceinline__ int pass_bins(int ps) { return ps == 2 ? 512 : NBIN; }
 
 // Exclusive scan over the 64 lanes of a wave (lane 0 first).
 __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t x) {
@@ -85,300 +72,327 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t x) {
   return inc - x;
 }
 
-// Radix select of the `kth` largest keys among entries for which keep(idx)
-// holds.  Returns threshold T and quota (entries == T to take, in index order).
-template <class KeyF, class KeepF>
-__device__ void radix_select(SelShared& sh, int L, int kth, KeyF key, KeepF keep, uint32_t& T, int& quota) {
-  if (kth <= 0) {
-    T = NONE;
-    quota = 0;
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += (uint32_t)__shfl_xor((int)x, off);
+  return x;
+}
+
+// Exclusive scan over the workgroup in thread order, plus the total.  sh: SW words.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* sh, uint32_t& total) {
+  const uint32_t ex = wave_excl_scan(x);
+  const int wv = threadIdx.x / WAVE;
+  if ((threadIdx.x & (WAVE - 1)) == WAVE - 1) sh[wv] = ex + x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < SW; ++i) {
+    const uint32_t s = sh[i];
+    before += (i < wv) ? s : 0u;
+    all += s;
+  }
+  __syncthreads();
+  total = all;
+  return before + ex;
+}
+
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* sh) {
+  uint32_t t;
+  block_excl_scan(x, sh, t);
+  return t;
+}
+
+// Digit pick over nb bins (bin(b) gives the count of digit b): the digit d with
+// count(> d) < krem <= count(>= d).  Returns d and count(> d) to every thread.
+// sh: SW + 2 words.
+template <class BinF>
+__device__ void block_pick(BinF bin, int nb, uint32_t krem, uint32_t* sh, uint32_t& dig, uint32_t& above_out) {
+  const int bpt = nb / SB;            // 8 or 2 bins per thread, from the top
+  uint32_t c[8];
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c[j] = (j < bpt) ? bin(nb - 1 - ((int)threadIdx.x * bpt + j)) : 0u;
+    s += c[j];
+  }
+  if (threadIdx.x == 0) { sh[SW] = 0u; sh[SW + 1] = 0u; }
+  uint32_t total;
+  uint32_t above = block_excl_scan(s, sh, total);
+  if (above < krem && krem <= above + s) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < bpt && above < krem && krem <= above + c[j]) {
+        sh[SW] = (uint32_t)(nb - 1 - ((int)threadIdx.x * bpt + j));
+        sh[SW + 1] = above;
+      }
+      above += c[j];
+    }
+  }
+  __syncthreads();
+  dig = sh[SW];
+  above_out = sh[SW + 1];
+  __syncthreads();
+}
+
+// The chunk of a workgroup: row r, scores [e_begin, e_end) of the row.
+struct Chunk {
+  int r, c, e_begin, e_end;
+};
+__device__ __forceinline__ Chunk chunk_of(int cpr, int ntile, int p) {
+  Chunk k;
+  k.r = blockIdx.x / cpr;
+  k.c = blockIdx.x % cpr;
+  k.e_begin = k.c * ntile * TILE;
+  k.e_end = min(p, k.e_begin + ntile * TILE);
+  return k;
+}
+
+// The thread's scores: [e0, e0 + 4*ntile) with e0 = e_begin + 4*ntile*tid, in
+// index order; the first n of them lie inside the chunk.  Every load is issued
+// before any is used: addresses past the chunk are clamped to its last score
+// (16-byte groups for rows of a multiple of 4 scores on a 16-byte aligned base,
+// single scores otherwise), so a partial chunk costs no more than a full one.
+struct ChunkKeys {
+  uint32_t k[NK];
+  int e0, n;
+};
+__device__ __forceinline__ void load_chunk(const float* row, const Chunk& ch, int ntile, bool vec, ChunkKeys& K) {
+  const int npt = 4 * ntile;
+  K.e0 = ch.e_begin + npt * (int)threadIdx.x;
+  K.n = max(0, min(npt, ch.e_end - K.e0));
+  if (vec) {
+    f32x4 v[MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+      v[t] = *reinterpret_cast<const f32x4*>(row + min(K.e0 + 4 * (t < ntile ? t : 0), ch.e_end - 4));
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) K.k[4 * t + j] = sel_key(v[t][j]);
     return;
   }
-  uint32_t prefix = 0, mask = 0;
-  int krem = kth;
-  const int wv = threadIdx.x / WAVE;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = threadIdx.x; i < NW * 256; i += ST) (&sh.hist[0][0])[i] = 0u;
-    __syncthreads();
-    for (int base = 0; base < L; base += ST) {
-      const int idx = base + threadIdx.x;
-      uint32_t d = NONE;
-      if (idx < L && keep(idx)) {
-        const uint32_t u = key(idx);
-        if ((u & mask) == prefix) d = (u >> shift) & 255u;
-      }
-      wave_count(sh.hist[wv], d);
-    }
-    __syncthreads();
-    if (threadIdx.x < 256) {
-      uint32_t t = 0;
+  float v[NK];
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) t += sh.hist[w2][threadIdx.x];
-      sh.tot[threadIdx.x] = t;
-    }
-    __syncthreads();
-    if (threadIdx.x < WAVE) {
-      const int lane = threadIdx.x;
-      uint32_t c4[4], s = 0;
+  for (int j = 0; j < NK; ++j) v[j] = row[min(K.e0 + (j < npt ? j : 0), ch.e_end - 1)];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { c4[q] = sh.tot[255 - 4 * lane - q]; s += c4[q]; }
-      uint32_t above = wave_excl_scan(s);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (above < (uint32_t)krem && (uint32_t)krem <= above + c4[q]) {
-          sh.misc[0] = 255u - 4u * lane - q;
-          sh.misc[1] = above;
-        }
-        above += c4[q];
-      }
-    }
-    __syncthreads();
-    const uint32_t b = sh.misc[0], above = sh.misc[1];
-    prefix |= b << shift;
-    mask |= 255u << shift;
-    krem -= (int)above;
-    __syncthreads();
-  }
-  T = prefix;
-  quota = krem;
+  for (int j = 0; j < NK; ++j) K.k[j] = sel_key(v[j]);
 }
 
-// Writes the indices selected by (key > T) or (key == T and tie rank < quota),
-// ascending, to out[].  Optionally only among entries with keep(idx).
-template <class KeyF, class KeepF>
-__device__ void emit_ordered(SelShared& sh, int L, KeyF key, KeepF keep, uint32_t T, int quota, int32_t* out,
-                             int cap) {
-  uint32_t ties = 0, sel = 0;
-  for (int base = 0; base < L; base += ST) {
-    const int idx = base + threadIdx.x;
-    const bool ok = idx < L && keep(idx);
-    const uint32_t u = ok ? key(idx) : 0u;
-    const bool eq = ok && T != NONE && u == T;
-    const bool gt = ok && T != NONE && u > T;
-    uint32_t teq;
-    const uint32_t rank = ties + block_excl(sh, eq, teq);
-    const bool take = gt || (eq && rank < (uint32_t)quota);
-    uint32_t tsel;
-    const uint32_t pos = sel + block_excl(sh, take, tsel);
-    if (take && pos < (uint32_t)cap) out[pos] = idx;
-    ties += teq;
-    sel += tsel;
-  }
-}
-
-// ---------------------------------------------------------------- layer-wide top-B
-// mode ADA / CK: k = P (host), budgets by safeguard.  LAVA: k from klist, budgets = counts,
-// and every head's share of the threshold ties is stored for the emission.
-__global__ __launch_bounds__(ST) void select_layer_kernel(const float* __restrict__ score, int hkv, int p, int P,
-                                                          const int64_t* __restrict__ klist, int alpha_num,
-                                                          int alpha_den, int lava, int32_t* __restrict__ budgets,
-                                                          uint32_t* __restrict__ hthr, int32_t* __restrict__ hquota,
-                                                          int64_t* __restrict__ sel_off, int n_inst) {
-  __shared__ SelShared sh;
-  __shared__ uint32_t cnt_gt[256], cnt_eq[256];
-  __shared__ int64_t qv[256], rv[256];
-  __shared__ int64_t sums[2];
-  const int inst = blockIdx.x;
-  const float* x = score + (size_t)inst * hkv * p;
-  const int L = hkv * p;
-  const int k = lava ? (int)klist[inst] : P;
-  auto key = [&](int i) { return score_key(x[i]); };
-  auto all = [](int) { return true; };
-  uint32_t T;
-  int quota;
-  radix_select(sh, L, k, key, all, T, quota);
-
-  for (int i = threadIdx.x; i < hkv; i += ST) { cnt_gt[i] = 0u; cnt_eq[i] = 0u; }
-  __syncthreads();
-  const int wv = threadIdx.x / WAVE;
-  (void)wv;
-  for (int base = 0; base < L; base += ST) {
-    const int idx = base + threadIdx.x;
-    uint32_t hg = NONE, he = NONE;
-    if (idx < L && T != NONE) {
-      const uint32_t u = key(idx);
-      const uint32_t hd = (uint32_t)(idx / p);
-      if (u > T) hg = hd;
-      else if (u == T) he = hd;
-    }
-    wave_count(cnt_gt, hg);
-    wave_count(cnt_eq, he);
-  }
-  __syncthreads();
-  if (threadIdx.x < hkv) {
-    const int g = threadIdx.x;
-    int64_t before = 0;
-    for (int j = 0; j < g; ++j) before += cnt_eq[j];
-    int64_t share = (int64_t)quota - before;
-    share = share < 0 ? 0 : (share > (int64_t)cnt_eq[g] ? (int64_t)cnt_eq[g] : share);
-    const int64_t f = (int64_t)cnt_gt[g] + share;
-    const size_t s = (size_t)inst * hkv + g;
-    if (lava) {
-      budgets[s] = (int32_t)f;
-      hthr[s] = T;
-      hquota[s] = (int32_t)share;
-    } else {
-      const int64_t a = alpha_num, b = alpha_den, h = hkv;
-      const int64_t num = a * h * f + (b - a) * (int64_t)k;
-      const int64_t den = b * h;
-      qv[g] = num / den;
-      rv[g] = num % den;
-    }
-  }
-  __syncthreads();
-  if (!lava) {
-    if (threadIdx.x == 0) {
-      int64_t sq = 0;
-      for (int j = 0; j < hkv; ++j) sq += qv[j];
-      sums[0] = (int64_t)k - sq;
-    }
-    __syncthreads();
-    if (threadIdx.x < hkv) {
-      const int g = threadIdx.x;
-      int rank = 0;
-      for (int j = 0; j < hkv; ++j) rank += (rv[j] > rv[g] || (rv[j] == rv[g] && j < g)) ? 1 : 0;
-      budgets[(size_t)inst * hkv + g] = (int32_t)(qv[g] + (rank < sums[0] ? 1 : 0));
-    }
-    if (threadIdx.x == 0) {
-      sel_off[inst] = (int64_t)inst * k;
-      if (inst == n_inst - 1) sel_off[n_inst] = (int64_t)n_inst * k;
-    }
-  }
-}
-
-// ---------------------------------------------------------------- per-head selection
-enum { HEAD_ADA = 0, HEAD_LAVA = 1, HEAD_CK = 2 };
-
-__global__ __launch_bounds__(ST) void select_head_kernel(const float* __restrict__ score,
-                                                         const float* __restrict__ score2, int hkv, int p,
-                                                         int mode, int ck_num, int ck_den,
-                                                         const int32_t* __restrict__ budgets,
-                                                         const uint32_t* __restrict__ hthr,
-                                                         const int32_t* __restrict__ hquota,
-                                                         const int64_t* __restrict__ sel_off,
-                                                         int32_t* __restrict__ sel) {
-  __shared__ SelShared sh;
-  extern __shared__ uint32_t member[];   // CriticalKV stage-1 membership bits, (p + 31) / 32 words
-  const int s = blockIdx.x, inst = s / hkv, g = s % hkv;
-  const float* x = score + (size_t)s * p;
-  const int B = budgets[s];
-  int64_t base = sel_off[inst];
-  for (int j = 0; j < g; ++j) base += budgets[(size_t)inst * hkv + j];
-  int32_t* out = sel + base;
-  auto keyA = [&](int i) { return score_key(x[i]); };
-  auto all = [](int) { return true; };
-  if (mode == HEAD_LAVA) {
-    emit_ordered(sh, p, keyA, all, hthr[s], hquota[s], out, B);
+// Member flags of the thread's scores (CriticalKV stage 1), clamped like the scores.
+__device__ __forceinline__ void load_member(const uint8_t* mrow, const Chunk& ch, int ntile, bool vec,
+                                            const ChunkKeys& K, uint8_t m[NK]) {
+  if (vec) {
+    uint32_t w[MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+      w[t] = *reinterpret_cast<const uint32_t*>(mrow + min(K.e0 + 4 * (t < ntile ? t : 0), ch.e_end - 4));
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m[4 * t + j] = (uint8_t)((w[t] >> (8 * j)) & 255u);
     return;
   }
-  if (mode == HEAD_ADA) {
-    uint32_t T;
-    int q;
-    radix_select(sh, p, B, keyA, all, T, q);
-    emit_ordered(sh, p, keyA, all, T, q, out, B);
-    return;
-  }
-  // CriticalKV two-stage.
-  const int b1 = (int)(((int64_t)B * ck_num) / ck_den);
-  const int b2 = B - b1;
-  uint32_t* mem = member;
-  uint32_t T1;
-  int q1;
-  radix_select(sh, p, b1, keyA, all, T1, q1);
-  {
-    uint32_t ties = 0;
-    for (int base2 = 0; base2 < p; base2 += ST) {
-      const int idx = base2 + threadIdx.x;
-      const bool ok = idx < p;
-      const uint32_t u = ok ? keyA(idx) : 0u;
-      const bool eq = ok && T1 != NONE && u == T1;
-      const bool gt = ok && T1 != NONE && u > T1;
-      uint32_t teq;
-      const uint32_t rank = ties + block_excl(sh, eq, teq);
-      const bool in1 = gt || (eq && rank < (uint32_t)q1);
-      const uint64_t bits = __ballot(in1);
-      if (__lane_id() == 0) {
-        const int wi = (base2 + (threadIdx.x & ~63)) / 32;
-        if (wi * 32 < p) mem[wi] = (uint32_t)bits;
-        if ((wi + 1) * 32 < p) mem[wi + 1] = (uint32_t)(bits >> 32);
-      }
-      ties += teq;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) m[j] = mrow[min(K.e0 + (j < 4 * ntile ? j : 0), ch.e_end - 1)];
+}
+
+// Counts the chunk's eligible digits into the LDS histogram h.  A thread's
+// scores are neighbours in the row (pooled scores come in plateaus), so equal
+// digits in a row of them go in with one atomic.
+__device__ __forceinline__ void chunk_hist(uint32_t* h, const ChunkKeys& K, const uint8_t (&m)[NK], bool use_m,
+                                           uint32_t prefix, int ps) {
+  uint32_t cur = NONE, run = 0;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const uint32_t u = K.k[j];
+    const bool el = j < K.n && (!use_m || m[j] == 0) && in_prefix(u, prefix, ps);
+    const uint32_t d = el ? digit_of(u, ps) : NONE;
+    if (d != cur) {
+      if (cur != NONE) atomicAdd(h + cur, run);
+      cur = d;
+      run = 0;
     }
+    ++run;
   }
-  __syncthreads();
-  const float* y = score2 + (size_t)s * p;
-  auto keyB = [&](int i) { return score_key(y[i]); };
-  auto notin1 = [&](int i) { return ((mem[i >> 5] >> (i & 31)) & 1u) == 0u; };
-  uint32_t T2;
-  int q2;
-  radix_select(sh, p, b2, keyB, notin1, T2, q2);
-  uint32_t ties2 = 0, sel_n = 0;
-  for (int base2 = 0; base2 < p; base2 += ST) {
-    const int idx = base2 + threadIdx.x;
-    const bool ok = idx < p;
-    const bool in1 = ok && !notin1(idx);
-    const uint32_t u = ok ? keyB(idx) : 0u;
-    const bool eq2 = ok && !in1 && T2 != NONE && u == T2;
-    const bool gt2 = ok && !in1 && T2 != NONE && u > T2;
-    uint32_t teq;
-    const uint32_t rank = ties2 + block_excl(sh, eq2, teq);
-    const bool take = in1 || gt2 || (eq2 && rank < (uint32_t)q2);
-    uint32_t tsel;
-    const uint32_t pos = sel_n + block_excl(sh, take, tsel);
-    if (take && pos < (uint32_t)B) out[pos] = idx;
-    ties2 += teq;
-    sel_n += tsel;
+  if (cur != NONE) atomicAdd(h + cur, run);
+}
+
+// Picks the digit of pass ps from the histogram hs (global, complete) and
+// clears it, also for a segment with nothing left to take (a first-pass
+// histogram holds counts even then).  st is the state before the pass.
+__device__ __forceinline__ RState pick_and_clear(uint32_t* hs, int ps, RState st, uint32_t* sh) {
+  const int nb = pass_bins(ps);
+  RState out = {NONE, 0};
+  if (st.krem > 0 && st.prefix != NONE) {
+    uint32_t d, above;
+    block_pick([&](int b) { return hs[b]; }, nb, (uint32_t)st.krem, sh, d, above);
+    out.prefix = st.prefix | (d << digit_shift(ps));
+    out.krem = st.krem - (int32_t)above;
+  }
+  for (int b = threadIdx.x; b < nb; b += SB) hs[b] = 0u;
+  return out;
+}
+
+// ---------------------------------------------------------------- zero fill
+__global__ __launch_bounds__(SB) void sel_zero_kernel(u32x4* __restrict__ p, size_t n16) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * SB + threadIdx.x; i < n16; i += (size_t)gridDim.x * SB) p[i] = z;
+}
+
+// ---------------------------------------------------------------- digit histograms
+// Adds the chunk's LDS histogram (nb bins) into the global one.
+__device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* hg, int nb) {
+  for (int b = threadIdx.x; b < nb; b += SB) {
+    const uint32_t v = h[b];
+    if (v) atomicAdd(hg + b, v);
   }
 }
 
-// ---------------------------------------------------------------- LAVa layer budgets
-// Per layer: S = sum s, Q = sum s ln s in fp64; e_l = (ln S - Q / S) / (hkv * p).
-__global__ __launch_bounds__(ST) void lava_entropy_kernel(const float* __restrict__ score, int hkv, int p,
-                                                          double* __restrict__ ent) {
-  __shared__ double red[2][NW];
-  const int l = blockIdx.x;
-  const float* x = score + (size_t)l * hkv * p;
-  const int L = hkv * p;
-  double S = 0.0, Q = 0.0;
-  for (int i = threadIdx.x; i < L; i += ST) {
-    const double v = (double)x[i];
-    S += v;
-    Q += (v > 0.0) ? v * log(v) : 0.0;
+// One digit pass over segments of seg_rows rows: the histogram of the digits
+// of pass ps among the candidates that match the segment's prefix.  Pass 0
+// takes k from kinit[segment], later passes continue from st[segment].  With
+// member flags, flagged scores are not candidates.
+__global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict__ score,
+                                                        const uint8_t* __restrict__ member, int p, int cpr,
+                                                        int ntile, int vec, int seg_rows, int ps,
+                                                        const int32_t* __restrict__ kinit,
+                                                        const RState* __restrict__ st, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[NBIN];
+  const Chunk ch = chunk_of(cpr, ntile, p);
+  const int s = ch.r / seg_rows;
+  RState cur;
+  if (ps == 0) {
+    cur.prefix = 0u;
+    cur.krem = kinit[s];
+  } else {
+    cur = st[s];
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    S += __shfl_xor(S, off);
-    Q += __shfl_xor(Q, off);
-  }
-  const int wv = threadIdx.x / WAVE;
-  if (__lane_id() == 0) { red[0][wv] = S; red[1][wv] = Q; }
+  if (cur.krem <= 0 || cur.prefix == NONE) return;
+  const int nb = pass_bins(ps);
+  ChunkKeys K;
+  uint8_t m[NK];
+  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  if (member) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
+  for (int b = threadIdx.x; b < nb; b += SB) h[b] = 0u;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  chunk_hist(h, K, m, member != nullptr, cur.prefix, ps);
+  __syncthreads();
+  flush_hist(h, hist + (size_t)s * NBIN, nb);
+}
+
+// The digit pick of pass ps for every segment, one workgroup each; pass 0
+// starts from kinit[segment].
+__global__ __launch_bounds__(SB) void radix_pick_kernel(uint32_t* __restrict__ hist, int ps,
+                                                        const int32_t* __restrict__ kinit, RState* __restrict__ st) {
+  __shared__ uint32_t sh[SW + 4];
+  const int s = blockIdx.x;
+  RState cur;
+  if (ps == 0) {
+    cur.prefix = 0u;
+    cur.krem = kinit[s];
+  } else {
+    cur = st[s];
+  }
+  const RState nx = pick_and_clear(hist + (size_t)s * NBIN, ps, cur, sh);
+  if (threadIdx.x == 0) st[s] = nx;
+}
+
+// ---------------------------------------------------------------- layer pass 0
+// First digit pass of the layer-wide top-k, kept per row (the row histograms
+// also serve each head's own top-k later).  For LAVa each chunk also leaves its
+// partial sums S = sum s and Q = sum s ln s (fp64) for the layer entropy.
+__global__ __launch_bounds__(SB) void layer_hist0_kernel(const float* __restrict__ score, int p, int cpr, int ntile,
+                                                         int vec, int lava, uint32_t* __restrict__ rowhist,
+                                                         double* __restrict__ part) {
+  __shared__ uint32_t h[NBIN];
+  __shared__ double dsh[2][SW];
+  const Chunk ch = chunk_of(cpr, ntile, p);
+  ChunkKeys K;
+  uint8_t m[NK];
+  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  for (int b = threadIdx.x; b < NBIN; b += SB) h[b] = 0u;
+  __syncthreads();
+  chunk_hist(h, K, m, false, 0u, 0);
+  if (lava) {
+    double S = 0.0, Q = 0.0;
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const double v = (double)__uint_as_float(K.k[j]);
+      if (j < K.n && v > 0.0) {
+        S += v;
+        Q += v * log(v);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      S += __shfl_xor(S, off);
+      Q += __shfl_xor(Q, off);
+    }
+    const int wv = threadIdx.x / WAVE;
+    if ((threadIdx.x & (WAVE - 1)) == 0) { dsh[0][wv] = S; dsh[1][wv] = Q; }
+  }
+  __syncthreads();
+  if (lava && threadIdx.x == 0) {
     double s2 = 0.0, q2 = 0.0;
-    for (int i = 0; i < NW; ++i) { s2 += red[0][i]; q2 += red[1][i]; }
-    ent[l] = (s2 > 0.0) ? (log(s2) - q2 / s2) / (double)L : 0.0;
+    for (int i = 0; i < SW; ++i) { s2 += dsh[0][i]; q2 += dsh[1][i]; }
+    part[2 * (size_t)blockIdx.x] = s2;
+    part[2 * (size_t)blockIdx.x + 1] = q2;
   }
+  flush_hist(h, rowhist + (size_t)ch.r * NBIN, NBIN);
 }
 
-// One workgroup: B'_l = largest remainder of B' * e_l / sum(e), sel_off = scan.
-__global__ __launch_bounds__(ST) void lava_budget_kernel(const double* __restrict__ ent, int L, int64_t Bp,
-                                                         int64_t* __restrict__ klist, int64_t* __restrict__ sel_off) {
+// First digit pick of every layer-wide top-k (one workgroup per instance) from
+// the sum of its rows' histograms, with k = kP, or klist[instance] for LAVa.
+// The row histograms are kept.
+__global__ __launch_bounds__(SB) void layer_pick0_kernel(const uint32_t* __restrict__ rowhist, int hkv, int kP,
+                                                         const int64_t* __restrict__ klist, RState* __restrict__ seg) {
+  __shared__ uint32_t sh[SW + 4];
+  const int inst = blockIdx.x;
+  const int k = klist ? (int)klist[inst] : kP;
+  if (k <= 0) {
+    if (threadIdx.x == 0) { RState none = {NONE, 0}; seg[inst] = none; }
+    return;
+  }
+  const uint32_t* h0 = rowhist + (size_t)inst * hkv * NBIN;
+  uint32_t d, above;
+  block_pick(
+      [&](int b) {
+        uint32_t t = 0;
+#pragma unroll 8
+        for (int g = 0; g < hkv; ++g) t += h0[(size_t)g * NBIN + b];
+        return t;
+      },
+      NBIN, (uint32_t)k, sh, d, above);
+  if (threadIdx.x == 0) { RState x = {d << 20, k - (int32_t)above}; seg[inst] = x; }
+}
+
+// LAVa: per layer, S and Q from the chunk partials in a fixed order,
+// e_l = (ln S - Q / S) / (hkv * p); then B'_l = largest remainder of
+// B' * e_l / sum(e) (equal remainders: lower layer first) and sel_off = scan.
+__global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restrict__ part, int L, int chunks_per_layer,
+                                                         int hkv, int p, int64_t Bp, int64_t* __restrict__ klist,
+                                                         int64_t* __restrict__ sel_off) {
   extern __shared__ __align__(16) char smem[];
-  double* rem = reinterpret_cast<double*>(smem);
+  double* rem = reinterpret_cast<double*>(smem);     // e_l first, then the remainders
   int64_t* fl = reinterpret_cast<int64_t*>(rem + L);
   __shared__ double Esh;
   __shared__ int64_t def;
+  for (int l = threadIdx.x; l < L; l += SB) {
+    double S = 0.0, Q = 0.0;
+    const double* pl = part + 2 * (size_t)l * chunks_per_layer;
+    for (int c = 0; c < chunks_per_layer; ++c) { S += pl[2 * c]; Q += pl[2 * c + 1]; }
+    rem[l] = (S > 0.0) ? (log(S) - Q / S) / ((double)hkv * (double)p) : 0.0;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     double E = 0.0;
-    for (int i = 0; i < L; ++i) E += ent[i];
+    for (int i = 0; i < L; ++i) E += rem[i];
     Esh = E;
   }
   __syncthreads();
   const double E = Esh;
-  for (int l = threadIdx.x; l < L; l += ST) {
-    const double x = (E > 0.0) ? ((double)Bp * ent[l]) / E : (double)Bp / (double)L;
+  for (int l = threadIdx.x; l < L; l += SB) {
+    const double x = (E > 0.0) ? ((double)Bp * rem[l]) / E : (double)Bp / (double)L;
     const double f = floor(x);
     fl[l] = (int64_t)f;
     rem[l] = x - f;
@@ -390,7 +404,7 @@ __global__ __launch_bounds__(ST) void lava_budget_kernel(const double* __restric
     def = Bp - s;
   }
   __syncthreads();
-  for (int l = threadIdx.x; l < L; l += ST) {
+  for (int l = threadIdx.x; l < L; l += SB) {
     int64_t rank = 0;
     for (int j = 0; j < L; ++j) rank += (rem[j] > rem[l] || (rem[j] == rem[l] && j < l)) ? 1 : 0;
     klist[l] = fl[l] + (rank < def ? 1 : 0);
@@ -403,52 +417,353 @@ __global__ __launch_bounds__(ST) void lava_budget_kernel(const double* __restric
   }
 }
 
+// ---------------------------------------------------------------- layer counts and budgets
+enum { MODE_ADA = 0, MODE_LAVA = 1, MODE_CK = 2 };
+
+// Per row: entries above the instance's layer threshold T and equal to it.
+__global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict__ score, int p, int cpr, int ntile,
+                                                         int vec, int hkv, const RState* __restrict__ seg,
+                                                         uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t sh[SW + 4];
+  const Chunk ch = chunk_of(cpr, ntile, p);
+  const RState L = seg[ch.r / hkv];
+  if (L.prefix == NONE) return;
+  ChunkKeys K;
+  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    gt += (j < K.n && K.k[j] > L.prefix) ? 1u : 0u;
+    eq += (j < K.n && K.k[j] == L.prefix) ? 1u : 0u;
+  }
+  const uint32_t both = block_sum(gt | (eq << 16), sh);   // at most 4096 of each
+  if (threadIdx.x == 0) {
+    if (both & 0xFFFFu) atomicAdd(cnt + 2 * (size_t)ch.r, both & 0xFFFFu);
+    if (both >> 16) atomicAdd(cnt + 2 * (size_t)ch.r + 1, both >> 16);
+  }
+}
+
+// One workgroup per row r (head g of instance i).  From the counts of the
+// instance's rows: the heads' layer counts f_g (ties shared out in flat index
+// order), then
+//  * Ada-KV / CriticalKV: the budget B_g by the safeguard, the row's offset in
+//    sel, the row's k for its own top-k (B_g, or b'_g = floor(B_g * ck_num /
+//    ck_den) for CriticalKV stage 1, b''_g = B_g - b'_g kept for stage 2) and
+//    the first digit pick of that top-k from the row's pass-0 histogram;
+//  * LAVa: B_g = f_g; the row keeps the layer threshold with its share of the ties.
+// Every workgroup of an instance computes the same head values.
+__global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int kP, int alpha_num, int alpha_den,
+                                                        int ck_num, int ck_den, int n_inst,
+                                                        const RState* __restrict__ seg,
+                                                        const uint32_t* __restrict__ cnt,
+                                                        uint32_t* __restrict__ rowhist, int32_t* __restrict__ budgets,
+                                                        int64_t* __restrict__ rowbase, int32_t* __restrict__ rowk2,
+                                                        RState* __restrict__ rowst, int64_t* __restrict__ sel_off) {
+  __shared__ uint32_t sh[SW + 4];
+  __shared__ int64_t gt_sh[256], eq_sh[256], f_sh[256], q_sh[256], r_sh[256];
+  __shared__ int64_t k1_sh, def_sh;
+  const int r = blockIdx.x, inst = r / hkv, g = r % hkv, r0 = inst * hkv;
+  const RState L = seg[inst];
+  for (int j = threadIdx.x; j < hkv; j += SB) {
+    gt_sh[j] = cnt[2 * (size_t)(r0 + j)];
+    eq_sh[j] = cnt[2 * (size_t)(r0 + j) + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t quota = (L.prefix == NONE) ? 0 : L.krem;
+    int64_t before = 0;
+    for (int j = 0; j < hkv; ++j) {
+      int64_t share = quota - before;
+      share = share < 0 ? 0 : (share > eq_sh[j] ? eq_sh[j] : share);
+      before += eq_sh[j];
+      f_sh[j] = gt_sh[j] + share;
+      q_sh[j] = share;
+    }
+  }
+  __syncthreads();
+  if (mode == MODE_LAVA) {
+    if (threadIdx.x == 0) {
+      int64_t base = sel_off[inst];
+      for (int j = 0; j < g; ++j) base += f_sh[j];
+      budgets[r] = (int32_t)f_sh[g];
+      rowbase[r] = base;
+      RState x = {L.prefix, (int32_t)q_sh[g]};
+      if (L.prefix == NONE) { x.prefix = NONE; x.krem = 0; }
+      rowst[r] = x;
+    }
+    return;
+  }
+  // Safeguard in exact integers: N_g = a*h*f_g + (b-a)*P over Den = b*h, floors
+  // plus one unit to the P - sum(floor) largest remainders (lower head first).
+  const int64_t a = alpha_num, b = alpha_den, h = hkv;
+  for (int j = threadIdx.x; j < hkv; j += SB) {
+    const int64_t num = a * h * f_sh[j] + (b - a) * (int64_t)kP;
+    const int64_t den = b * h;
+    q_sh[j] = num / den;
+    r_sh[j] = num % den;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t sq = 0;
+    for (int j = 0; j < hkv; ++j) sq += q_sh[j];
+    def_sh = (int64_t)kP - sq;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < hkv; j += SB) {
+    int rank = 0;
+    for (int i = 0; i < hkv; ++i) rank += (r_sh[i] > r_sh[j] || (r_sh[i] == r_sh[j] && i < j)) ? 1 : 0;
+    f_sh[j] = q_sh[j] + (rank < def_sh ? 1 : 0);     // B_j
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t base = (int64_t)inst * kP;
+    for (int j = 0; j < g; ++j) base += f_sh[j];
+    const int64_t Bg = f_sh[g];
+    const int64_t k1 = (mode == MODE_CK) ? (Bg * ck_num) / ck_den : Bg;
+    budgets[r] = (int32_t)Bg;
+    rowbase[r] = base;
+    if (mode == MODE_CK) rowk2[r] = (int32_t)(Bg - k1);
+    k1_sh = k1;
+    if (g == 0) {
+      sel_off[inst] = (int64_t)inst * kP;
+      if (inst == n_inst - 1) sel_off[n_inst] = (int64_t)n_inst * kP;
+    }
+  }
+  __syncthreads();
+  RState init = {0u, (int32_t)k1_sh};
+  const RState x = pick_and_clear(rowhist + (size_t)r * NBIN, 0, init, sh);
+  if (threadIdx.x == 0) rowst[r] = x;
+}
+
+// ---------------------------------------------------------------- per-chunk counts and emission
+// Class of a score against a row's (T, quota): 2 = kept (above T, or a stage-1
+// member when member flags are given), 1 = tie (equal to T), 0 = dropped.
+__device__ __forceinline__ int klass(uint32_t u, bool ok, bool mem, uint32_t T) {
+  if (!ok) return 0;
+  if (mem) return 2;
+  if (T == NONE) return 0;
+  return u > T ? 2 : (u == T ? 1 : 0);
+}
+
+__global__ __launch_bounds__(SB) void chunk_count_kernel(const float* __restrict__ score,
+                                                         const uint8_t* __restrict__ member, int p, int cpr,
+                                                         int ntile, int vec, const RState* __restrict__ rowst,
+                                                         uint32_t* __restrict__ cc) {
+  __shared__ uint32_t sh[SW + 4];
+  const Chunk ch = chunk_of(cpr, ntile, p);
+  const RState S = rowst[ch.r];
+  ChunkKeys K;
+  uint8_t m[NK];
+  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  if (member) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
+  uint32_t n2 = 0, n1 = 0;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int kc = klass(K.k[j], j < K.n, member != nullptr && m[j] != 0, S.prefix);
+    n2 += kc == 2 ? 1u : 0u;
+    n1 += kc == 1 ? 1u : 0u;
+  }
+  const uint32_t both = block_sum(n2 | (n1 << 16), sh);   // at most 4096 of each
+  if (threadIdx.x == 0) {
+    cc[2 * (size_t)blockIdx.x] = both & 0xFFFFu;
+    cc[2 * (size_t)blockIdx.x + 1] = both >> 16;
+  }
+}
+
+// Writes the kept scores of the chunk in index order: as token indices at
+// sel[rowbase[r] + position] (at most cap[r] of them, never past sel_total), or
+// as member flags.
+__global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ score, const uint8_t* __restrict__ member,
+                                                  int p, int cpr, int ntile, int vec, const RState* __restrict__ rowst,
+                                                  const uint32_t* __restrict__ cc, const int64_t* __restrict__ rowbase,
+                                                  const int32_t* __restrict__ cap, int32_t* __restrict__ sel,
+                                                  int64_t sel_total, uint8_t* __restrict__ member_out) {
+  __shared__ uint32_t sh[SW + 4];
+  __shared__ uint32_t before_sh[2][SW];
+  const Chunk ch = chunk_of(cpr, ntile, p);
+  const RState S = rowst[ch.r];
+  ChunkKeys K;
+  uint8_t m[NK];
+  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  if (member) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
+  // Kept scores and ties of the row's earlier chunks.
+  uint32_t b2 = 0, b1 = 0;
+  for (int c = threadIdx.x; c < ch.c; c += SB) {
+    b2 += cc[2 * ((size_t)ch.r * cpr + c)];
+    b1 += cc[2 * ((size_t)ch.r * cpr + c) + 1];
+  }
+  b2 = wave_sum(b2);
+  b1 = wave_sum(b1);
+  if ((threadIdx.x & (WAVE - 1)) == 0) { before_sh[0][threadIdx.x / WAVE] = b2; before_sh[1][threadIdx.x / WAVE] = b1; }
+  __syncthreads();
+  uint32_t B2 = 0, B1 = 0;
+#pragma unroll
+  for (int i = 0; i < SW; ++i) { B2 += before_sh[0][i]; B1 += before_sh[1][i]; }
+  const uint32_t quota = (S.prefix == NONE) ? 0u : (uint32_t)S.krem;
+  const uint32_t qrem = quota > B1 ? quota - B1 : 0u;
+  const uint32_t pos0 = B2 + (quota < B1 ? quota : B1);
+  const int64_t base = rowbase ? rowbase[ch.r] : 0;
+  const uint32_t lim = cap ? (uint32_t)cap[ch.r] : 0xFFFFFFFFu;
+
+  int kc[NK];
+  uint32_t n2 = 0, n1 = 0;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    kc[j] = klass(K.k[j], j < K.n, member != nullptr && m[j] != 0, S.prefix);
+    n2 += kc[j] == 2 ? 1u : 0u;
+    n1 += kc[j] == 1 ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan(n2 | (n1 << 16), sh, tot);
+  (void)tot;
+  const uint32_t e2 = ex & 0xFFFFu, e1 = ex >> 16;
+  uint32_t tie = e1;                                   // ties of the chunk before this thread's scores
+  uint32_t pos = pos0 + e2 + (e1 < qrem ? e1 : qrem);
+  uint8_t take[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    bool tk = kc[j] == 2;
+    if (kc[j] == 1) { tk = tie < qrem; ++tie; }
+    take[j] = tk ? 1 : 0;
+    if (tk && sel != nullptr && pos < lim && base + pos < sel_total) sel[base + pos] = K.e0 + j;
+    pos += tk ? 1u : 0u;
+  }
+  if (member_out != nullptr) {
+    uint8_t* mo = member_out + (size_t)ch.r * p;
+    if (vec && ch.e_end - ch.e_begin == ntile * TILE) {
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        if (t < ntile) {
+          const uint32_t w = (uint32_t)take[4 * t] | ((uint32_t)take[4 * t + 1] << 8) |
+                             ((uint32_t)take[4 * t + 2] << 16) | ((uint32_t)take[4 * t + 3] << 24);
+          *reinterpret_cast<uint32_t*>(mo + K.e0 + 4 * t) = w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NK; ++j)
+        if (j < K.n) mo[K.e0 + j] = take[j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- workspace plan
 struct AllocPlan {
-  size_t off_thr, off_quota, off_ent, off_k, total;
+  int R, cpr, ntile, nchunk;
+  size_t off_rowhist, off_seghist, off_cnt, zero_end;
+  size_t off_seg, off_row, off_row2, off_rowk2, off_rowbase, off_cc, off_member, off_part, off_klist, total;
 };
 
-AllocPlan plan_alloc(const Geo& g) {
+AllocPlan plan_alloc(const Geo& g, const adakv_alloc& a) {
   AllocPlan P{};
-  const size_t S = (size_t)g.I * g.hkv;
+  P.R = g.I * g.hkv;
+  P.ntile = MAXT;
+  auto chunks = [&](int nt) { return (int64_t)P.R * ((g.p + nt * TILE - 1) / (nt * TILE)); };
+  while (P.ntile > 1 && chunks(P.ntile) < 2048) P.ntile /= 2;
+  P.cpr = (g.p + P.ntile * TILE - 1) / (P.ntile * TILE);
+  P.nchunk = P.R * P.cpr;
   size_t off = 0;
-  P.off_thr = off;    off = align_up(off + S * 4, 256);
-  P.off_quota = off;  off = align_up(off + S * 4, 256);
-  P.off_ent = off;    off = align_up(off + (size_t)g.I * 8, 256);
-  P.off_k = off;      off = align_up(off + (size_t)g.I * 8, 256);
+  P.off_rowhist = off;  off = align_up(off + (size_t)P.R * NBIN * 4, 256);
+  P.off_seghist = off;  off = align_up(off + (size_t)g.I * NBIN * 4, 256);
+  P.off_cnt = off;      off = align_up(off + (size_t)P.R * 8, 256);
+  P.zero_end = off;
+  P.off_seg = off;      off = align_up(off + (size_t)g.I * sizeof(RState), 256);
+  P.off_row = off;      off = align_up(off + (size_t)P.R * sizeof(RState), 256);
+  P.off_row2 = off;     off = align_up(off + (size_t)P.R * sizeof(RState), 256);
+  P.off_rowk2 = off;    off = align_up(off + (size_t)P.R * 4, 256);
+  P.off_rowbase = off;  off = align_up(off + (size_t)P.R * 8, 256);
+  P.off_cc = off;       off = align_up(off + (size_t)P.nchunk * 8, 256);
+  P.off_member = off;
+  if (a.mode == ADAKV_ALLOC_ADA_CRITICALKV) off = align_up(off + (size_t)P.R * g.p, 256);
+  P.off_part = off;
+  if (a.mode == ADAKV_ALLOC_LAVA_LAYERS) off = align_up(off + (size_t)P.nchunk * 16, 256);
+  P.off_klist = off;    off = align_up(off + (size_t)g.I * 8, 256);
   P.total = off;
   return P;
 }
 
 }  // namespace
 
-size_t alloc_ws_bytes(const Geo& g, const adakv_alloc&) { return plan_alloc(g).total; }
+size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a) { return plan_alloc(g, a).total; }
 
+// Launch order (every kernel on `st`, nothing waits on the host):
+//   zero histograms and counts
+//   layer-wide top-k: pass-0 row histograms [LAVa: + entropy partials, layer budgets],
+//     pick 0, then (histogram, pick) for passes 1 and 2
+//   layer counts per row -> per-row budgets, offsets and first pick of the head's top-k
+//   [Ada-KV / CriticalKV] (histogram, pick) for passes 1 and 2 of every head's top-k
+//   per-chunk counts -> emission in index order
+//   [CriticalKV] stage 1 emits member flags; stage 2 runs the head top-k again on the
+//     composite score over non-members and emits the union.
 hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* score, const float* score2,
                            int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st) {
-  const AllocPlan P = plan_alloc(g);
-  uint32_t* hthr = reinterpret_cast<uint32_t*>(ws + P.off_thr);
-  int32_t* hquota = reinterpret_cast<int32_t*>(ws + P.off_quota);
-  double* ent = reinterpret_cast<double*>(ws + P.off_ent);
-  int64_t* klist = reinterpret_cast<int64_t*>(ws + P.off_k);
-  const int S = g.I * g.hkv;
-  if (a.mode == ADAKV_ALLOC_LAVA_LAYERS) {
+  const AllocPlan P = plan_alloc(g, a);
+  uint32_t* rowhist = reinterpret_cast<uint32_t*>(ws + P.off_rowhist);
+  uint32_t* seghist = reinterpret_cast<uint32_t*>(ws + P.off_seghist);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + P.off_cnt);
+  RState* segst = reinterpret_cast<RState*>(ws + P.off_seg);
+  RState* rowst = reinterpret_cast<RState*>(ws + P.off_row);
+  RState* rowst2 = reinterpret_cast<RState*>(ws + P.off_row2);
+  int32_t* rowk2 = reinterpret_cast<int32_t*>(ws + P.off_rowk2);
+  int64_t* rowbase = reinterpret_cast<int64_t*>(ws + P.off_rowbase);
+  uint32_t* cc = reinterpret_cast<uint32_t*>(ws + P.off_cc);
+  uint8_t* member = reinterpret_cast<uint8_t*>(ws + P.off_member);
+  double* part = reinterpret_cast<double*>(ws + P.off_part);
+  int64_t* klist = reinterpret_cast<int64_t*>(ws + P.off_klist);
+
+  const bool vec1 = (g.p % 4 == 0) && (reinterpret_cast<uintptr_t>(score) % 16 == 0);
+  const bool vec2 = (g.p % 4 == 0) && (reinterpret_cast<uintptr_t>(score2) % 16 == 0);
+  const int nc = P.nchunk, cpr = P.cpr, nt = P.ntile, hkv = g.hkv, R = P.R;
+  const bool lava = a.mode == ADAKV_ALLOC_LAVA_LAYERS;
+  const bool ck = a.mode == ADAKV_ALLOC_ADA_CRITICALKV;
+  const int mode = lava ? MODE_LAVA : (ck ? MODE_CK : MODE_ADA);
+  const int kP = lava ? 0 : (int)(a.budget - (int64_t)g.w * g.hkv);
+  const int64_t sel_total = lava ? a.budget - (int64_t)g.I * g.w * g.hkv : (int64_t)g.I * kP;
+
+  {
+    const size_t n16 = P.zero_end / 16;
+    const int blocks = (int)std::min<size_t>((n16 + SB - 1) / SB, 4096);
+    sel_zero_kernel<<<blocks, SB, 0, st>>>(reinterpret_cast<u32x4*>(ws), n16);
+  }
+  // Layer-wide top-k.
+  layer_hist0_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, lava ? 1 : 0, rowhist, part);
+  if (lava) {
     const int64_t Bp = a.budget - (int64_t)g.I * g.w * g.hkv;
-    lava_entropy_kernel<<<g.I, ST, 0, st>>>(score, g.hkv, g.p, ent);
     const size_t sm = (size_t)g.I * (sizeof(double) + sizeof(int64_t));
-    lava_budget_kernel<<<1, ST, sm, st>>>(ent, g.I, Bp, klist, sel_off);
-    select_layer_kernel<<<g.I, ST, 0, st>>>(score, g.hkv, g.p, 0, klist, 0, 1, 1, budgets, hthr, hquota, sel_off,
-                                            g.I);
-    select_head_kernel<<<S, ST, 0, st>>>(score, nullptr, g.hkv, g.p, HEAD_LAVA, 0, 1, budgets, hthr, hquota,
-                                         sel_off, sel);
+    lava_budget_kernel<<<1, SB, sm, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp, klist, sel_off);
+  }
+  layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, lava ? klist : nullptr, segst);
+  for (int ps = 1; ps < 3; ++ps) {
+    radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, segst, seghist);
+    radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, segst);
+  }
+  // Head budgets.
+  layer_count_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, hkv, segst, cnt);
+  row_budget_kernel<<<R, SB, 0, st>>>(hkv, mode, kP, a.alpha_num, a.alpha_den, a.ck_num, a.ck_den, g.I, segst, cnt,
+                                      rowhist, budgets, rowbase, rowk2, rowst, sel_off);
+  // Every head's own top-k (LAVa keeps the layer threshold).
+  if (!lava) {
+    for (int ps = 1; ps < 3; ++ps) {
+      radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, rowst, rowhist);
+      radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, rowst);
+    }
+  }
+  chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
+  if (!ck) {
+    emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets, sel, sel_total,
+                                   nullptr);
     return hipGetLastError();
   }
-  const int P0 = (int)(a.budget - (int64_t)g.w * g.hkv);
-  select_layer_kernel<<<g.I, ST, 0, st>>>(score, g.hkv, g.p, P0, nullptr, a.alpha_num, a.alpha_den, 0, budgets,
-                                          hthr, hquota, sel_off, g.I);
-  const int mode = (a.mode == ADAKV_ALLOC_ADA_CRITICALKV) ? HEAD_CK : HEAD_ADA;
-  const size_t lds = (mode == HEAD_CK) ? (size_t)((g.p + 31) / 32) * 4 : 0;
-  select_head_kernel<<<S, ST, lds, st>>>(score, score2, g.hkv, g.p, mode, a.ck_num, a.ck_den, budgets, hthr, hquota,
-                                         sel_off, sel);
+  // CriticalKV: stage-1 members, then stage 2 on the composite score over the rest.
+  emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
+                                 member);
+  for (int ps = 0; ps < 3; ++ps) {
+    radix_hist_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, 1, ps, rowk2, rowst2, rowhist);
+    radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, rowk2, rowst2);
+  }
+  chunk_count_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc);
+  emit_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc, rowbase, budgets, sel, sel_total,
+                                 nullptr);
   return hipGetLastError();
 }
 
