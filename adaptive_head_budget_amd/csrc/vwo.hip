@@ -10,7 +10,11 @@
 // and folds every product element into |.| row sums as soon as it leaves the
 // accumulator: the [keys x hidden] product is never written.  W^O is read in
 // the nn.Linear layout [hidden, hq*d], so a 64-column tile of W^O_i is 64
-// contiguous 256-byte rows, staged through LDS and shared by the 4 waves.
+// contiguous 256-byte rows.  Each tile is loaded into registers two tiles
+// ahead of its multiply and written to one of two LDS slots, 16-byte chunk ch
+// of row r at position ch ^ (r & 15), so the 16 rows of one B-operand read fall
+// in 16 different bank groups.  One barrier per tile, and loads stay in flight
+// across it.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,20 +24,56 @@ namespace {
 constexpr int D = 128;
 constexpr int KEYS = 256;          // keys per workgroup (64 per wave)
 constexpr int NT = 64;             // hidden columns per tile
-constexpr int WSTRIDE = D * 2 + 16;
+constexpr int ROWB = D * 2;        // bytes per W^O tile row
+constexpr int SLOT = NT * ROWB;    // 16 KB per tile
+constexpr int CPT = SLOT / 16 / 256;   // 16-byte chunks per thread per tile
 constexpr int KSTEPS = D / 32;
+constexpr int MAXG = 8;
 
-__global__ __launch_bounds__(256) void vwo_norm_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ w_o,
-                                                       const float* __restrict__ head_scores, float* __restrict__ comp,
-                                                       int inst0, int hq, int hkv, int G, int n, int p, int hidden,
-                                                       float eps) {
-  __shared__ __align__(16) char wt[2][NT * WSTRIDE];
+// Workgroup barrier for LDS only: global loads issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __restrict__ v,
+                                                          const uint16_t* __restrict__ w_o,
+                                                          const float* __restrict__ head_scores,
+                                                          float* __restrict__ comp, int inst0, int hq, int hkv, int G,
+                                                          int n, int p, int hidden, float eps) {
+  __shared__ __align__(16) char wt[2][SLOT];
+  __shared__ float ahs[MAXG][KEYS];     // (A_i + eps) of the workgroup's keys
   const int g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int gq = lane >> 4, c = lane & 15;
-  const int key0 = blockIdx.x * KEYS + 64 * wv;
+  const int kwg = blockIdx.x * KEYS;
+  const int key0 = kwg + 64 * wv;
   const uint16_t* vb = v + ((size_t)inst * hkv + g) * (size_t)n * D;
+  const size_t wrow = (size_t)hq * D;
+  const int ntiles = hidden / NT;
+  const int total = G * ntiles;        // (head, tile) pairs in order
 
+  // this thread's chunks of a tile: row r = idx / 16, chunk idx % 16
+  auto load_tile = [&](u32x4 (&reg)[CPT], int T) {
+    const uint16_t* wb = w_o + (size_t)(g * G + T / ntiles) * D + (size_t)((T % ntiles) * NT) * wrow;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      reg[i] = ld16(wb + (size_t)(idx >> 4) * wrow + (idx & 15) * 8);
+    }
+  };
+  auto store_tile = [&](const u32x4 (&reg)[CPT], char* slot) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = threadIdx.x + 256 * i, r = idx >> 4, ch = idx & 15;
+      st16(slot + r * ROWB + ((ch ^ (r & 15)) * 16), reg[i]);
+    }
+  };
+
+  u32x4 ra[CPT], rb[CPT];
+  load_tile(ra, 0);
+  if (total > 1) load_tile(rb, 1);
+  for (int idx = threadIdx.x; idx < G * KEYS; idx += 256) {
+    const int h = idx / KEYS, t = kwg + idx % KEYS;
+    ahs[h][idx % KEYS] = (t < p) ? head_scores[((size_t)il * hq + g * G + h) * p + t] + eps : 0.f;
+  }
   // A operands: 4 M-blocks of 16 keys, held for the whole workgroup.
   bf16x8 aop[4][KSTEPS];
 #pragma unroll
@@ -43,87 +83,61 @@ __global__ __launch_bounds__(256) void vwo_norm_kernel(const uint16_t* __restric
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) aop[mb][ks] = Mma<uint16_t>::load(vb + (size_t)t * D + ks * 32 + 8 * gq);
   }
-  float cacc[4][4];
+  store_tile(ra, wt[0]);
+  if (total > 2) load_tile(ra, 2);
+  __syncthreads();     // ahs and tile 0 in LDS
+
+  float cacc[4][4], rsum[4][4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cacc[mb][j] = 0.f;
+    for (int j = 0; j < 4; ++j) { cacc[mb][j] = 0.f; rsum[mb][j] = 0.f; }
 
-  const int ntiles = hidden / NT;
-  for (int h = 0; h < G; ++h) {
-    const int i = g * G + h;
-    const uint16_t* wb = w_o + (size_t)i * D;   // column block of head i, row stride hq*D
-    const size_t wrow = (size_t)hq * D;
-    float rsum[4][4];
+  // Tile T is in slot T % 2; the registers of tile T+1 are `nxt` (written to the
+  // other slot after the multiply), and `nxt` then takes tile T+3.
+  auto step = [&](int T, u32x4 (&nxt)[CPT]) {
+    const char* slot = wt[T & 1];
+    // one 16-column block at a time: its |.| sums overlap the next block's MFMAs
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int nb = 0; nb < 4; ++nb) {
+      const int r = 16 * nb + c;
+      f32x4 acc[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rsum[mb][j] = 0.f;
-    // stage tile 0
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < NT * 16; idx += 256) {
-      const int r = idx >> 4, ch = idx & 15;
-      st16(wt[0] + r * WSTRIDE + ch * 16, ld16(wb + (size_t)r * wrow + ch * 8));
-    }
-    __syncthreads();
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int cur = tile & 1;
-      // prefetch the next tile into registers while this one is multiplied
-      u32x4 pre[4];
-      const bool more = tile + 1 < ntiles;
-      if (more) {
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int idx = threadIdx.x + 256 * q2;
-          const int r = idx >> 4, ch = idx & 15;
-          pre[q2] = ld16(wb + (size_t)((tile + 1) * NT + r) * wrow + ch * 8);
-        }
-      }
-      f32x4 acc[4][4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = zero4();
+      for (int mb = 0; mb < 4; ++mb) acc[mb] = zero4();
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 bop = *reinterpret_cast<const bf16x8*>(slot + r * ROWB + (((ks * 4 + gq) ^ c) * 16));
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const bf16x8 bop = Mma<uint16_t>::load(
-              reinterpret_cast<const uint16_t*>(wt[cur] + (16 * nb + c) * WSTRIDE) + ks * 32 + 8 * gq);
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = Mma<uint16_t>::mma(aop[mb][ks], bop, acc[mb][nb]);
-        }
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = Mma<uint16_t>::mma(aop[mb][ks], bop, acc[mb]);
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) rsum[mb][j] += fabsf(acc[mb][nb][j]);
-      if (more) {
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int idx = threadIdx.x + 256 * q2;
-          const int r = idx >> 4, ch = idx & 15;
-          st16(wt[cur ^ 1] + r * WSTRIDE + ch * 16, pre[q2]);
-        }
-      }
-      __syncthreads();
+        for (int j = 0; j < 4; ++j) rsum[mb][j] += fabsf(acc[mb][j]);
     }
-    // rsum[mb][j]: partial over this lane's columns of key key0 + 16mb + 4gq + j
+    if ((T + 1) % ntiles == 0) {
+      // head done: rsum[mb][j] is this lane's part of key key0 + 16mb + 4gq + j
+      const int h = T / ntiles;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = rsum[mb][j];
-        x += shfl_xor(x, 8);
-        x += shfl_xor(x, 4);
-        x += shfl_xor(x, 2);
-        x += shfl_xor(x, 1);
-        const int t = key0 + 16 * mb + 4 * gq + j;
-        const float a = (t < p) ? head_scores[((size_t)il * hq + i) * p + t] : 0.f;
-        cacc[mb][j] += (a + eps) * x;
-      }
+        for (int j = 0; j < 4; ++j) {
+          float x = rsum[mb][j];
+          x += shfl_xor(x, 8);
+          x += shfl_xor(x, 4);
+          x += shfl_xor(x, 2);
+          x += shfl_xor(x, 1);
+          cacc[mb][j] += ahs[h][64 * wv + 16 * mb + 4 * gq + j] * x;
+          rsum[mb][j] = 0.f;
+        }
+    }
+    if (T + 1 < total) store_tile(nxt, wt[(T + 1) & 1]);
+    lds_barrier();     // tile T+1 in LDS; slot T & 1 free
+    if (T + 3 < total) load_tile(nxt, T + 3);
+  };
+  for (int T = 0; T < total; T += 2) {
+    step(T, rb);
+    if (T + 1 < total) step(T + 1, ra);
   }
   const float invG = 1.0f / (float)G;
   if (c == 0) {
@@ -141,7 +155,7 @@ __global__ __launch_bounds__(256) void vwo_norm_kernel(const uint16_t* __restric
 
 hipError_t launch_vwo(const Geo& g, int inst0, int ni, const void* v, const void* w_o, const float* head_scores,
                       float* score2, hipStream_t st) {
-  if (g.dtype != ADAKV_BF16 || g.d != D || g.hidden % NT != 0) return hipErrorInvalidValue;
+  if (g.dtype != ADAKV_BF16 || g.d != D || g.hidden % NT != 0 || g.G > MAXG) return hipErrorInvalidValue;
   dim3 grid((g.p + KEYS - 1) / KEYS, g.hkv, ni);
   vwo_norm_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(w_o),
                                         head_scores, score2, inst0, g.hq, g.hkv, g.G, g.n, g.p, g.hidden, g.eps);
