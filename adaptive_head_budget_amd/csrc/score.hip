@@ -354,22 +354,21 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
     if (t + 1 < tiles_per_wg && k0 + TILE < p) tr.load(kb, n, k0 + TILE);   // next tile in flight
 
     if (active) {
-      f32x4 acc[9][NB];
-#pragma unroll
-      for (int mb = 0; mb < 9; ++mb) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
-        const T* arow = reinterpret_cast<const T*>(mb < 8 ? a_base + mb * 16 * L::STRIDE : a_halo);
-#pragma unroll
-        for (int ks = 0; ks < L::KSTEPS; ++ks) {
-          const typename M::op_t a = M::load(arow + ks * M::KSTEP);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
-        }
-      }
       const int kbase = k0 + 32 * gq;   // first key of this lane group
-
       if (KIND == EMIT_SNAP) {
+        f32x4 acc[9][NB];
+#pragma unroll
+        for (int mb = 0; mb < 9; ++mb) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
+          const T* arow = reinterpret_cast<const T*>(mb < 8 ? a_base + mb * 16 * L::STRIDE : a_halo);
+#pragma unroll
+          for (int ks = 0; ks < L::KSTEPS; ++ks) {
+            const typename M::op_t a = M::load(arow + ks * M::KSTEP);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
+          }
+        }
         const bool interior = k0 >= 3 && k0 + TILE + 3 <= p;   // all pooled keys inside the prefix
         float ks[32];
 #pragma unroll
@@ -421,7 +420,9 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
         hs[h * TILE + 32 * gq + 2 * c] = s0;
         hs[h * TILE + 32 * gq + 2 * c + 1] = s1;
       } else {
-        // LAVa: causal weights summed over the head's rows, before pooling.
+        // LAVa: causal weights summed over the head's rows, before pooling.  Rows
+        // are summed before pooling, so each M-block is folded in as soon as its
+        // MFMAs finish (one block of accumulators live at a time).
         const bool interior = k0 >= HALO && k0 + TILE + HALO <= p;   // every key <= p <= p + r, >= 0
         float ks[32], hsum[4];
 #pragma unroll
@@ -430,30 +431,33 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
         for (int j = 0; j < 4; ++j) hsum[j] = 0.f;
         const int hkey0 = (gq == 0) ? k0 - HALO : ((gq == 3) ? k0 + TILE : -1);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int r = 16 * nb + c;
-          const int lim = min(n - 1, p + r);
-          const float mc = smc[nb], il_row = sil[nb];
-          if (interior) {
+        for (int mb = 0; mb < 9; ++mb) {
+          f32x4 acc[NB];
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
+          for (int nb = 0; nb < NB; ++nb) acc[nb] = zero4();
+          const T* arow = reinterpret_cast<const T*>(mb < 8 ? a_base + mb * 16 * L::STRIDE : a_halo);
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-                ks[4 * mb + j] = fmaf(fast_exp2(fmaf(acc[mb][nb][j], c2, -mc)), il_row, ks[4 * mb + j]);
-          } else {
+          for (int ks2 = 0; ks2 < L::KSTEPS; ++ks2) {
+            const typename M::op_t a = M::load(arow + ks2 * M::KSTEP);
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float e = fast_exp2(fmaf(acc[mb][nb][j], c2, -mc));
-                ks[4 * mb + j] += (kbase + 4 * mb + j <= lim) ? e * il_row : 0.f;
-              }
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = M::mma(a, qop[nb][ks2], acc[nb]);
           }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = hkey0 + j;
-            const float e = fast_exp2(fmaf(acc[8][nb][j], c2, -mc));
-            hsum[j] += (hkey0 >= 0 && key >= 0 && key <= lim) ? e * il_row : 0.f;
+          for (int nb = 0; nb < NB; ++nb) {
+            const int r = 16 * nb + c;
+            const int lim = min(n - 1, p + r);
+            const float mc = smc[nb], il_row = sil[nb];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float e = fast_exp2(fmaf(acc[nb][j], c2, -mc));
+              if (mb < 8) {
+                if (interior) ks[4 * mb + j] = fmaf(e, il_row, ks[4 * mb + j]);
+                else ks[4 * mb + j] += (kbase + 4 * mb + j <= lim) ? e * il_row : 0.f;
+              } else {
+                const int key = hkey0 + j;
+                hsum[j] += (hkey0 >= 0 && key >= 0 && key <= lim) ? e * il_row : 0.f;
+              }
+            }
           }
         }
         float s0, s1;
