@@ -64,6 +64,16 @@ __device__ __forceinline__ float shfl_xor(float x, int mask) {
   return shfl_lane(x, (int)(__lane_id() ^ mask));
 }
 
+// Lane moves inside rows of 16 lanes on the vector unit (DPP), no LDS traffic:
+// DPP_MIRROR: lane i <- lane 15 - i; DPP_HALF_MIRROR: i <- 7 - i within each 8;
+// DPP_XOR2 / DPP_XOR1: i <- i ^ 2 / i ^ 1 within each 4.  All four are
+// involutions, so they pair lanes like a butterfly.
+enum { DPP_MIRROR = 0x140, DPP_HALF_MIRROR = 0x141, DPP_XOR2 = 0x4E, DPP_XOR1 = 0xB1 };
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // exp2 on the hardware transcendental unit (results below 2^-126 flush to zero).

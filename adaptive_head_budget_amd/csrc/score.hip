@@ -7,7 +7,8 @@
 // M side (A operand, staged through LDS), window rows the N side (B operand,
 // held in registers).  The A rows are permuted so that every lane ends up with
 // 32 consecutive keys of one window row, which makes the max pooling a
-// register-local sliding maximum.
+// register-local sliding maximum.  The row sums over a lane group use DPP lane
+// moves on the vector unit rather than LDS permutes.
 //
 // Definitions followed:
 //  * Ada-KV notes, Algorithm 2 ("Ada-KV Integration") steps 2-4: softmax of the
@@ -35,7 +36,8 @@ constexpr int TROWS = TILE + 2 * HALO;
 template <typename T, int D>
 struct Lay {
   static constexpr int ROWB = D * (int)sizeof(T);
-  static constexpr int STRIDE = ROWB + 16;           // odd count of 16-B units per LDS row
+  static constexpr int STRIDE = ROWB;                // LDS row pitch (chunks swizzled, no padding)
+  static constexpr int RP = ROWB >= 256 ? 1 : 256 / ROWB;   // rows per 256 bytes
   static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
   static constexpr int EPC = 16 / (int)sizeof(T);    // elements per chunk
   static constexpr int KSTEPS = D / Mma<T>::KSTEP;
@@ -60,6 +62,24 @@ __device__ __forceinline__ int a_row(int mb, int m) {
   return ((m >> 2) == 3) ? TILE + HALO + (m & 3) : TILE + (m & 3);
 }
 
+// 16-byte chunk ch of LDS row R is stored at position ch ^ swz(R): the 16 rows
+// of one MFMA operand read (same logical chunk) fall in 16 distinct bank groups.
+template <typename T, int D>
+__device__ __forceinline__ int swz(int R) {
+  using L = Lay<T, D>;
+  return (R / L::RP) & (L::CPR - 1);
+}
+
+// Address of the A operand of M-block mb, k-step ks for lane (m = c, group gq).
+template <typename T, int D>
+__device__ __forceinline__ const T* a_ptr(const char* lds, int mb, int ks, int c, int gq) {
+  using L = Lay<T, D>;
+  using M = Mma<T>;
+  const int R = a_row(mb, c);
+  const int eb = (ks * M::KSTEP + M::KPL * gq) * (int)sizeof(T);   // byte offset in the row
+  return reinterpret_cast<const T*>(lds + R * L::STRIDE + (((eb >> 4) ^ swz<T, D>(R)) << 4) + (eb & 15));
+}
+
 // K tile staging in two halves so the global loads of tile t+1 are in
 // flight while tile t is multiplied: load() fills registers, store() moves
 // them to LDS.  Keys [k0 + KLO, k0 + KHI) of one head; keys outside [0, n)
@@ -81,7 +101,8 @@ struct TileRegs {
       const int koff = KLO + idx / L::CPR, ch = idx % L::CPR;
       kof[i] = koff;
       src[i] = koff * D + ch * L::EPC;
-      dst[i] = (idx < CHUNKS) ? tile_row(koff) * L::STRIDE + ch * 16 : -1;
+      const int R = (idx < CHUNKS) ? tile_row(koff) : 0;
+      dst[i] = (idx < CHUNKS) ? R * L::STRIDE + ((ch ^ swz<T, D>(R)) * 16) : -1;
     }
   }
   __device__ __forceinline__ void load(const T* kb, int n, int k0) {
@@ -116,53 +137,33 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2,
 
 // Sum 32 per-lane values across the 16 lanes of a lane group (lanes sharing
 // lane/16); afterwards lane c of the group holds the totals of entries 2c, 2c+1.
+// A butterfly of four DPP involutions (mirror, half mirror, quad ^2, quad ^1):
+// at each step a lane keeps the half of its entries selected by one bit of c
+// and adds its partner's copy of that half.
+template <int CTRL, int HALF>
+__device__ __forceinline__ void rs_step(const float* in, float* out, bool upper) {
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float send = upper ? in[i] : in[i + HALF];
+    const float keep = upper ? in[i + HALF] : in[i];
+    out[i] = keep + dpp<CTRL>(send);
+  }
+}
 __device__ __forceinline__ void reduce_scatter16(float (&x)[32], int c, float& o0, float& o1) {
   float y[16], z[8], u[4], t[2];
-  {
-    const bool b = (c >> 3) & 1;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float send = b ? x[i] : x[i + 16];
-      const float keep = b ? x[i + 16] : x[i];
-      y[i] = keep + shfl_xor(send, 8);
-    }
-  }
-  {
-    const bool b = (c >> 2) & 1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float send = b ? y[i] : y[i + 8];
-      const float keep = b ? y[i + 8] : y[i];
-      z[i] = keep + shfl_xor(send, 4);
-    }
-  }
-  {
-    const bool b = (c >> 1) & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = b ? z[i] : z[i + 4];
-      const float keep = b ? z[i + 4] : z[i];
-      u[i] = keep + shfl_xor(send, 2);
-    }
-  }
-  {
-    const bool b = c & 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float send = b ? u[i] : u[i + 2];
-      const float keep = b ? u[i + 2] : u[i];
-      t[i] = keep + shfl_xor(send, 1);
-    }
-  }
+  rs_step<DPP_MIRROR, 16>(x, y, (c >> 3) & 1);
+  rs_step<DPP_HALF_MIRROR, 8>(y, z, (c >> 2) & 1);
+  rs_step<DPP_XOR2, 4>(z, u, (c >> 1) & 1);
+  rs_step<DPP_XOR1, 2>(u, t, c & 1);
   o0 = t[0];
   o1 = t[1];
 }
 
 __device__ __forceinline__ float allsum16(float x) {
-  x += shfl_xor(x, 8);
-  x += shfl_xor(x, 4);
-  x += shfl_xor(x, 2);
-  x += shfl_xor(x, 1);
+  x += dpp<DPP_MIRROR>(x);
+  x += dpp<DPP_HALF_MIRROR>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_XOR1>(x);
   return x;
 }
 
@@ -182,8 +183,6 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
   const bool active = h < G;
   const T* kb = k + ((size_t)inst * hkv + g) * (size_t)n * D;
   const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (active ? h : 0)) * (size_t)w * D;
-  // lane's A-operand row in LDS for M-block 0 (block mb adds 16 rows)
-  const char* a_base = lds + a_row(0, c) * L::STRIDE + M::KPL * gq * (int)sizeof(T);
 
   typename M::op_t qop[NB][L::KSTEPS];
 #pragma unroll
@@ -213,10 +212,9 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
     for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
-      const T* arow = reinterpret_cast<const T*>(a_base + mb * 16 * L::STRIDE);
 #pragma unroll
       for (int ks = 0; ks < L::KSTEPS; ++ks) {
-        const typename M::op_t a = M::load(arow + ks * M::KSTEP);
+        const typename M::op_t a = M::load(a_ptr<T, D>(lds, mb, ks, c, gq));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
       }
@@ -317,8 +315,6 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
   const int Gw = G * w;
   const T* kb = k + ((size_t)inst * hkv + g) * (size_t)n * D;
   const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (active ? h : 0)) * (size_t)w * D;
-  const char* a_base = lds + a_row(0, c) * L::STRIDE + M::KPL * gq * (int)sizeof(T);
-  const char* a_halo = lds + a_row(8, c) * L::STRIDE + M::KPL * gq * (int)sizeof(T);
 
   typename M::op_t qop[NB][L::KSTEPS];
   float smc[NB], sil[NB];   // row max * c2 and 1 / row sum
@@ -361,10 +357,9 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
         for (int mb = 0; mb < 9; ++mb) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
-          const T* arow = reinterpret_cast<const T*>(mb < 8 ? a_base + mb * 16 * L::STRIDE : a_halo);
 #pragma unroll
           for (int ks = 0; ks < L::KSTEPS; ++ks) {
-            const typename M::op_t a = M::load(arow + ks * M::KSTEP);
+            const typename M::op_t a = M::load(a_ptr<T, D>(lds, mb, ks, c, gq));
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
           }
@@ -435,10 +430,9 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
           f32x4 acc[NB];
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) acc[nb] = zero4();
-          const T* arow = reinterpret_cast<const T*>(mb < 8 ? a_base + mb * 16 * L::STRIDE : a_halo);
 #pragma unroll
           for (int ks2 = 0; ks2 < L::KSTEPS; ++ks2) {
-            const typename M::op_t a = M::load(arow + ks2 * M::KSTEP);
+            const typename M::op_t a = M::load(a_ptr<T, D>(lds, mb, ks2, c, gq));
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = M::mma(a, qop[nb][ks2], acc[nb]);
           }
