@@ -167,6 +167,37 @@ __device__ __forceinline__ float allsum16(float x) {
   return x;
 }
 
+// Logits of M-block mb for the NB window-row blocks: Q_win K^T with the head
+// dimension split into two halves accumulated separately and added at the end.
+// The matrix units round their running sum every few products; with one
+// accumulator, the error of a logit of magnitude ~600 (a head with temperature
+// 0.1) reaches ~1e-4, which moves a softmax weight by ~1e-5 relative.  Two
+// half-length sums halve the magnitude the rounding works at.
+template <typename T, int D, int NB>
+__device__ __forceinline__ void logits_block(const char* lds, int mb, int c, int gq,
+                                             const typename Mma<T>::op_t (&qop)[NB][Lay<T, D>::KSTEPS],
+                                             f32x4 (&out)[NB]) {
+  using L = Lay<T, D>;
+  using M = Mma<T>;
+  constexpr int HALF = L::KSTEPS / 2;
+  f32x4 lo[NB], hi[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) { lo[nb] = zero4(); hi[nb] = zero4(); }
+#pragma unroll
+  for (int ks = 0; ks < L::KSTEPS; ++ks) {
+    const typename M::op_t a = M::load(a_ptr<T, D>(lds, mb, ks, c, gq));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (ks < HALF) lo[nb] = M::mma(a, qop[nb][ks], lo[nb]);
+      else hi[nb] = M::mma(a, qop[nb][ks], hi[nb]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[nb][j] = lo[nb][j] + hi[nb][j];
+}
+
 // ---------------------------------------------------------------- pass 1
 // Workgroup = max(G, 4) waves; wave h < G owns query head g*G + h (its w window
 // rows on the N side, NB blocks of 16); the others only help load K.
@@ -209,16 +240,7 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
     if (!active) continue;
     f32x4 acc[8][NB];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < L::KSTEPS; ++ks) {
-        const typename M::op_t a = M::load(a_ptr<T, D>(lds, mb, ks, c, gq));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
-      }
-    }
+    for (int mb = 0; mb < 8; ++mb) logits_block<T, D, NB>(lds, mb, c, gq, qop, acc[mb]);
     // every key of the tile inside every row's domain: no per-key test
     const bool full = k0 + TILE - 1 <= (CAUSAL ? min(kend - 1, p) : kend - 1);
 #pragma unroll
@@ -238,19 +260,18 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
             if (k0 + 32 * gq + 4 * mb + j <= lim) lm = fmaxf(lm, acc[mb][nb][j]);
       }
       if (lm != -INFINITY) {
-        const float lmc = lm * c2;
         float ls = 0.f;
         if (full) {
 #pragma unroll
           for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ls += fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
+            for (int j = 0; j < 4; ++j) ls += fast_exp2((acc[mb][nb][j] - lm) * c2);
         } else {
 #pragma unroll
           for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float e = fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
+              const float e = fast_exp2((acc[mb][nb][j] - lm) * c2);
               ls += (k0 + 32 * gq + 4 * mb + j <= lim) ? e : 0.f;
             }
         }
@@ -317,7 +338,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
   const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (active ? h : 0)) * (size_t)w * D;
 
   typename M::op_t qop[NB][L::KSTEPS];
-  float smc[NB], sil[NB];   // row max * c2 and 1 / row sum
+  float smc[NB], sil[NB];   // row max and 1 / row sum
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int r = 16 * nb + c;
@@ -327,7 +348,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
       qop[nb][ks] = ok ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
     if (ok) {
       const float2 st = stats[((size_t)il * hkv + g) * Gw + h * w + r];
-      smc[nb] = st.x * c2;
+      smc[nb] = st.x;
       sil[nb] = st.y;
     } else {
       smc[nb] = 0.f;    // padding rows: q = 0, weight 0
@@ -354,16 +375,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
       if (KIND == EMIT_SNAP) {
         f32x4 acc[9][NB];
 #pragma unroll
-        for (int mb = 0; mb < 9; ++mb) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = zero4();
-#pragma unroll
-          for (int ks = 0; ks < L::KSTEPS; ++ks) {
-            const typename M::op_t a = M::load(a_ptr<T, D>(lds, mb, ks, c, gq));
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = M::mma(a, qop[nb][ks], acc[mb][nb]);
-          }
-        }
+        for (int mb = 0; mb < 9; ++mb) logits_block<T, D, NB>(lds, mb, c, gq, qop, acc[mb]);
         const bool interior = k0 >= 3 && k0 + TILE + 3 <= p;   // all pooled keys inside the prefix
         float ks[32];
 #pragma unroll
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 #pragma unroll
             for (int kk = 0; kk < 32; ++kk) {
               const float pooled = fmax3(a3[kk], a3[kk + 2], a3[kk + 4]);
-              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
+              ks[kk] = fmaf(fast_exp2((pooled - mc) * c2), il_row, ks[kk]);
             }
           } else {
 #pragma unroll
@@ -406,7 +418,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
               float pooled = x[kk + 3];
               if (RHO >= 1) pooled = fmax3(pooled, x[kk + 2], x[kk + 4]);
               if (RHO >= 2) pooled = fmax3(pooled, x[kk + 1], x[kk + 5]);
-              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
+              ks[kk] = fmaf(fast_exp2((pooled - mc) * c2), il_row, ks[kk]);
             }
           }
         }
@@ -428,14 +440,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 #pragma unroll
         for (int mb = 0; mb < 9; ++mb) {
           f32x4 acc[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[nb] = zero4();
-#pragma unroll
-          for (int ks2 = 0; ks2 < L::KSTEPS; ++ks2) {
-            const typename M::op_t a = M::load(a_ptr<T, D>(lds, mb, ks2, c, gq));
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[nb] = M::mma(a, qop[nb][ks2], acc[nb]);
-          }
+          logits_block<T, D, NB>(lds, mb, c, gq, qop, acc);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const int r = 16 * nb + c;
@@ -443,7 +448,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
             const float mc = smc[nb], il_row = sil[nb];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float e = fast_exp2(fmaf(acc[nb][j], c2, -mc));
+              const float e = fast_exp2((acc[nb][j] - mc) * c2);
               if (mb < 8) {
                 if (interior) ks[4 * mb + j] = fmaf(e, il_row, ks[4 * mb + j]);
                 else ks[4 * mb + j] += (kbase + 4 * mb + j <= lim) ? e * il_row : 0.f;

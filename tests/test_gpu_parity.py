@@ -261,3 +261,78 @@ def test_llama_model_full_sampled(gpu_lib):
         log(f"  inst {i}: flat cache exact after {steps} appends; decode max-abs {ma:.2e} rel-L2 {rl:.2e}")
     del data, ev
     torch.cuda.empty_cache()
+
+
+def test_lava_full_sampled(gpu_lib):
+    """The 32-layer Mistral-7B LAVa workload at n = 131072 exactly as the
+    benchmark launches it: the layer budgets and every layer's selection
+    bit-exact against the oracle's allocation run on the GPU's own fp32 scores;
+    two layers' scores and flat segments against the oracle."""
+    cfg = configs.MISTRAL7B_LAVA
+    log("drawing full Mistral-7B LAVa inputs on the device")
+    data = synth.make_batch_torch(cfg, "cuda")
+    ev = pipeline.Eviction(cfg)
+    ev.evict(data["q_win"], data["k"], data["v"])
+    torch.cuda.synchronize()
+    score = ev.score.cpu().numpy()
+    b, off, sel = ev.host_selection()
+    L, w = cfg.instances, cfg.w
+    assert int(off[L]) == cfg.budget - L * w * cfg.hkv
+    r = allocation.lava_allocate(score.astype(np.float64), cfg.budget, w)
+    lb = np.array([off[l + 1] - off[l] for l in range(L)])
+    if np.array_equal(lb, r["layer_budgets"]):
+        for l in range(L):
+            check_selection(b[l], off[l], sel[l], r["budgets"][l], r["sel"][l], f"lava full layer {l}")
+        log("  layer budgets and all 32 layers' selections exact")
+    else:
+        assert near_tie_in_layer_split(r["entropy"], cfg.budget - L * w * cfg.hkv), "layer budgets differ"
+        log("  layer budgets differ at a float64 near-tie; selections not compared")
+    kf = pipeline.to_host_f64(ev.k_flat)
+    vf = pipeline.to_host_f64(ev.v_flat)
+    ss = ev.seg_start.cpu().numpy()
+    sl = ev.seg_len.cpu().numpy()
+    for l in (0, 19):
+        q64 = pipeline.to_host_f64(data["q_win"][l])
+        k64 = pipeline.to_host_f64(data["k"][l])
+        v64 = pipeline.to_host_f64(data["v"][l])
+        ref, _ = oracle_scores("lava", q64, k64, v64, None, cfg.pool, 0.0)
+        worst = assert_scores_close(score[l], ref, f"lava full layer {l}")
+        check_flat(kf, vf, ss, sl, l, cfg.hkv, k64, v64, sel[l], w, f"lava full layer {l}")
+        log(f"  layer {l}: scores worst rel {worst:.2e}; flat segments exact")
+
+
+def test_criticalkv_full_sampled(gpu_lib):
+    """The Qwen2.5-32B CriticalKV layer at n = 65536, hidden 5120, as the
+    benchmark launches it: the Ada-KV scores in full, the composite at 512
+    sampled keys (the full V.W^O in float64 would take minutes), the two-stage
+    selection bit-exact on the GPU's own fp32 scores, and the flat segments."""
+    from oracle import scoring
+    cfg = configs.QWEN32B_CK
+    log("drawing full Qwen2.5-32B inputs on the device")
+    data = synth.make_batch_torch(cfg, "cuda")
+    ev = pipeline.Eviction(cfg)
+    ev.evict(data["q_win"], data["k"], data["v"], data["w_o"])
+    torch.cuda.synchronize()
+    score = ev.score.cpu().numpy()[0]
+    score2 = ev.score2.cpu().numpy()[0]
+    b, off, sel = ev.host_selection()
+    q64 = pipeline.to_host_f64(data["q_win"][0])
+    k64 = pipeline.to_host_f64(data["k"][0])
+    v64 = pipeline.to_host_f64(data["v"][0])
+    wo64 = pipeline.to_host_f64(data["w_o"])
+    hq, hkv, p = cfg.hq, cfg.hkv, cfg.p
+    a = scoring.snapkv_head_scores(q64, k64, cfg.pool)
+    worst = assert_scores_close(score, scoring.group_mean(a, hkv), "criticalkv full attention score")
+    rng = np.random.default_rng(7)
+    keys = np.unique(np.concatenate([[0, 1, p - 2, p - 1], rng.choice(p, 508, replace=False)]))
+    nrm = scoring.projected_value_norms(v64, wo64.T, hq, keys)
+    comp = ((a[:, keys] + cfg.eps) * nrm).reshape(hkv, hq // hkv, keys.size).mean(axis=1)
+    worst2 = assert_scores_close(score2[:, keys], comp, "criticalkv full composite (sampled keys)")
+    r = allocation.criticalkv_allocate(score.astype(np.float64), score2.astype(np.float64), cfg.budget, cfg.w,
+                                       cfg.alpha, cfg.ck)
+    check_selection(b[0], int(off[0]), sel[0], r["budgets"], r["sel"], "criticalkv full", off_ref=0)
+    kf = pipeline.to_host_f64(ev.k_flat)
+    vf = pipeline.to_host_f64(ev.v_flat)
+    check_flat(kf, vf, ev.seg_start.cpu().numpy(), ev.seg_len.cpu().numpy(), 0, hkv, k64, v64, sel[0], cfg.w,
+               "criticalkv full")
+    log(f"  scores worst rel {worst:.2e}, composite worst rel {worst2:.2e}; selection and flat segments exact")
