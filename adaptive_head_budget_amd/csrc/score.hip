@@ -128,10 +128,14 @@ struct TileRegs {
   }
 };
 
-__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2, float c2) {
+// Row statistics live in the base-2 domain: m is the row maximum times
+// log2(e)/sqrt(d) (one rounding), and every weight is exp2(fma(z, c2, -m)).
+// Both passes use the same rounded m, so its rounding error is a common
+// factor of a row's weights and its sum and cancels in the normalised weight.
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
   const float M = fmaxf(m, m2);
   if (M == -INFINITY) return;
-  l = l * fast_exp2((m - M) * c2) + l2 * fast_exp2((m2 - M) * c2);
+  l = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
   m = M;
 }
 
@@ -260,22 +264,23 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
             if (k0 + 32 * gq + 4 * mb + j <= lim) lm = fmaxf(lm, acc[mb][nb][j]);
       }
       if (lm != -INFINITY) {
+        const float lmc = lm * c2;
         float ls = 0.f;
         if (full) {
 #pragma unroll
           for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ls += fast_exp2((acc[mb][nb][j] - lm) * c2);
+            for (int j = 0; j < 4; ++j) ls += fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
         } else {
 #pragma unroll
           for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float e = fast_exp2((acc[mb][nb][j] - lm) * c2);
+              const float e = fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
               ls += (k0 + 32 * gq + 4 * mb + j <= lim) ? e : 0.f;
             }
         }
-        merge_ml(rm[nb], rl[nb], lm, ls, c2);
+        merge_ml(rm[nb], rl[nb], lmc, ls);
       }
     }
   }
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
 #pragma unroll
     for (int mask = 16; mask <= 32; mask <<= 1) {
       const float om = shfl_xor(rm[nb], mask), ol = shfl_xor(rl[nb], mask);
-      merge_ml(rm[nb], rl[nb], om, ol, c2);
+      merge_ml(rm[nb], rl[nb], om, ol);
     }
     const int r = 16 * nb + c;
     if (gq == 0 && r < w)
@@ -297,7 +302,7 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
 // lane and the reduction tree) into (row max, 1 / row sum).
 __global__ __launch_bounds__(256) void score_stats_merge_kernel(const float2* __restrict__ part,
                                                                 float2* __restrict__ stats, int nrows, int Gw,
-                                                                int nchunk, float c2) {
+                                                                int nchunk) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= nrows) return;
   const int lane = threadIdx.x & 63;
@@ -305,12 +310,12 @@ __global__ __launch_bounds__(256) void score_stats_merge_kernel(const float2* __
   float m = -INFINITY, l = 0.f;
   for (int ch = lane; ch < nchunk; ch += 64) {
     const float2 v = part[((size_t)seg * nchunk + ch) * Gw + row];
-    merge_ml(m, l, v.x, v.y, c2);
+    merge_ml(m, l, v.x, v.y);
   }
 #pragma unroll
   for (int mask = 1; mask < 64; mask <<= 1) {
     const float om = shfl_xor(m, mask), ol = shfl_xor(l, mask);
-    merge_ml(m, l, om, ol, c2);
+    merge_ml(m, l, om, ol);
   }
   if (lane == 0) stats[t] = make_float2(m, 1.0f / l);
 }
@@ -338,7 +343,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
   const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (active ? h : 0)) * (size_t)w * D;
 
   typename M::op_t qop[NB][L::KSTEPS];
-  float smc[NB], sil[NB];   // row max and 1 / row sum
+  float smc[NB], sil[NB];   // scaled row max and 1 / row sum
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int r = 16 * nb + c;
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 #pragma unroll
             for (int kk = 0; kk < 32; ++kk) {
               const float pooled = fmax3(a3[kk], a3[kk + 2], a3[kk + 4]);
-              ks[kk] = fmaf(fast_exp2((pooled - mc) * c2), il_row, ks[kk]);
+              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
             }
           } else {
 #pragma unroll
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
               float pooled = x[kk + 3];
               if (RHO >= 1) pooled = fmax3(pooled, x[kk + 2], x[kk + 4]);
               if (RHO >= 2) pooled = fmax3(pooled, x[kk + 1], x[kk + 5]);
-              ks[kk] = fmaf(fast_exp2((pooled - mc) * c2), il_row, ks[kk]);
+              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
             }
           }
         }
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
             const float mc = smc[nb], il_row = sil[nb];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float e = fast_exp2((acc[nb][j] - mc) * c2);
+              const float e = fast_exp2(fmaf(acc[nb][j], c2, -mc));
               if (mb < 8) {
                 if (interior) ks[4 * mb + j] = fmaf(e, il_row, ks[4 * mb + j]);
                 else ks[4 * mb + j] += (kbase + 4 * mb + j <= lim) ? e * il_row : 0.f;
@@ -625,7 +630,7 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
       score_stats_kernel<T, D, NB, false><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
                                                                           g.w, g.p, P.kend, nchunk, kpw, c2);
     const int nrows = ni * g.hkv * Gw;
-    score_stats_merge_kernel<<<(nrows + 3) / 4, 256, 0, st>>>(part, stats, nrows, Gw, nchunk, c2);
+    score_stats_merge_kernel<<<(nrows + 3) / 4, 256, 0, st>>>(part, stats, nrows, Gw, nchunk);
     const long tiles_total = (long)ntiles * g.hkv * ni;
     int tpw = (int)std::max<long>(1, (tiles_total + target - 1) / target);
     if (tpw > ntiles) tpw = ntiles;
