@@ -33,7 +33,7 @@ constexpr int CH = 4 * WR;      // rows per chunk (4 waves)
 // read of chunk ch of row r then uses slot ch ^ (r & 15), and the 16 rows of
 // one read land in 16 different bank groups.
 template <typename T, int D, int GT>
-__global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
+__global__ __launch_bounds__(256, 4) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                      const T* __restrict__ v_new, T* __restrict__ kf,
                                                      T* __restrict__ vf, const int64_t* __restrict__ seg_start,
                                                      const int32_t* __restrict__ seg_len, int hq, int hkv, int G,
@@ -49,10 +49,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   constexpr int RS = WAVE / LPR;               // row slots per wave
   constexpr int RPL = WR / RS;                 // value rows per lane per chunk
   constexpr int MB = WR / 16;                  // M-blocks per wave
+  // A wave's key slot also holds its partial output once its rows are done.
+  static_assert(GT * D * sizeof(float) <= WR * ROWB, "partial output must fit a key slot");
   __shared__ __align__(16) char kbuf[4][WR * ROWB];
   __shared__ float P[4][WR][GT];
   __shared__ float Sc[4][GT];
-  __shared__ float Ow[4][GT][D];
   __shared__ float Mw[4][GT], Lw[4][GT];
 
   const int s = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
@@ -193,11 +194,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     for (int h = 0; h < GT; ++h)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] += shfl_xor(o[h][e], msk);
+  float* ow = reinterpret_cast<float*>(kbuf[wv]);   // [GT][D]; only this wave used this slot
   if (rs == 0) {
 #pragma unroll
     for (int h = 0; h < GT; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) Ow[wv][h][cc * EPL + e] = o[h][e];
+      for (int e = 0; e < EPL; ++e) ow[h * D + cc * EPL + e] = o[h][e];
   }
   if (gq == 0 && c < GT) {
     Mw[wv][c] = m_run;
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     for (int w2 = 0; w2 < 4; ++w2) {
       const float sc = (Mw[w2][h] == -INFINITY) ? 0.f : fast_exp2((Mw[w2][h] - Mx) * c2);
       l2 += sc * Lw[w2][h];
-      if (e < D) acc2 += sc * Ow[w2][h][e];
+      if (e < D) acc2 += sc * reinterpret_cast<const float*>(kbuf[w2])[h * D + e];
     }
     if (nsplit == 1) {
       if (e < D) out[((size_t)inst * hq + (size_t)g * G + h) * D + e] = acc2 / l2;

@@ -298,36 +298,14 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
   }
 }
 
-// One wave per window row: merge the chunk partials (chunk order fixed by the
-// lane and the reduction tree) into (row max, 1 / row sum).
-__global__ __launch_bounds__(256) void score_stats_merge_kernel(const float2* __restrict__ part,
-                                                                float2* __restrict__ stats, int nrows, int Gw,
-                                                                int nchunk) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= nrows) return;
-  const int lane = threadIdx.x & 63;
-  const int seg = t / Gw, row = t % Gw;
-  float m = -INFINITY, l = 0.f;
-  for (int ch = lane; ch < nchunk; ch += 64) {
-    const float2 v = part[((size_t)seg * nchunk + ch) * Gw + row];
-    merge_ml(m, l, v.x, v.y);
-  }
-#pragma unroll
-  for (int mask = 1; mask < 64; mask <<= 1) {
-    const float om = shfl_xor(m, mask), ol = shfl_xor(l, mask);
-    merge_ml(m, l, om, ol);
-  }
-  if (lane == 0) stats[t] = make_float2(m, 1.0f / l);
-}
-
 // ---------------------------------------------------------------- pass 2
 enum { EMIT_SNAP = 0, EMIT_LAVA = 1 };
 
 template <typename T, int D, int NB, int POOL, int KIND>
 __global__ __launch_bounds__(512) void score_emit_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const float2* __restrict__ stats,
+    const T* __restrict__ q, const T* __restrict__ k, const float2* __restrict__ part,
     const uint32_t* __restrict__ vbar_bits, float* __restrict__ score, float* __restrict__ head_scores,
-    int inst0, int hq, int hkv, int G, int n, int w, int p, int tiles_per_wg, float c2) {
+    int inst0, int hq, int hkv, int G, int n, int w, int p, int nchunk, int tiles_per_wg, float c2) {
   using L = Lay<T, D>;
   using M = Mma<T>;
   constexpr int RHO = (POOL - 1) / 2;
@@ -342,6 +320,9 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
   const T* kb = k + ((size_t)inst * hkv + g) * (size_t)n * D;
   const T* qb = q + ((size_t)inst * hq + (size_t)g * G + (active ? h : 0)) * (size_t)w * D;
 
+  // Row statistics: the pass-1 chunk partials of each row merged here, lane
+  // group gq folding chunks gq, gq+4, ... in order, then the four groups
+  // combined (the same order in every workgroup of the head).
   typename M::op_t qop[NB][L::KSTEPS];
   float smc[NB], sil[NB];   // scaled row max and 1 / row sum
 #pragma unroll
@@ -351,14 +332,21 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 #pragma unroll
     for (int ks = 0; ks < L::KSTEPS; ++ks)
       qop[nb][ks] = ok ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
+    float m = -INFINITY, l = 0.f;
     if (ok) {
-      const float2 st = stats[((size_t)il * hkv + g) * Gw + h * w + r];
-      smc[nb] = st.x;
-      sil[nb] = st.y;
-    } else {
-      smc[nb] = 0.f;    // padding rows: q = 0, weight 0
-      sil[nb] = 0.f;
+      const float2* pr = part + ((size_t)il * hkv + g) * nchunk * (size_t)Gw + h * w + r;
+      for (int ch = gq; ch < nchunk; ch += 4) {
+        const float2 v = pr[(size_t)ch * Gw];
+        merge_ml(m, l, v.x, v.y);
+      }
     }
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const float om = shfl_xor(m, mask), ol = shfl_xor(l, mask);
+      merge_ml(m, l, om, ol);
+    }
+    smc[nb] = ok ? m : 0.f;          // padding rows: q = 0, weight 0
+    sil[nb] = ok ? 1.0f / l : 0.f;
   }
   const float vscale = (KIND == EMIT_LAVA) ? __uint_as_float(vbar_bits[(size_t)inst * hkv + g]) / (float)w : 0.f;
   const float inv_gw = 1.0f / (float)Gw, inv_w = 1.0f / (float)w;
@@ -561,13 +549,13 @@ struct ScorePlan {
   int ib;        // instances per batch
   int nchunk;    // stats chunks per head
   int kend;      // end of the widest row domain
-  size_t off_part, off_stats, off_heads, off_vbar, total;
+  size_t off_part, off_heads, off_vbar, total;
 };
 
 ScorePlan plan_score(const Geo& g) {
   ScorePlan P{};
   const size_t inst_k_bytes = (size_t)g.hkv * g.n * g.d * (g.dtype == ADAKV_BF16 ? 2 : 4);
-  size_t ib = (size_t)(128u << 20) / (inst_k_bytes ? inst_k_bytes : 1);
+  size_t ib = (size_t)(1024u << 20) / (inst_k_bytes ? inst_k_bytes : 1);   // ~1 GiB of K per launch
   if (ib < 1) ib = 1;
   if (ib > (size_t)g.I) ib = g.I;
   P.ib = (int)ib;
@@ -576,7 +564,6 @@ ScorePlan plan_score(const Geo& g) {
   const size_t Gw = (size_t)g.G * g.w;
   size_t off = 0;
   P.off_part = off;  off = align_up(off + (size_t)P.ib * g.hkv * P.nchunk * Gw * sizeof(float2), 256);
-  P.off_stats = off; off = align_up(off + (size_t)P.ib * g.hkv * Gw * sizeof(float2), 256);
   P.off_heads = off;
   if (g.scorer == ADAKV_SCORE_CRITICALKV) off = align_up(off + (size_t)P.ib * g.hq * g.p * sizeof(float), 256);
   P.off_vbar = off;
@@ -591,14 +578,12 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   using L = Lay<T, D>;
   const float c2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
   float2* part = reinterpret_cast<float2*>(ws + P.off_part);
-  float2* stats = reinterpret_cast<float2*>(ws + P.off_stats);
   float* heads = (g.scorer == ADAKV_SCORE_CRITICALKV) ? reinterpret_cast<float*>(ws + P.off_heads) : nullptr;
   uint32_t* vbar = reinterpret_cast<uint32_t*>(ws + P.off_vbar);
   const T* qt = static_cast<const T*>(q);
   const T* kt = static_cast<const T*>(k);
   const bool lava = g.scorer == ADAKV_SCORE_LAVA;
   const int threads = std::max(g.G, 4) * WAVE;
-  const int Gw = g.G * g.w;
   const size_t lds_stats = (size_t)TILE * L::STRIDE;
   const size_t lds_emit = (size_t)TROWS * L::STRIDE + (size_t)(g.G + 1) * TROWS * sizeof(float);
   const int ntiles = (g.p + TILE - 1) / TILE;
@@ -629,8 +614,6 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
     else
       score_stats_kernel<T, D, NB, false><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
                                                                           g.w, g.p, P.kend, nchunk, kpw, c2);
-    const int nrows = ni * g.hkv * Gw;
-    score_stats_merge_kernel<<<(nrows + 3) / 4, 256, 0, st>>>(part, stats, nrows, Gw, nchunk);
     const long tiles_total = (long)ntiles * g.hkv * ni;
     int tpw = (int)std::max<long>(1, (tiles_total + target - 1) / target);
     if (tpw > ntiles) tpw = ntiles;
@@ -639,10 +622,10 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   do {                                                                                                       \
     if (lava)                                                                                                \
       score_emit_kernel<T, D, NB, POOLV, EMIT_LAVA><<<g2, threads, lds_emit, st>>>(                          \
-          qt, kt, stats, vbar, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, tpw, c2);                \
+          qt, kt, part, vbar, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
     else                                                                                                     \
       score_emit_kernel<T, D, NB, POOLV, EMIT_SNAP><<<g2, threads, lds_emit, st>>>(                          \
-          qt, kt, stats, vbar, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, tpw, c2);                  \
+          qt, kt, part, vbar, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
   } while (0)
     switch (g.pool) {
       case 1: EMIT(1); break;
