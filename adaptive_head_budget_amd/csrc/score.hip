@@ -304,7 +304,7 @@ enum { EMIT_SNAP = 0, EMIT_LAVA = 1 };
 template <typename T, int D, int NB, int POOL, int KIND>
 __global__ __launch_bounds__(512) void score_emit_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float2* __restrict__ part,
-    const uint32_t* __restrict__ vbar_bits, float* __restrict__ score, float* __restrict__ head_scores,
+    const float* __restrict__ vpart, int nvblk, float* __restrict__ score, float* __restrict__ head_scores,
     int inst0, int hq, int hkv, int G, int n, int w, int p, int nchunk, int tiles_per_wg, float c2) {
   using L = Lay<T, D>;
   using M = Mma<T>;
@@ -348,7 +348,15 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
     smc[nb] = ok ? m : 0.f;          // padding rows: q = 0, weight 0
     sil[nb] = ok ? 1.0f / l : 0.f;
   }
-  const float vscale = (KIND == EMIT_LAVA) ? __uint_as_float(vbar_bits[(size_t)inst * hkv + g]) / (float)w : 0.f;
+  // LAVa: max_k ||V[k]||_1 of the head from the value-norm kernel's block maxima
+  float vscale = 0.f;
+  if (KIND == EMIT_LAVA) {
+    float vb = 0.f;
+    for (int b = lane; b < nvblk; b += WAVE) vb = fmaxf(vb, vpart[((size_t)inst * hkv + g) * nvblk + b]);
+#pragma unroll
+    for (int mask = 1; mask < 64; mask <<= 1) vb = fmaxf(vb, shfl_xor(vb, mask));
+    vscale = vb / (float)w;
+  }
   const float inv_gw = 1.0f / (float)Gw, inv_w = 1.0f / (float)w;
 
   const int t0 = blockIdx.x * tiles_per_wg;
@@ -502,49 +510,72 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
   }
 }
 
-// LAVa value-norm maximum: vbar[i, g] = max_t sum_e |v[i, g, t, e]| (row sums in
-// a fixed order; the maximum is taken with an integer atomic on the bit
-// pattern, exact and order independent for non-negative floats).
+// LAVa value-norm maximum, max_t sum_e |v[i, g, t, e]|, as one maximum per block
+// of rows_per_wg rows (row sums in a fixed order; a maximum is exact and order
+// independent), reduced by the consumer.  No atomics: with one per wave,
+// contention on the few targets held the workgroups back and cost a fifth of
+// the read bandwidth.  V is read once, so the loads are nontemporal; each lane
+// keeps U of them in flight and a row's |.| sum is completed across its lanes
+// with DPP moves.
+template <int LPR>
+__device__ __forceinline__ float rowsum_lanes(float x) {
+  if (LPR >= 16) x += dpp<DPP_MIRROR>(x);
+  if (LPR >= 8) x += dpp<DPP_HALF_MIRROR>(x);
+  if (LPR >= 4) x += dpp<DPP_XOR2>(x);
+  if (LPR >= 2) x += dpp<DPP_XOR1>(x);
+  return x;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void vbar_kernel(const T* __restrict__ v, uint32_t* __restrict__ vbar_bits,
+__global__ __launch_bounds__(256) void vbar_kernel(const T* __restrict__ v, float* __restrict__ vpart,
                                                    int inst0, int hkv, int n, int rows_per_wg) {
+  __shared__ float wmax[4];
   using L = Lay<T, D>;
   constexpr int LPR = L::CPR;              // lanes per row
-  constexpr int RPP = 256 / LPR;           // rows per pass of the workgroup
+  static_assert(LPR <= 16 && (LPR & (LPR - 1)) == 0, "a row spans at most one 16-lane DPP row");
+  constexpr int RPL = WAVE / LPR;          // rows per wave load
+  constexpr int U = 8;                     // loads in flight per lane
   const int g = blockIdx.y, inst = inst0 + blockIdx.z;
   const T* vb = v + ((size_t)inst * hkv + g) * (size_t)n * D;
-  const int lr = threadIdx.x / LPR, ch = threadIdx.x % LPR;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lr = lane / LPR, ch = lane % LPR;
   const int r0 = blockIdx.x * rows_per_wg, r1 = min(n, r0 + rows_per_wg);
+  const int nwv = blockDim.x / WAVE;
   float best = 0.f;
-  for (int base = r0; base < r1; base += RPP) {   // same trip count for every lane
-    const int r = base + lr;
-    float s = 0.f;
-    if (r < r1) {
-      const u32x4 x = ld16(vb + (size_t)r * D + ch * L::EPC);
+  for (int base = r0 + wv * U * RPL; base < r1; base += nwv * U * RPL) {   // same trip count in a wave
+    u32x4 x[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int r = base + i * RPL + lr;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      x[i] = (r < r1) ? ld16_nt(vb + (size_t)r * D + ch * L::EPC) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      float s = 0.f;
       if (sizeof(T) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s += fabsf(bf16_bits_to_f32(x[e] & 0xffffu)) + fabsf(bf16_bits_to_f32(x[e] >> 16));
+          s += fabsf(bf16_bits_to_f32(x[i][e] & 0xffffu)) + fabsf(bf16_bits_to_f32(x[i][e] >> 16));
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s += fabsf(__uint_as_float(x[e]));
+        for (int e = 0; e < 4; ++e) s += fabsf(__uint_as_float(x[i][e]));
       }
+      best = fmaxf(best, rowsum_lanes<LPR>(s));
     }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) s += shfl_xor(s, m);
-    best = fmaxf(best, s);
   }
 #pragma unroll
   for (int m = LPR; m < 64; m <<= 1) best = fmaxf(best, shfl_xor(best, m));
-  if ((threadIdx.x & 63) == 0) atomicMax(vbar_bits + (size_t)inst * hkv + g, __float_as_uint(best));
-}
-
-__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int cnt) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < cnt) p[t] = v;
+  if (lane == 0) wmax[wv] = best;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    vpart[((size_t)inst * hkv + g) * gridDim.x + blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
 // ---------------------------------------------------------------- host side
+constexpr int VBAR_ROWS = 2048;   // rows per value-norm workgroup
+int vbar_blocks(const Geo& g) { return (g.n + VBAR_ROWS - 1) / VBAR_ROWS; }
+
 struct ScorePlan {
   int ib;        // instances per batch
   int nchunk;    // stats chunks per head
@@ -567,7 +598,7 @@ ScorePlan plan_score(const Geo& g) {
   P.off_heads = off;
   if (g.scorer == ADAKV_SCORE_CRITICALKV) off = align_up(off + (size_t)P.ib * g.hq * g.p * sizeof(float), 256);
   P.off_vbar = off;
-  off = align_up(off + (size_t)g.I * g.hkv * sizeof(uint32_t), 256);
+  if (g.scorer == ADAKV_SCORE_LAVA) off = align_up(off + (size_t)g.I * g.hkv * vbar_blocks(g) * sizeof(float), 256);
   P.total = off;
   return P;
 }
@@ -579,7 +610,8 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   const float c2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
   float2* part = reinterpret_cast<float2*>(ws + P.off_part);
   float* heads = (g.scorer == ADAKV_SCORE_CRITICALKV) ? reinterpret_cast<float*>(ws + P.off_heads) : nullptr;
-  uint32_t* vbar = reinterpret_cast<uint32_t*>(ws + P.off_vbar);
+  float* vpart = reinterpret_cast<float*>(ws + P.off_vbar);
+  const int nvblk = vbar_blocks(g);
   const T* qt = static_cast<const T*>(q);
   const T* kt = static_cast<const T*>(k);
   const bool lava = g.scorer == ADAKV_SCORE_LAVA;
@@ -589,11 +621,8 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   const int ntiles = (g.p + TILE - 1) / TILE;
 
   if (lava) {
-    const int cnt = g.I * g.hkv;
-    fill_u32_kernel<<<(cnt + 255) / 256, 256, 0, st>>>(vbar, 0u, cnt);
-    const int rows_per_wg = 2048;
-    dim3 grid((g.n + rows_per_wg - 1) / rows_per_wg, g.hkv, g.I);
-    vbar_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(v), vbar, 0, g.hkv, g.n, rows_per_wg);
+    dim3 grid(nvblk, g.hkv, g.I);
+    vbar_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(v), vpart, 0, g.hkv, g.n, VBAR_ROWS);
   }
   // about two resident workgroups per CU, each streaming many tiles
   int dev = 0, cus = 256;
@@ -622,10 +651,10 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   do {                                                                                                       \
     if (lava)                                                                                                \
       score_emit_kernel<T, D, NB, POOLV, EMIT_LAVA><<<g2, threads, lds_emit, st>>>(                          \
-          qt, kt, part, vbar, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
+          qt, kt, part, vpart, nvblk, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
     else                                                                                                     \
       score_emit_kernel<T, D, NB, POOLV, EMIT_SNAP><<<g2, threads, lds_emit, st>>>(                          \
-          qt, kt, part, vbar, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
+          qt, kt, part, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
   } while (0)
     switch (g.pool) {
       case 1: EMIT(1); break;
