@@ -6,7 +6,8 @@
 // tensor.  Segment s = i*hkv + g occupies rows seg_start[s] .. seg_start[s+1]-1:
 // B_g selected rows (ascending token order), w window rows, then `reserve`
 // rows kept free for decode appends.  The copy is a pure byte move: every row
-// is moved by 16-byte lanes, consecutive lanes covering consecutive bytes.
+// is moved by 16-byte lanes, consecutive lanes covering consecutive bytes,
+// with nontemporal loads and stores (each byte is touched once here).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -67,26 +68,41 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(const char* __restric
                                                            int64_t flat_rows, char* __restrict__ kf,
                                                            char* __restrict__ vf) {
   __shared__ int64_t src_row[RPW], dst_row[RPW];
+  __shared__ int s_first;
   const int64_t r0 = (int64_t)blockIdx.x * RPW;
+  // packed(s) = seg_start[s] - s * reserve: first retained row of segment s,
+  // strictly increasing in s (every segment holds at least its w window rows)
+  auto packed = [&](int s) { return seg_start[s] - (int64_t)s * reserve; };
+  if (threadIdx.x < WAVE) {
+    // segment of row r0 by a 64-way search: each round one wave probes 64
+    // evenly spaced segments of the range and keeps the last one at or before r0
+    const int lane = threadIdx.x;
+    int lo = 0, len = S;
+    while (len > 1) {
+      const int step = (len + WAVE - 1) / WAVE;
+      const bool ok = lane * step < len && packed(lo + lane * step) <= r0;
+      const uint64_t m = __ballot(ok);   // lane 0 probes lo itself: always set
+      const int j = 63 - __builtin_clzll(m);
+      lo += j * step;
+      len = min(step, len - j * step);
+    }
+    if (lane == 0) s_first = lo;
+  }
+  __syncthreads();
   if (threadIdx.x < RPW) {
     const int64_t r = r0 + threadIdx.x;
     int64_t src = -1, dst = -1;
     if (r < total_rows) {
-      // largest s with packed(s) <= r, packed(s) = seg_start[s] - s * reserve
-      int lo = 0, hi = S - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seg_start[mid] - (int64_t)mid * reserve <= r) lo = mid;
-        else hi = mid - 1;
-      }
-      const int s = lo, inst = s / hkv, g = s % hkv;
-      const int64_t packed_s = seg_start[s] - (int64_t)s * reserve;
+      int s = s_first;
+      while (s + 1 < S && packed(s + 1) <= r) ++s;
+      const int inst = s / hkv, g = s % hkv;
+      const int64_t packed_s = packed(s);
       const int64_t j = r - packed_s;
       const int B = budgets[s];
       int64_t tok;
       if (j < B) {
         const int s0 = inst * hkv;
-        const int64_t head_off = packed_s - (seg_start[s0] - (int64_t)s0 * reserve) - (int64_t)g * w;
+        const int64_t head_off = packed_s - packed(s0) - (int64_t)g * w;
         tok = sel[sel_off[inst] + head_off + j];
       } else {
         tok = (int64_t)p + (j - B);
@@ -108,10 +124,10 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(const char* __restric
     const int64_t src = src_row[rr];
     if (src < 0) continue;
     const int64_t dst = dst_row[rr];
-    const u32x4 a = ld16(k + src * ROWB + ch * 16);
-    const u32x4 b = ld16(v + src * ROWB + ch * 16);
-    st16(kf + dst * ROWB + ch * 16, a);
-    st16(vf + dst * ROWB + ch * 16, b);
+    const u32x4 a = ld16_nt(k + src * ROWB + ch * 16);
+    const u32x4 b = ld16_nt(v + src * ROWB + ch * 16);
+    st16_nt(kf + dst * ROWB + ch * 16, a);
+    st16_nt(vf + dst * ROWB + ch * 16, b);
   }
 }
 
