@@ -118,16 +118,25 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(const char* __restric
   __syncthreads();
   constexpr int LPR = ROWB / 16;          // lanes per row
   constexpr int RPP = 256 / LPR;          // rows per pass
+  constexpr int NP = RPW / RPP;           // rows per thread
   const int rr0 = threadIdx.x / LPR, ch = threadIdx.x % LPR;
+  // all of the thread's loads are issued before its first store
+  u32x4 a[NP], b[NP];
 #pragma unroll
-  for (int rr = rr0; rr < RPW; rr += RPP) {
-    const int64_t src = src_row[rr];
-    if (src < 0) continue;
-    const int64_t dst = dst_row[rr];
-    const u32x4 a = ld16_nt(k + src * ROWB + ch * 16);
-    const u32x4 b = ld16_nt(v + src * ROWB + ch * 16);
-    st16_nt(kf + dst * ROWB + ch * 16, a);
-    st16_nt(vf + dst * ROWB + ch * 16, b);
+  for (int i = 0; i < NP; ++i) {
+    const int64_t src = src_row[rr0 + i * RPP];
+    if (src >= 0) {
+      a[i] = ld16_nt(k + src * ROWB + ch * 16);
+      b[i] = ld16_nt(v + src * ROWB + ch * 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int64_t src = src_row[rr0 + i * RPP], dst = dst_row[rr0 + i * RPP];
+    if (src >= 0) {
+      st16_nt(kf + dst * ROWB + ch * 16, a[i]);
+      st16_nt(vf + dst * ROWB + ch * 16, b[i]);
+    }
   }
 }
 

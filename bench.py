@@ -76,6 +76,29 @@ def evict_bytes(cfg) -> int:
     return b
 
 
+def compact_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one compaction: every retained K and V row read
+    once and written once."""
+    el = 2 if cfg.dtype == "bf16" else 4
+    retained = (cfg.budget if cfg.scorer == "lava" else cfg.instances * cfg.budget)
+    return retained * 2 * cfg.d * el * 2
+
+
+def score_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one scoring pass: K read once (V too for LAVa and
+    CriticalKV), the window queries, the scores written (CriticalKV: W^O once and
+    the second score array too)."""
+    el = 2 if cfg.dtype == "bf16" else 4
+    I, hkv, hq, d, n, w, p = cfg.instances, cfg.hkv, cfg.hq, cfg.d, cfg.n, cfg.w, cfg.p
+    kv = I * hkv * n * d * el
+    b = kv + I * hq * w * d * el + I * hkv * p * 4
+    if cfg.scorer != "snapkv":
+        b += kv
+    if cfg.scorer == "criticalkv":
+        b += hq * d * cfg.hidden * el + I * hkv * p * 4
+    return b
+
+
 def cpu_baseline(cfg):
     """The oracle, untuned, on one instance of the workload on the host cores."""
     from adaptive_head_budget_amd import synth
@@ -196,7 +219,14 @@ def main():
                    "scorer": cfg.scorer},
         "phases_ms": {"score": sc, "allocate": al, "compact": co, "evict": evict_ms, "decode_total": dec_ms_step},
         "evict_hbm_gbps": evict_bytes(cfg) / (evict_ms * 1e-3) / 1e9,
+        "score_hbm_gbps": score_bytes(cfg) / (sc * 1e-3) / 1e9,
+        "compact_hbm_gbps": compact_bytes(cfg) / (co * 1e-3) / 1e9,
     }
+    if cfg.scorer == "criticalkv":
+        # the projected-norm contraction bounds this workload: its flops over the
+        # whole scoring call (window scores included, so a lower bound on the rate)
+        vwo_flops = 2.0 * cfg.instances * cfg.hq * cfg.p * cfg.d * cfg.hidden
+        out["score_mfma_tflops_lower_bound"] = vwo_flops / (sc * 1e-3) / 1e12
     if steps_dec:
         avg_launch_s = float(np.mean(dec_launch_ms)) * 1e-3
         per_launch_bytes = dec_bytes_total / steps_dec
