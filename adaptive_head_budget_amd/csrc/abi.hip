@@ -100,8 +100,9 @@ size_t adakv_workspace_bytes(const adakv_shape* shape, const adakv_alloc* alloc,
   return need < 256 ? 256 : need;
 }
 
-adakv_status adakv_score(const adakv_shape* shape, const void* q_win, const void* k, const void* v, const void* w_o,
-                         float* score, float* score2, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+adakv_status score_call(const adakv_shape* shape, const void* q_win, const void* k, const void* v, const void* w_o,
+                        const float* row_lse, float* score, float* score2, void* ws, size_t ws_bytes, void* stream) {
   Geo g{};
   adakv_status st = check_shape(shape, g);
   if (st != ADAKV_OK) return st;
@@ -114,8 +115,21 @@ adakv_status adakv_score(const adakv_shape* shape, const void* q_win, const void
     if (g.dtype != ADAKV_BF16 || g.d != 128 || g.hidden % 64 != 0) return ADAKV_EUNSUPPORTED;
   }
   if (ws_bytes < score_ws_bytes(g)) return ADAKV_EWORKSPACE;
-  return hip_status(launch_score(g, q_win, k, v, w_o, score, score2, static_cast<char*>(ws),
+  return hip_status(launch_score(g, q_win, k, v, w_o, row_lse, score, score2, static_cast<char*>(ws),
                                  static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+adakv_status adakv_score(const adakv_shape* shape, const void* q_win, const void* k, const void* v, const void* w_o,
+                         float* score, float* score2, void* ws, size_t ws_bytes, void* stream) {
+  return score_call(shape, q_win, k, v, w_o, nullptr, score, score2, ws, ws_bytes, stream);
+}
+
+adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const void* k, const void* v,
+                             const void* w_o, const float* row_lse, float* score, float* score2, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!aligned16(row_lse)) return ADAKV_EINVAL;
+  return score_call(shape, q_win, k, v, w_o, row_lse, score, score2, ws, ws_bytes, stream);
 }
 
 adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, const float* score,

@@ -18,8 +18,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- scoring (score.hip, vwo.hip)
 size_t score_ws_bytes(const Geo& g);
+// row_lse: NULL (two passes over K) or the caller's per-row log-sum-exp [I, hq, w]
 hipError_t launch_score(const Geo& g, const void* q, const void* k, const void* v, const void* w_o,
-                        float* score, float* score2, char* ws, hipStream_t st);
+                        const float* row_lse, float* score, float* score2, char* ws, hipStream_t st);
 hipError_t launch_vwo(const Geo& g, int inst0, int ni, const void* v, const void* w_o,
                       const float* head_scores, float* score2, hipStream_t st);
 

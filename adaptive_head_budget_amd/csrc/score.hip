@@ -304,8 +304,9 @@ enum { EMIT_SNAP = 0, EMIT_LAVA = 1 };
 template <typename T, int D, int NB, int POOL, int KIND>
 __global__ __launch_bounds__(512) void score_emit_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float2* __restrict__ part,
-    const float* __restrict__ vpart, int nvblk, float* __restrict__ score, float* __restrict__ head_scores,
-    int inst0, int hq, int hkv, int G, int n, int w, int p, int nchunk, int tiles_per_wg, float c2) {
+    const float* __restrict__ row_lse, const float* __restrict__ vpart, int nvblk, float* __restrict__ score,
+    float* __restrict__ head_scores, int inst0, int hq, int hkv, int G, int n, int w, int p, int nchunk,
+    int tiles_per_wg, float c2) {
   using L = Lay<T, D>;
   using M = Mma<T>;
   constexpr int RHO = (POOL - 1) / 2;
@@ -322,7 +323,11 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 
   // Row statistics: the pass-1 chunk partials of each row merged here, lane
   // group gq folding chunks gq, gq+4, ... in order, then the four groups
-  // combined (the same order in every workgroup of the head).
+  // combined (the same order in every workgroup of the head).  With row_lse
+  // given (natural-log log-sum-exp of the row's logits / sqrt(d) over its
+  // domain) there is no pass 1: the row's weights are exp2(z*c2 - lse*log2 e),
+  // lse*log2 e split in float64 into hi + lo, hi the reference and exp2(-lo)
+  // the row factor, so the fp32 rounding of the product costs nothing.
   typename M::op_t qop[NB][L::KSTEPS];
   float smc[NB], sil[NB];   // scaled row max and 1 / row sum
 #pragma unroll
@@ -332,6 +337,17 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 #pragma unroll
     for (int ks = 0; ks < L::KSTEPS; ++ks)
       qop[nb][ks] = ok ? M::load(qb + (size_t)r * D + ks * M::KSTEP + M::KPL * gq) : M::zero();
+    if (row_lse != nullptr) {
+      smc[nb] = 0.f;                 // padding rows: q = 0, weight 0
+      sil[nb] = 0.f;
+      if (ok) {
+        const double x = (double)row_lse[((size_t)inst * hq + (size_t)g * G + h) * w + r] * 1.4426950408889634;
+        const float hi = (float)x;
+        smc[nb] = hi;
+        sil[nb] = fast_exp2(-(float)(x - (double)hi));
+      }
+      continue;
+    }
     float m = -INFINITY, l = 0.f;
     if (ok) {
       const float2* pr = part + ((size_t)il * hkv + g) * nchunk * (size_t)Gw + h * w + r;
@@ -605,7 +621,8 @@ ScorePlan plan_score(const Geo& g) {
 
 template <typename T, int D, int NB>
 hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void* k, const void* v,
-                     const void* w_o, float* score, float* score2, char* ws, hipStream_t st) {
+                     const void* w_o, const float* row_lse, float* score, float* score2, char* ws,
+                     hipStream_t st) {
   using L = Lay<T, D>;
   const float c2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
   float2* part = reinterpret_cast<float2*>(ws + P.off_part);
@@ -637,7 +654,9 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
     const int kpw = spw * TILE;
     const int nchunk = (P.kend + kpw - 1) / kpw;
     dim3 g1(nchunk, g.hkv, ni);
-    if (lava)
+    if (row_lse != nullptr) {
+      // the caller's row statistics replace pass 1
+    } else if (lava)
       score_stats_kernel<T, D, NB, true><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
                                                                          g.w, g.p, P.kend, nchunk, kpw, c2);
     else
@@ -651,10 +670,10 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   do {                                                                                                       \
     if (lava)                                                                                                \
       score_emit_kernel<T, D, NB, POOLV, EMIT_LAVA><<<g2, threads, lds_emit, st>>>(                          \
-          qt, kt, part, vpart, nvblk, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
+          qt, kt, part, row_lse, vpart, nvblk, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
     else                                                                                                     \
       score_emit_kernel<T, D, NB, POOLV, EMIT_SNAP><<<g2, threads, lds_emit, st>>>(                          \
-          qt, kt, part, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
+          qt, kt, part, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
   } while (0)
     switch (g.pool) {
       case 1: EMIT(1); break;
@@ -673,10 +692,11 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
 
 template <typename T, int D>
 hipError_t run_score_nb(const Geo& g, const ScorePlan& P, const void* q, const void* k, const void* v,
-                        const void* w_o, float* score, float* score2, char* ws, hipStream_t st) {
-  if (g.w <= 16) return run_score<T, D, 1>(g, P, q, k, v, w_o, score, score2, ws, st);
-  if (g.w <= 32) return run_score<T, D, 2>(g, P, q, k, v, w_o, score, score2, ws, st);
-  return run_score<T, D, 4>(g, P, q, k, v, w_o, score, score2, ws, st);
+                        const void* w_o, const float* row_lse, float* score, float* score2, char* ws,
+                        hipStream_t st) {
+  if (g.w <= 16) return run_score<T, D, 1>(g, P, q, k, v, w_o, row_lse, score, score2, ws, st);
+  if (g.w <= 32) return run_score<T, D, 2>(g, P, q, k, v, w_o, row_lse, score, score2, ws, st);
+  return run_score<T, D, 4>(g, P, q, k, v, w_o, row_lse, score, score2, ws, st);
 }
 
 }  // namespace
@@ -684,14 +704,14 @@ hipError_t run_score_nb(const Geo& g, const ScorePlan& P, const void* q, const v
 size_t score_ws_bytes(const Geo& g) { return plan_score(g).total; }
 
 hipError_t launch_score(const Geo& g, const void* q, const void* k, const void* v, const void* w_o,
-                        float* score, float* score2, char* ws, hipStream_t st) {
+                        const float* row_lse, float* score, float* score2, char* ws, hipStream_t st) {
   const ScorePlan P = plan_score(g);
   if (g.dtype == ADAKV_BF16) {
-    if (g.d == 128) return run_score_nb<uint16_t, 128>(g, P, q, k, v, w_o, score, score2, ws, st);
-    if (g.d == 64) return run_score_nb<uint16_t, 64>(g, P, q, k, v, w_o, score, score2, ws, st);
+    if (g.d == 128) return run_score_nb<uint16_t, 128>(g, P, q, k, v, w_o, row_lse, score, score2, ws, st);
+    if (g.d == 64) return run_score_nb<uint16_t, 64>(g, P, q, k, v, w_o, row_lse, score, score2, ws, st);
   } else {
-    if (g.d == 16) return run_score_nb<float, 16>(g, P, q, k, v, w_o, score, score2, ws, st);
-    if (g.d == 64) return run_score_nb<float, 64>(g, P, q, k, v, w_o, score, score2, ws, st);
+    if (g.d == 16) return run_score_nb<float, 16>(g, P, q, k, v, w_o, row_lse, score, score2, ws, st);
+    if (g.d == 64) return run_score_nb<float, 64>(g, P, q, k, v, w_o, row_lse, score, score2, ws, st);
   }
   return hipErrorInvalidValue;
 }

@@ -20,7 +20,7 @@ ADAKV_BF16, ADAKV_F32 = 0, 1
 ADAKV_SCORE_SNAPKV, ADAKV_SCORE_LAVA, ADAKV_SCORE_CRITICALKV = 0, 1, 2
 ADAKV_ALLOC_ADA, ADAKV_ALLOC_LAVA_LAYERS, ADAKV_ALLOC_ADA_CRITICALKV = 0, 1, 2
 
-EXPORTS = ("adakv_workspace_bytes", "adakv_score", "adakv_allocate", "adakv_compact",
+EXPORTS = ("adakv_workspace_bytes", "adakv_score", "adakv_score_lse", "adakv_allocate", "adakv_compact",
            "adakv_decode_attn", "adakv_strerror", "adakv_version")
 
 
@@ -61,6 +61,8 @@ def load(path: Optional[str] = None):
     lib.adakv_workspace_bytes.restype = ctypes.c_size_t
     lib.adakv_score.argtypes = [S, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.adakv_score.restype = ctypes.c_int
+    lib.adakv_score_lse.argtypes = [S, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.adakv_score_lse.restype = ctypes.c_int
     lib.adakv_allocate.argtypes = [S, A, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.adakv_allocate.restype = ctypes.c_int
     lib.adakv_compact.argtypes = [S, A, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
@@ -119,6 +121,12 @@ def adakv_score(shape, q_win, k, v, w_o, score, score2, ws, stream=None):
     st = load().adakv_score(ctypes.byref(shape), _p(q_win), _p(k), _p(v), _p(w_o), _p(score), _p(score2),
                             _p(ws), _nbytes(ws), _stream(stream))
     _check(st, "adakv_score")
+
+
+def adakv_score_lse(shape, q_win, k, v, w_o, row_lse, score, score2, ws, stream=None):
+    st = load().adakv_score_lse(ctypes.byref(shape), _p(q_win), _p(k), _p(v), _p(w_o), _p(row_lse), _p(score),
+                                _p(score2), _p(ws), _nbytes(ws), _stream(stream))
+    _check(st, "adakv_score_lse")
 
 
 def adakv_allocate(shape, alloc, score, score2, budgets, sel, sel_off, ws, stream=None):

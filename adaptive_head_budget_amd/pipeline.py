@@ -85,8 +85,13 @@ class Eviction:
         self.out = torch.empty((I, s.hq, s.d), dtype=torch.float32, device=device)
         self.step = 0
 
-    def run_score(self, q_win, k, v=None, w_o=None, stream=None):
-        lib.adakv_score(self.shape, q_win, k, v, w_o, self.score, self.score2, self.ws, stream)
+    def run_score(self, q_win, k, v=None, w_o=None, stream=None, row_lse=None):
+        """Window scores; with row_lse [I, hq, w] (float32 log-sum-exp of each
+        window row over its domain) the single-pass entry point is used."""
+        if row_lse is None:
+            lib.adakv_score(self.shape, q_win, k, v, w_o, self.score, self.score2, self.ws, stream)
+        else:
+            lib.adakv_score_lse(self.shape, q_win, k, v, w_o, row_lse, self.score, self.score2, self.ws, stream)
 
     def run_allocate(self, stream=None):
         lib.adakv_allocate(self.shape, self.alloc, self.score, self.score2, self.budgets, self.sel, self.sel_off,
@@ -103,8 +108,8 @@ class Eviction:
         if k_new is not None:
             self.step += 1
 
-    def evict(self, q_win, k, v=None, w_o=None, stream=None):
-        self.run_score(q_win, k, v, w_o, stream)
+    def evict(self, q_win, k, v=None, w_o=None, stream=None, row_lse=None):
+        self.run_score(q_win, k, v, w_o, stream, row_lse)
         self.run_allocate(stream)
         self.run_compact(k, v, stream)
 

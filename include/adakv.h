@@ -4,6 +4,7 @@
  *
  * The path, per layer instance (one layer of one sequence):
  *   adakv_score        observation-window scores of every prefix token
+ *   adakv_score_lse    the same with the window softmax normaliser supplied
  *   adakv_allocate     layer-wide top-B -> per-head budgets -> per-head selection
  *   adakv_compact      selected rows + window rows -> one flat variable-length cache
  *   adakv_decode_attn  decode attention over the flat cache (optional append)
@@ -136,6 +137,25 @@ size_t adakv_workspace_bytes(const adakv_shape* shape, const adakv_alloc* alloc,
 adakv_status adakv_score(const adakv_shape* shape, const void* q_win, const void* k, const void* v,
                          const void* w_o, float* score, float* score2, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* Observation-window scoring with the window softmax normaliser supplied.
+ *
+ * The same scores as adakv_score, but the log-sum-exp of every window row's
+ * logits over the row's key domain comes from the caller instead of a first
+ * pass over the keys, so K is read once.  An attention pass over the window
+ * rows (the prefill, which computes them anyway: [LAVa-notes] "时间复杂度与
+ * 内存使用分析" counts the recent-attention recomputation separately from the
+ * cache computation) leaves exactly this statistic behind.
+ *
+ *   row_lse [I, hq, w] float32   natural-log log-sum-exp of q_win[j,r].k[g,t]/sqrt(d)
+ *                                over row r's domain: the prefix t < p for
+ *                                SNAPKV and CRITICALKV (the domain adakv_score
+ *                                normalises over), t <= p + r for LAVA.  Finite.
+ * Every other argument, the outputs and the supported shapes are those of
+ * adakv_score; ws may be the same size. */
+adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const void* k, const void* v,
+                             const void* w_o, const float* row_lse, float* score, float* score2, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Budget allocation and selection.  Scores must be finite and >= 0 (-0.0 is
  * treated as +0.0).  Ranking: a larger score first; equal scores by the smaller

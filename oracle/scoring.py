@@ -36,7 +36,34 @@ def maxpool_same(x: np.ndarray, kernel: int) -> np.ndarray:
     return out
 
 
-def snapkv_head_scores(q_win: np.ndarray, k: np.ndarray, pool: int) -> np.ndarray:
+def window_lse(q_win: np.ndarray, k: np.ndarray, causal: bool) -> np.ndarray:
+    """Log-sum-exp (natural log) of every window row's logits over the row's
+    key domain, [Hq, w]: the normaliser of the window softmax.
+
+    causal=False: the prefix keys t < p (the Ada-KV / CriticalKV domain,
+    Ada-KV notes, Algorithm 2 step 2); causal=True: keys 0 .. p + r for window
+    row r (the LAVa domain, LAVa notes, Definition 1).  This is the per-row
+    statistic an attention pass over those rows leaves behind; the scorers
+    below accept it in place of computing the normaliser themselves.
+    """
+    hq, w, d = q_win.shape
+    hkv, n, _ = k.shape
+    G = hq // hkv
+    p = n - w
+    out = np.empty((hq, w), dtype=np.float64)
+    for i in range(hq):
+        g = i // G
+        if causal:
+            z = (q_win[i] @ k[g].T) / math.sqrt(d)
+            z = np.where(np.arange(n)[None, :] > (p + np.arange(w))[:, None], -np.inf, z)
+        else:
+            z = (q_win[i] @ k[g, :p].T) / math.sqrt(d)
+        m = z.max(axis=1, keepdims=True)
+        out[i] = (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
+    return out
+
+
+def snapkv_head_scores(q_win: np.ndarray, k: np.ndarray, pool: int, lse: np.ndarray | None = None) -> np.ndarray:
     """Per-query-head window score A-bar_i over the prefix keys, [Hq, p].
 
     Ada-KV notes, Algorithm 2, steps 2-4: softmax of Q_i^win K_i^T, where K_i is
@@ -44,6 +71,8 @@ def snapkv_head_scores(q_win: np.ndarray, k: np.ndarray, pool: int) -> np.ndarra
     row, then the mean over the window rows.  Logits are divided by sqrt(d_h):
     the Ada-KV paper (arXiv HTML, Section 3.1, footnote 5) drops the factor only
     to simplify notation, and the LAVa and CriticalKV pages keep it.
+    With `lse` [Hq, w] given, the softmax normaliser of row r is exp(lse[i, r])
+    (weights exp(z - lse)) instead of being summed here.
     """
     hq, w, d = q_win.shape
     hkv, n, _ = k.shape
@@ -53,7 +82,7 @@ def snapkv_head_scores(q_win: np.ndarray, k: np.ndarray, pool: int) -> np.ndarra
     for i in range(hq):
         g = i // G
         z = (q_win[i] @ k[g, :p].T) / math.sqrt(d)
-        P = softmax_rows(z)
+        P = softmax_rows(z) if lse is None else np.exp(z - np.asarray(lse, dtype=np.float64)[i][:, None])
         out[i] = maxpool_same(P, pool).mean(axis=0)
     return out
 
@@ -68,13 +97,13 @@ def group_mean(a_heads: np.ndarray, hkv: int) -> np.ndarray:
     return a_heads.reshape(hkv, hq // hkv, p).mean(axis=1)
 
 
-def snapkv_scores(q_win: np.ndarray, k: np.ndarray, pool: int) -> np.ndarray:
+def snapkv_scores(q_win: np.ndarray, k: np.ndarray, pool: int, lse: np.ndarray | None = None) -> np.ndarray:
     """Ada-KV / SnapKV score per KV head, [Hkv, p]."""
-    return group_mean(snapkv_head_scores(q_win, k, pool), k.shape[0])
+    return group_mean(snapkv_head_scores(q_win, k, pool, lse), k.shape[0])
 
 
 def lava_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, pool: int,
-                full: bool = False):
+                full: bool = False, lse: np.ndarray | None = None):
     """LAVa score per KV head and the per-head value-norm maximum.
 
     LAVa notes, Definition 1: s[i] = (max_k ||V[k]||_1 / w) * sum over the w
@@ -86,7 +115,8 @@ def lava_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, pool: int,
     eviction only touches tokens outside the recent window ("动态头预算的逐层缓存驱逐").
 
     Returns (scores [Hkv, p], vbar [Hkv]); with full=True the unpooled and
-    pooled vectors over all n tokens are returned as well.
+    pooled vectors over all n tokens are returned as well.  With `lse` [Hq, w]
+    given, row r's weights are exp(z - lse[i, r]) over its causal keys.
     """
     hq, w, d = q_win.shape
     hkv, n, _ = k.shape
@@ -98,7 +128,10 @@ def lava_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, pool: int,
         g = i // G
         z = (q_win[i] @ k[g].T) / math.sqrt(d)
         z = np.where(causal, -np.inf, z)
-        S[i] = softmax_rows(z).sum(axis=0)
+        if lse is None:
+            S[i] = softmax_rows(z).sum(axis=0)
+        else:
+            S[i] = np.exp(z - np.asarray(lse, dtype=np.float64)[i][:, None]).sum(axis=0)
     vbar = np.abs(v).sum(axis=2).max(axis=1)                          # [Hkv]
     s = (vbar[:, None] / w) * S.reshape(hkv, G, n).max(axis=1)
     pooled = maxpool_same(s, pool)
@@ -130,7 +163,7 @@ def projected_value_norms(v: np.ndarray, w_o: np.ndarray, hq: int, rows: slice |
 
 
 def criticalkv_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, w_o: np.ndarray,
-                      pool: int, eps: float):
+                      pool: int, eps: float, lse: np.ndarray | None = None):
     """Ada-KV score (for the budgets) and the CriticalKV composite per KV head.
 
     CriticalKV notes, "两阶段贪心选择算法": composite (A_i + eps) * ||V W^O||_1
@@ -143,7 +176,7 @@ def criticalkv_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, w_o: np.n
     hq = q_win.shape[0]
     hkv, n, _ = k.shape
     p = n - q_win.shape[1]
-    a = snapkv_head_scores(q_win, k, pool)
+    a = snapkv_head_scores(q_win, k, pool, lse)
     nrm = projected_value_norms(v, w_o, hq, slice(0, p))
     comp = ((a + eps) * nrm).reshape(hkv, hq // hkv, p).mean(axis=1)
     return group_mean(a, hkv), comp, a, nrm

@@ -54,16 +54,17 @@ def assert_decode_close(got: np.ndarray, ref: np.ndarray, what: str):
     return float(err.max()), rel
 
 
-def oracle_scores(scorer, q, k, v, w_o, pool, eps):
-    """Oracle scores of one instance (float64 inputs)."""
+def oracle_scores(scorer, q, k, v, w_o, pool, eps, lse=None):
+    """Oracle scores of one instance (float64 inputs); `lse` [Hq, w] is the
+    supplied window-row normaliser of the single-pass entry point."""
     if scorer == "snapkv":
-        return scoring.snapkv_scores(q, k, pool), None
+        return scoring.snapkv_scores(q, k, pool, lse), None
     if scorer == "lava":
-        s, _ = scoring.lava_scores(q, k, v, pool)
+        s, _ = scoring.lava_scores(q, k, v, pool, lse=lse)
         return s, None
     # criticalkv: w_o given in the nn.Linear layout [hidden, hq*d]; the oracle
     # takes the pages' W^O = its transpose.
-    s, comp, _, _ = scoring.criticalkv_scores(q, k, v, w_o.T, pool, eps)
+    s, comp, _, _ = scoring.criticalkv_scores(q, k, v, w_o.T, pool, eps, lse)
     return s, comp
 
 

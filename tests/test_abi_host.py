@@ -91,6 +91,20 @@ def score_status(L, shape, ws_bytes=1 << 40, ptrs=FAKE):
     return L.adakv_score(ctypes.byref(shape), ptrs, ptrs, ptrs, ptrs, ptrs, ptrs, ptrs, ws_bytes, None)
 
 
+def score_lse_status(L, shape, lse=FAKE, ws_bytes=1 << 40, ptrs=FAKE):
+    return L.adakv_score_lse(ctypes.byref(shape), ptrs, ptrs, ptrs, ptrs, lse, ptrs, ptrs, ptrs, ws_bytes, None)
+
+
+def test_score_lse_validates_like_score(L):
+    s = _shape()
+    assert score_lse_status(L, s, lse=None) == lib.ADAKV_EINVAL       # the normaliser is required
+    assert score_lse_status(L, s, lse=FAKE + 4) == lib.ADAKV_EINVAL
+    assert score_lse_status(L, s, ptrs=None) == lib.ADAKV_EINVAL
+    assert score_lse_status(L, s, ws_bytes=16) == lib.ADAKV_EWORKSPACE
+    assert score_lse_status(L, _shape(hq=33)) == lib.ADAKV_EINVAL
+    assert score_lse_status(L, _shape(w=65)) == lib.ADAKV_EUNSUPPORTED
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(hq=33), lib.ADAKV_EINVAL),            # hq not a multiple of hkv
     (dict(n=32), lib.ADAKV_EINVAL),             # no prefix: n <= w

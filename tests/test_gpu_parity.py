@@ -11,7 +11,7 @@ import torch
 
 from adaptive_head_budget_amd import configs, pipeline, synth
 from adaptive_head_budget_amd.configs import scaled
-from oracle import allocation, cache
+from oracle import allocation, cache, scoring
 from parity_util import (assert_decode_close, assert_scores_close, check_flat, check_selection, jaccard, log,
                          near_tie_in_layer_split, oracle_scores)
 
@@ -28,9 +28,11 @@ def _w(x, dtype):
     return synth.widen(x, dtype)
 
 
-def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None):
+def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, single_pass=False):
     """Run score -> allocate -> compact -> decode on numpy-drawn inputs and
-    check every stage.  Returns the Eviction object."""
+    check every stage.  Returns the Eviction object.  single_pass: score
+    through adakv_score_lse with the oracle's window-row log-sum-exp (rounded
+    to float32, the same input for both sides)."""
     log(f"case {label}: {cfg.name} I={I} n={n} budget={budget} reserve={reserve} steps={steps}")
     if steps != cfg.decode_steps:
         cfg = scaled(cfg, decode_steps=steps)       # draws of q, k, v do not depend on this
@@ -41,16 +43,22 @@ def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None):
     v = pipeline.to_device(st["v"], dt)
     w_o = pipeline.to_device(insts[0]["w_o"], dt) if cfg.scorer == "criticalkv" else None
     ev = pipeline.Eviction(cfg, n_inst=I, n=n, budget=budget, reserve=reserve)
-    ev.run_score(q, k, v if cfg.scorer != "snapkv" else None, w_o)
-    torch.cuda.synchronize()
-    score = ev.score.cpu().numpy()
-    score2 = ev.score2.cpu().numpy() if ev.score2 is not None else None
     w = cfg.w
     k64 = [_w(x["k"], dt) for x in insts]
     v64 = [_w(x["v"], dt) for x in insts]
+    lse32 = None
+    if single_pass:
+        lse32 = np.stack([scoring.window_lse(_w(insts[i]["q_win"], dt), k64[i], causal=cfg.scorer == "lava")
+                          for i in range(I)]).astype(np.float32)
+    ev.run_score(q, k, v if cfg.scorer != "snapkv" else None, w_o,
+                 row_lse=None if lse32 is None else torch.from_numpy(lse32).cuda())
+    torch.cuda.synchronize()
+    score = ev.score.cpu().numpy()
+    score2 = ev.score2.cpu().numpy() if ev.score2 is not None else None
     for i in (range(I) if check_scores_of is None else check_scores_of):
         ref, ref2 = oracle_scores(cfg.scorer, _w(insts[i]["q_win"], dt), k64[i], v64[i],
-                                  _w(insts[0]["w_o"], dt) if w_o is not None else None, cfg.pool, cfg.eps)
+                                  _w(insts[0]["w_o"], dt) if w_o is not None else None, cfg.pool, cfg.eps,
+                                  None if lse32 is None else lse32[i].astype(np.float64))
         worst = assert_scores_close(score[i], ref, f"{label} score inst {i}")
         if ref2 is not None:
             assert_scores_close(score2[i], ref2, f"{label} composite inst {i}")
@@ -139,6 +147,28 @@ def test_criticalkv_reduced(gpu_lib):
     cfg = scaled(configs.QWEN32B_CK, hidden=1024)
     n = 2100
     run_case(cfg, 1, n, (40 * cfg.hkv * n) // 100, 0, 0, "criticalkv n2100 D1024")
+
+
+# ------------------------------------------------------------------ single pass (row statistics supplied)
+def test_single_pass_tiny(gpu_lib):
+    cfg = configs.TINY_MHA
+    run_case(cfg, 1, cfg.n, cfg.budget, cfg.reserve, cfg.decode_steps, "tiny single-pass", single_pass=True)
+
+
+def test_single_pass_llama_reduced(gpu_lib):
+    cfg = scaled(configs.LLAMA8B_MODEL, layers=2, batch=2)
+    run_case(cfg, 4, 3000, 8 * 200, 1, 1, "llama-model I4 n3000 single-pass", single_pass=True)
+
+
+def test_single_pass_lava_reduced(gpu_lib):
+    cfg = scaled(configs.MISTRAL7B_LAVA, layers=4)
+    run_case(cfg, 4, 3000, 4 * 8 * (32 + 96), 0, 0, "lava L4 n3000 single-pass", single_pass=True)
+
+
+def test_single_pass_criticalkv_reduced(gpu_lib):
+    cfg = scaled(configs.QWEN32B_CK, hidden=1024)
+    n = 2100
+    run_case(cfg, 1, n, (40 * cfg.hkv * n) // 100, 0, 0, "criticalkv n2100 D1024 single-pass", single_pass=True)
 
 
 # ------------------------------------------------------------------ edge cases

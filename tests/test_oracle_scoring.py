@@ -200,3 +200,44 @@ def _mean_then_pool(q_win, k, pool):
 def test_pins_catch_planted_mistakes():
     assert not check_single_row_is_softmax_attention(_no_sqrt_d)
     assert not check_pool_each_row_then_mean(_mean_then_pool)
+
+
+# ---------------------------------------------------------------- supplied normaliser
+def test_window_lse_matches_scipy_logsumexp():
+    """The row statistic is SciPy's logsumexp of the scaled logits over the
+    row's domain: the prefix keys, or keys 0 .. p + r causally."""
+    import scipy.special
+    r = rng(31)
+    hq, hkv, w, d, n = 4, 2, 3, 8, 25
+    q = r.standard_normal((hq, w, d)) * 3.0
+    k = r.standard_normal((hkv, n, d))
+    p = n - w
+    pre = scoring.window_lse(q, k, causal=False)
+    cau = scoring.window_lse(q, k, causal=True)
+    for i in range(hq):
+        z = q[i] @ k[i // 2].T / math.sqrt(d)
+        np.testing.assert_allclose(pre[i], scipy.special.logsumexp(z[:, :p], axis=1), rtol=1e-14)
+        for row in range(w):
+            np.testing.assert_allclose(cau[i, row], scipy.special.logsumexp(z[row, :p + row + 1]), rtol=1e-14)
+
+
+def test_scores_from_supplied_normaliser():
+    """With the exact normaliser supplied the scores are the two-pass scores;
+    every row's normaliser raised by delta scales the Ada-KV score by
+    exp(-delta) (max pooling and the means are positively homogeneous) and
+    the LAVa score likewise."""
+    r = rng(32)
+    hq, hkv, w, d, n = 4, 2, 4, 16, 40
+    q = r.standard_normal((hq, w, d)) * 2.0
+    k = r.standard_normal((hkv, n, d))
+    v = r.standard_normal((hkv, n, d))
+    a = scoring.snapkv_scores(q, k, 3)
+    lse = scoring.window_lse(q, k, causal=False)
+    np.testing.assert_allclose(scoring.snapkv_scores(q, k, 3, lse), a, rtol=1e-12)
+    np.testing.assert_allclose(scoring.snapkv_scores(q, k, 3, lse + 0.7), a * math.exp(-0.7), rtol=1e-12)
+    s, _ = scoring.lava_scores(q, k, v, 5)
+    lc = scoring.window_lse(q, k, causal=True)
+    np.testing.assert_allclose(scoring.lava_scores(q, k, v, 5, lse=lc)[0], s, rtol=1e-12)
+    np.testing.assert_allclose(scoring.lava_scores(q, k, v, 5, lse=lc - 0.3)[0], s * math.exp(0.3), rtol=1e-12)
+    # the Ada-KV domain excludes the window keys: the causal statistic is not it
+    assert not np.allclose(scoring.snapkv_scores(q, k, 3, lc), a, rtol=1e-6)
