@@ -166,7 +166,11 @@ adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const 
  *               (Algorithm 2, step 8) alpha*f_g + (1-alpha)*P/hkv is made
  *               integer exactly (floors, then one extra unit to the largest
  *               remainders, lower head first on equal remainders) so the
- *               budgets sum to P; then each head keeps its top B_g.
+ *               budgets sum to P; then each head keeps its top B_g.  alpha
+ *               weighs the adaptive counts as the formula is printed; the
+ *               reading in which alpha weighs the uniform share instead
+ *               ("smaller alpha, more aggressive allocation" in the notes'
+ *               robustness analysis) is alpha_num/alpha_den = 1 - alpha.
  *   LAVA_LAYERS [LAVa-notes] "基于不确定性的层预算分配": instance l is layer l;
  *               e_l = entropy of the layer's normalised scores / (hkv*p);
  *               B' = budget - I*w*hkv is split in proportion to e_l (largest

@@ -191,7 +191,7 @@ def test_budget_extremes(gpu_lib):
     run_case(base, 1, n, base.n * 0 + n * base.hkv, 1, 1, "keep all")       # P = hkv * p
 
 
-@pytest.mark.parametrize("alpha", [(0, 1), (1, 1), (1, 2)])
+@pytest.mark.parametrize("alpha", [(0, 1), (1, 1), (1, 2), (4, 5)])   # (4, 5): the other reading of alpha = 0.2
 def test_safeguard_settings(gpu_lib, alpha):
     cfg = scaled(configs.LLAMA8B_LAYER, alpha=alpha, name=f"alpha{alpha[0]}_{alpha[1]}", decode_steps=0)
     run_case(cfg, 2, 1500, 8 * 100, 0, 0, f"alpha {alpha}")
