@@ -8,9 +8,10 @@ suite, the package smoke check and the benchmark's CPU-baseline leg may use
 it.
 
 Modules
-  scoring     observation-window scores: Ada-KV/SnapKV, LAVa, CriticalKV
+  scoring     observation-window scores: Ada-KV/SnapKV, LAVa, CriticalKV, LaProx
   allocation  Ada-KV budget allocation with the safeguard, per-head top-k,
-              LAVa entropy layer budgets, CriticalKV two-stage selection
+              LAVa entropy layer budgets, CriticalKV two-stage selection,
+              the model-wide top-k of LaProx
   cache       compaction into the retained cache and decode attention
   bounds      the pages' loss bounds and the renormalisation identity
 

@@ -162,3 +162,28 @@ def criticalkv_allocate(score: np.ndarray, composite: np.ndarray, budget: int, w
     out = dict(base)
     out.update({"sel": sel, "stage1": s1, "stage2": s2})
     return out
+
+
+def global_allocate(scores: np.ndarray, total: int, w: int) -> Dict:
+    """Model-wide top-k over every head of every instance.
+
+    LaProx page, Algorithm 1: S = TopK(p, B_total), with window tokens scored
+    infinity (so always kept); abstract and Section 1: tokens of all heads and
+    all layers get globally comparable scores and one model-wide selection
+    replaces per-head decisions.  The windows are kept outside the ranking:
+    B' = total - L * w * Hkv prefix entries are taken from the flattened
+    [L, Hkv, p] scores by (-score, flat index).  A per-layer top-k is this
+    with L = 1.
+    scores: [L, Hkv, p].  Returns dict with B', budgets [L, Hkv], layer totals
+    and sel[l][g] (ascending).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    L, hkv, p = scores.shape
+    Bp = int(total) - L * w * hkv
+    if Bp < 0 or Bp > L * hkv * p:
+        raise ValueError("total budget out of range")
+    top = top_indices(scores.ravel(), Bp)
+    row = top // p
+    budgets = np.bincount(row, minlength=L * hkv).astype(np.int64).reshape(L, hkv)
+    sel = [[np.sort(top[row == l * hkv + g] % p) for g in range(hkv)] for l in range(L)]
+    return {"Bp": Bp, "budgets": budgets, "layer_budgets": budgets.sum(axis=1), "sel": sel}

@@ -36,15 +36,16 @@ def maxpool_same(x: np.ndarray, kernel: int) -> np.ndarray:
     return out
 
 
-def window_lse(q_win: np.ndarray, k: np.ndarray, causal: bool) -> np.ndarray:
+def window_lse(q_win: np.ndarray, k: np.ndarray, causal: bool, full: bool = False) -> np.ndarray:
     """Log-sum-exp (natural log) of every window row's logits over the row's
     key domain, [Hq, w]: the normaliser of the window softmax.
 
     causal=False: the prefix keys t < p (the Ada-KV / CriticalKV domain,
     Ada-KV notes, Algorithm 2 step 2); causal=True: keys 0 .. p + r for window
-    row r (the LAVa domain, LAVa notes, Definition 1).  This is the per-row
-    statistic an attention pass over those rows leaves behind; the scorers
-    below accept it in place of computing the normaliser themselves.
+    row r (the LAVa domain, LAVa notes, Definition 1); full=True: all n keys
+    with no mask (the LaProx domain, see laprox_head_scores).  This is the
+    per-row statistic an attention pass over those rows leaves behind; the
+    scorers below accept it in place of computing the normaliser themselves.
     """
     hq, w, d = q_win.shape
     hkv, n, _ = k.shape
@@ -53,7 +54,9 @@ def window_lse(q_win: np.ndarray, k: np.ndarray, causal: bool) -> np.ndarray:
     out = np.empty((hq, w), dtype=np.float64)
     for i in range(hq):
         g = i // G
-        if causal:
+        if full:
+            z = (q_win[i] @ k[g].T) / math.sqrt(d)
+        elif causal:
             z = (q_win[i] @ k[g].T) / math.sqrt(d)
             z = np.where(np.arange(n)[None, :] > (p + np.arange(w))[:, None], -np.inf, z)
         else:
@@ -180,3 +183,77 @@ def criticalkv_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, w_o: np.n
     nrm = projected_value_norms(v, w_o, hq, slice(0, p))
     comp = ((a + eps) * nrm).reshape(hkv, hq // hkv, p).mean(axis=1)
     return group_mean(a, hkv), comp, a, nrm
+
+
+def projected_value_l2(v: np.ndarray, w_o: np.ndarray, hq: int, rows: slice | np.ndarray | None = None) -> np.ndarray:
+    """||(V W^O_i)[k, :]||_2 for every query head i and the chosen keys, [Hq, keys].
+
+    LaProx page, Section 4.1, Algorithm 1: H = V W_O and the factor
+    ||H[i, :]||_2 of token i.  W^O_i is the d-row block i of the [Hq*d, D]
+    output projection, as in projected_value_norms; the product is formed in
+    row chunks, which changes no arithmetic of any output element.
+    """
+    hkv, n, d = v.shape
+    G = hq // hkv
+    keys = np.arange(n)[rows] if rows is not None else np.arange(n)
+    out = np.empty((hq, keys.size), dtype=np.float64)
+    for i in range(hq):
+        g = i // G
+        wi = w_o[i * d:(i + 1) * d]
+        for s in range(0, keys.size, 2048):
+            kk = keys[s:s + 2048]
+            h = v[g, kk] @ wi
+            out[i, s:s + 2048] = np.sqrt((h * h).sum(axis=1))
+    return out
+
+
+def laprox_attention_l2(q_win: np.ndarray, k: np.ndarray, lse: np.ndarray | None = None) -> np.ndarray:
+    """||A_i[:, t]||_2 over the w window rows for every query head i and prefix
+    token t, [Hq, p].
+
+    LaProx page, Section 4.1, Algorithm 1: A = Softmax(Q[-w:, ] K^T / sqrt(d_k))
+    over the cached keys, as printed: every window row over all n keys, no
+    mask.  The norm runs down column t of A, i.e. over the window rows.  With
+    `lse` [Hq, w] given, row r's weights are exp(z - lse[i, r]).
+    """
+    hq, w, d = q_win.shape
+    hkv, n, _ = k.shape
+    G = hq // hkv
+    p = n - w
+    out = np.empty((hq, p), dtype=np.float64)
+    for i in range(hq):
+        g = i // G
+        z = (q_win[i] @ k[g].T) / math.sqrt(d)
+        A = softmax_rows(z) if lse is None else np.exp(z - np.asarray(lse, dtype=np.float64)[i][:, None])
+        out[i] = np.sqrt((A[:, :p] ** 2).sum(axis=0))
+    return out
+
+
+def laprox_head_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, w_o: np.ndarray,
+                       lse: np.ndarray | None = None, keys: np.ndarray | None = None) -> np.ndarray:
+    """LaProx token score per query head, p_i[t] = ||A_i[:, t]||_2 * ||(V W^O_i)[t, :]||_2,
+    [Hq, p] (or [Hq, len(keys)] for a subset of prefix tokens).
+
+    LaProx page, Section 4.1, Algorithm 1, "评分 token": tokens of the window
+    (t >= T - w) score infinity and are always kept, so only the prefix is
+    scored here.  Section 4 opening: the layer output splits exactly into per-
+    head contributions, and p_i[t] is the Frobenius norm of head i's rank-one
+    contribution A_i[:, t] (V W^O_i)[t, :] of token t.
+    """
+    hq, w, d = q_win.shape
+    hkv, n, _ = k.shape
+    p = n - w
+    a = laprox_attention_l2(q_win, k, lse)
+    if keys is None:
+        keys = np.arange(p)
+    return a[:, keys] * projected_value_l2(v, w_o, hq, np.asarray(keys))
+
+
+def laprox_scores(q_win: np.ndarray, k: np.ndarray, v: np.ndarray, w_o: np.ndarray,
+                  lse: np.ndarray | None = None, keys: np.ndarray | None = None) -> np.ndarray:
+    """LaProx score per KV head, [Hkv, p]: the mean of p_i over the query heads
+    of the group.  The page describes multi-head attention only; a GQA KV entry
+    serves its G query heads, and the group takes the mean of their scores as
+    the Ada-KV and CriticalKV scorers do (for a fixed G the mean ranks as the
+    sum does, also across layers)."""
+    return group_mean(laprox_head_scores(q_win, k, v, w_o, lse, keys), k.shape[0])

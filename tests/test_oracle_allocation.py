@@ -275,3 +275,66 @@ def _index_tie_reversed(score, budget, w, alpha):
 def test_pins_catch_planted_mistakes():
     assert not check_safeguard(_reversed_alpha)
     assert not check_alg1_fixture(_index_tie_reversed)
+
+
+# ---------------------------------------------------------------- model-wide top-k (LaProx)
+def check_global_brute_force(fn) -> bool:
+    """Scores drawn from a few values (many ties): the kept entries are the
+    first B' of every (instance, head, token) triple sorted by Python's own
+    tuple order (-score, l, g, t); budgets are their counts."""
+    r = np.random.default_rng(51)
+    L, hkv, p, w = 3, 2, 9, 2
+    s = r.integers(0, 4, (L, hkv, p)).astype(np.float64)
+    for Bp in (0, 1, 7, 20, L * hkv * p):
+        out = fn(s, Bp + L * w * hkv, w)
+        order = sorted((-s[l, g, t], l, g, t) for l in range(L) for g in range(hkv) for t in range(p))[:Bp]
+        for l in range(L):
+            for g in range(hkv):
+                want = sorted(t for (_, ll, gg, t) in order if (ll, gg) == (l, g))
+                if list(out["sel"][l][g]) != want or out["budgets"][l][g] != len(want):
+                    return False
+    return True
+
+
+def test_global_allocate_brute_force():
+    assert check_global_brute_force(allocation.global_allocate)
+
+
+def test_global_allocate_single_layer_is_ada_without_safeguard():
+    """L = 1: one top-B' over the heads is Ada-KV's Algorithm 1 with the
+    counts used as budgets (alpha = 1)."""
+    r = np.random.default_rng(52)
+    hkv, p, w = 4, 50, 3
+    s = r.random((hkv, p)) ** 3
+    for B in (w * hkv, w * hkv + 17, w * hkv + hkv * p):
+        a = allocation.ada_allocate(s, B, w, (1, 1))
+        gl = allocation.global_allocate(s[None], B, w)
+        assert list(gl["budgets"][0]) == list(a["budgets"])
+        assert all(list(x) == list(y) for x, y in zip(gl["sel"][0], a["sel"]))
+
+
+def test_global_allocate_threshold_invariant():
+    r = np.random.default_rng(53)
+    L, hkv, p, w = 4, 3, 40, 2
+    s = r.random((L, hkv, p)) ** 5
+    out = allocation.global_allocate(s, 150 + L * w * hkv, w)
+    assert out["budgets"].sum() == 150 and out["layer_budgets"].sum() == 150
+    kept = np.zeros_like(s, dtype=bool)
+    for l in range(L):
+        for g in range(hkv):
+            kept[l, g, out["sel"][l][g]] = True
+    assert s[kept].min() >= s[~kept].max()
+    with pytest.raises(ValueError):
+        allocation.global_allocate(s, L * w * hkv - 1, w)
+
+
+def _global_per_layer(scores, total, w):
+    """Planted: equal per-layer shares instead of one model-wide ranking."""
+    L, hkv, p = scores.shape
+    Bp = total - L * w * hkv
+    outs = [allocation.global_allocate(scores[l:l + 1], Bp // L + (l < Bp % L) + w * hkv, w) for l in range(L)]
+    return {"budgets": np.stack([o["budgets"][0] for o in outs]), "sel": [o["sel"][0] for o in outs]}
+
+
+def test_global_pins_catch_planted_mistakes():
+    assert not check_global_brute_force(_global_per_layer)

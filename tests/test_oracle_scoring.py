@@ -241,3 +241,102 @@ def test_scores_from_supplied_normaliser():
     np.testing.assert_allclose(scoring.lava_scores(q, k, v, 5, lse=lc - 0.3)[0], s * math.exp(0.3), rtol=1e-12)
     # the Ada-KV domain excludes the window keys: the causal statistic is not it
     assert not np.allclose(scoring.snapkv_scores(q, k, 3, lc), a, rtol=1e-6)
+
+
+# ---------------------------------------------------------------- LaProx
+def check_laprox_is_frobenius_norm(fn) -> bool:
+    """G = 1: p_i[t] is the Frobenius norm of the explicit w x D matrix
+    A_i[:, t] (V W^O_i)[t, :], with A from torch's scaled-dot-product attention
+    over all n keys (no mask) and the product formed entry by entry."""
+    r = rng(41)
+    hq, hkv, w, d, n, D = 3, 3, 4, 8, 19, 6
+    q = r.standard_normal((hq, w, d)) * 1.5
+    k = r.standard_normal((hkv, n, d))
+    v = r.standard_normal((hkv, n, d))
+    w_o = r.standard_normal((hq * d, D))
+    got = fn(q, k, v, w_o)
+    p = n - w
+    for i in range(hq):
+        A = sdpa_weights(q[i], k[i])                                     # [w, n]
+        for t in range(p):
+            h = [sum(v[i, t, e] * w_o[i * d + e, c] for e in range(d)) for c in range(D)]
+            M = np.array([[A[row, t] * h[c] for c in range(D)] for row in range(w)])
+            if not np.isclose(got[i, t], np.linalg.norm(M, "fro"), rtol=1e-12, atol=0.0):
+                return False
+    return True
+
+
+def test_laprox_is_frobenius_norm_of_token_contribution():
+    assert check_laprox_is_frobenius_norm(scoring.laprox_head_scores)
+
+
+def check_laprox_uniform_closed_form(fn) -> bool:
+    """Constant keys: every weight is 1/n, so ||A_i[:, t]||_2 = sqrt(w)/n; with
+    W^O_i = c_i * I (D = d) the value factor is c_i ||V_g[t]||_2, and the group
+    takes the mean over its heads."""
+    r = rng(42)
+    hq, hkv, w, d, n = 4, 2, 5, 8, 30
+    q = r.standard_normal((hq, w, d))
+    k = np.broadcast_to(r.standard_normal((hkv, 1, d)), (hkv, n, d)).copy()
+    v = r.standard_normal((hkv, n, d))
+    c = np.array([0.5, 2.0, 3.0, 7.0])
+    w_o = np.concatenate([c[i] * np.eye(d) for i in range(hq)], axis=0)
+    got = fn(q, k, v, w_o)
+    p = n - w
+    ref = np.stack([math.sqrt(w) / n * np.linalg.norm(v[g, :p], axis=1) * c[2 * g:2 * g + 2].mean()
+                    for g in range(hkv)])
+    return bool(np.allclose(got, ref, rtol=1e-13, atol=0.0))
+
+
+def test_laprox_uniform_attention_closed_form():
+    assert check_laprox_uniform_closed_form(scoring.laprox_scores)
+
+
+def test_laprox_group_mean_and_key_subset():
+    r = rng(43)
+    hq, hkv, w, d, n, D = 4, 2, 3, 8, 26, 10
+    q = r.standard_normal((hq, w, d)) * 2.0
+    k = r.standard_normal((hkv, n, d))
+    v = r.standard_normal((hkv, n, d))
+    w_o = r.standard_normal((hq * d, D))
+    s = scoring.laprox_scores(q, k, v, w_o)
+    for g in range(hkv):
+        parts = [scoring.laprox_head_scores(q[i:i + 1], k[g:g + 1], v[g:g + 1], w_o[i * d:(i + 1) * d])[0]
+                 for i in (2 * g, 2 * g + 1)]
+        np.testing.assert_allclose(s[g], 0.5 * (parts[0] + parts[1]), rtol=1e-13)
+    keys = np.array([0, 5, 22])
+    np.testing.assert_allclose(scoring.laprox_scores(q, k, v, w_o, keys=keys), s[:, keys], rtol=1e-13)
+    # the supplied normaliser over all keys reproduces the two-pass score; the
+    # prefix-only normaliser (the Ada-KV domain) does not
+    lse = scoring.window_lse(q, k, causal=False, full=True)
+    np.testing.assert_allclose(scoring.laprox_scores(q, k, v, w_o, lse), s, rtol=1e-12)
+    assert not np.allclose(scoring.laprox_scores(q, k, v, w_o, scoring.window_lse(q, k, causal=False)), s,
+                           rtol=1e-6)
+
+
+def _laprox_causal(q_win, k, v, w_o):
+    """Planted: causal window rows (the LAVa domain) instead of the printed softmax."""
+    hq, w, d = q_win.shape
+    hkv, n, _ = k.shape
+    p = n - w
+    out = np.empty((hq, p))
+    for i in range(hq):
+        g = i // (hq // hkv)
+        z = q_win[i] @ k[g].T / math.sqrt(d)
+        z = np.where(np.arange(n)[None, :] > (p + np.arange(w))[:, None], -np.inf, z)
+        a = np.sqrt((scoring.softmax_rows(z)[:, :p] ** 2).sum(axis=0))
+        out[i] = a * scoring.projected_value_l2(v, w_o, hq)[i, :p]
+    return out
+
+
+def _laprox_l1_values(q_win, k, v, w_o):
+    """Planted: the L1 value norm of CriticalKV in place of the L2 norm."""
+    hkv = k.shape[0]
+    a = scoring.laprox_attention_l2(q_win, k)
+    nrm = scoring.projected_value_norms(v, w_o, q_win.shape[0], slice(0, a.shape[1]))
+    return scoring.group_mean(a * nrm, hkv)
+
+
+def test_laprox_pins_catch_planted_mistakes():
+    assert not check_laprox_is_frobenius_norm(_laprox_causal)
+    assert not check_laprox_uniform_closed_form(_laprox_l1_values)
