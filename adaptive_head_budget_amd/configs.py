@@ -13,6 +13,10 @@ Sources for the settings (page title, section):
     written as multiples of H*L; 128K contexts in the latency study.
   * CriticalKV notes, "主实验": 40 % budget, Qwen2.5-32B among the models;
     "损失函数 / 训练策略": stage split alpha 0.5.
+  * LaProx page, abstract and Section 3: Mistral-7B-Instruct (v0.3) is the
+    model analysed; 5 % of the KV cache kept; one model-wide selection across
+    heads and layers.  The window length is not given there; the other pages'
+    32 is used.
 """
 from __future__ import annotations
 
@@ -32,12 +36,12 @@ class Workload:
     layers: int
     batch: int
     dtype: str              # "bf16" or "f32"
-    scorer: str             # "snapkv", "lava" or "criticalkv"
+    scorer: str             # "snapkv", "lava", "criticalkv" or "laprox"
     budget: int             # snapkv/criticalkv: per instance, window included;
-                            # lava: total over all layers, windows included
+                            # lava, laprox: total over all layers, windows included
     alpha: Tuple[int, int] = (1, 5)   # Ada-KV safeguard as an exact rational
     ck: Tuple[int, int] = (1, 2)      # CriticalKV stage-1 share
-    hidden: int = 0                   # CriticalKV: model hidden size D
+    hidden: int = 0                   # CriticalKV, LaProx: model hidden size D
     eps: float = 1e-6                 # CriticalKV: additive epsilon
     sinks: int = 0                    # leading keys aligned with the queries
     tau: Union[Tuple[float, ...], Tuple[str, float, float]] = ("loguniform", 0.1, 3.0)
@@ -83,7 +87,12 @@ QWEN32B_CK = Workload(
     layers=1, batch=1, dtype="bf16", scorer="criticalkv",
     budget=(40 * 8 * 65536) // 100, hidden=5120, sinks=4, reserve=0, decode_steps=0)
 
-ALL = (TINY_MHA, LLAMA8B_LAYER, LLAMA8B_MODEL, MISTRAL7B_LAVA, QWEN32B_CK)
+MISTRAL7B_LAPROX = Workload(
+    name="mistral-7b_laprox_32L_n32768", hq=32, hkv=8, d=128, n=32768, w=32, pool=1,
+    layers=32, batch=1, dtype="bf16", scorer="laprox",
+    budget=(5 * 32 * 8 * 32768) // 100, hidden=4096, sinks=4, reserve=0, decode_steps=0)
+
+ALL = (TINY_MHA, LLAMA8B_LAYER, LLAMA8B_MODEL, MISTRAL7B_LAVA, QWEN32B_CK, MISTRAL7B_LAPROX)
 BY_NAME = {c.name: c for c in ALL}
 
 

@@ -18,7 +18,7 @@ adakv_status check_shape(const adakv_shape* s, Geo& g) {
   if (s->hq % s->hkv != 0) return ADAKV_EINVAL;
   if (s->pool < 1 || s->pool % 2 == 0) return ADAKV_EINVAL;
   if (s->dtype != ADAKV_BF16 && s->dtype != ADAKV_F32) return ADAKV_EINVAL;
-  if (s->scorer < ADAKV_SCORE_SNAPKV || s->scorer > ADAKV_SCORE_CRITICALKV) return ADAKV_EINVAL;
+  if (s->scorer < ADAKV_SCORE_SNAPKV || s->scorer > ADAKV_SCORE_LAPROX) return ADAKV_EINVAL;
   // sizes that keep every index in 32 bits per segment and 64 bits overall
   if ((int64_t)s->hkv * (s->n - s->w) > (int64_t)1 << 30) return ADAKV_EUNSUPPORTED;
   if (s->hkv > 256) return ADAKV_EUNSUPPORTED;
@@ -42,10 +42,15 @@ adakv_status check_shape(const adakv_shape* s, Geo& g) {
 
 adakv_status check_alloc(const adakv_alloc* a, const Geo& g) {
   if (a == nullptr) return ADAKV_EINVAL;
-  if (a->mode < ADAKV_ALLOC_ADA || a->mode > ADAKV_ALLOC_ADA_CRITICALKV) return ADAKV_EINVAL;
+  if (a->mode < ADAKV_ALLOC_ADA || a->mode > ADAKV_ALLOC_GLOBAL) return ADAKV_EINVAL;
   if (a->mode == ADAKV_ALLOC_LAVA_LAYERS) {
     const int64_t bp = a->budget - (int64_t)g.I * g.w * g.hkv;
     if (bp < 0 || bp > (int64_t)g.hkv * g.p) return ADAKV_EINVAL;
+  } else if (a->mode == ADAKV_ALLOC_GLOBAL) {
+    const int64_t bp = a->budget - (int64_t)g.I * g.w * g.hkv;
+    if (bp < 0 || bp > (int64_t)g.I * g.hkv * g.p) return ADAKV_EINVAL;
+    // one radix select over every score of the call: 32-bit counts
+    if ((int64_t)g.I * g.hkv * g.p > (int64_t)INT32_MAX) return ADAKV_EUNSUPPORTED;
   } else {
     if (a->alpha_den <= 0 || a->alpha_num < 0 || a->alpha_num > a->alpha_den) return ADAKV_EINVAL;
     if (a->budget < (int64_t)g.w * g.hkv || a->budget > (int64_t)g.n * g.hkv) return ADAKV_EINVAL;
@@ -61,7 +66,7 @@ adakv_status check_alloc(const adakv_alloc* a, const Geo& g) {
 
 // Rows the selection keeps over all instances (window rows excluded).
 int64_t selected_rows(const adakv_alloc& a, const Geo& g) {
-  if (a.mode == ADAKV_ALLOC_LAVA_LAYERS) return a.budget - (int64_t)g.I * g.w * g.hkv;
+  if (a.mode == ADAKV_ALLOC_LAVA_LAYERS || a.mode == ADAKV_ALLOC_GLOBAL) return a.budget - (int64_t)g.I * g.w * g.hkv;
   return (int64_t)g.I * (a.budget - (int64_t)g.w * g.hkv);
 }
 
@@ -114,6 +119,10 @@ adakv_status score_call(const adakv_shape* shape, const void* q_win, const void*
     if (g.hidden < 1 || !(g.eps >= 0.f) || !std::isfinite(g.eps)) return ADAKV_EINVAL;
     if (g.dtype != ADAKV_BF16 || g.d != 128 || g.hidden % 64 != 0) return ADAKV_EUNSUPPORTED;
   }
+  if (g.scorer == ADAKV_SCORE_LAPROX) {
+    if (!aligned16(v) || !aligned16(w_o) || g.hidden < 1 || g.pool != 1) return ADAKV_EINVAL;
+    if (g.dtype != ADAKV_BF16 || g.d != 128 || g.hidden % 64 != 0) return ADAKV_EUNSUPPORTED;
+  }
   if (ws_bytes < score_ws_bytes(g)) return ADAKV_EWORKSPACE;
   return hip_status(launch_score(g, q_win, k, v, w_o, row_lse, score, score2, static_cast<char*>(ws),
                                  static_cast<hipStream_t>(stream)));
@@ -144,6 +153,7 @@ adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, 
   if (selected_rows(*alloc, g) > 0 && !aligned16(sel)) return ADAKV_EINVAL;
   if (alloc->mode == ADAKV_ALLOC_ADA_CRITICALKV && !aligned16(score2)) return ADAKV_EINVAL;
   if (alloc->mode == ADAKV_ALLOC_LAVA_LAYERS && g.I > 4096) return ADAKV_EUNSUPPORTED;
+  if (alloc->mode == ADAKV_ALLOC_GLOBAL && (int64_t)g.I * g.hkv > ((int64_t)1 << 20)) return ADAKV_EUNSUPPORTED;
   if (ws_bytes < alloc_ws_bytes(g, *alloc)) return ADAKV_EWORKSPACE;
   return hip_status(launch_allocate(g, *alloc, score, score2, budgets, sel, sel_off, static_cast<char*>(ws),
                                     static_cast<hipStream_t>(stream)));

@@ -20,6 +20,10 @@
 //    row weights summed, group maximum, times max_k ||V[k]||_1 / w, max pooled.
 //  * CriticalKV notes, "作为通用插件融入现有驱逐流水线": the per-query-head Ada-KV
 //    score is kept for the composite score.
+//  * LaProx page, Section 4.1, Algorithm 1: every window row softmaxed over all
+//    n keys (no mask, as printed); per head and prefix key the sum over the rows
+//    of the squared weights, whose square root is ||A[:, t]||_2 (the value
+//    factor ||(V W_O)[t, :]||_2 and the product come from the V W^O kernel).
 #include <algorithm>
 #include <cmath>
 
@@ -299,7 +303,9 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
 }
 
 // ---------------------------------------------------------------- pass 2
-enum { EMIT_SNAP = 0, EMIT_LAVA = 1 };
+// EMIT_SQ: the SNAP path without pooling on squared weights, written per head
+// unscaled (sum over rows of A^2).
+enum { EMIT_SNAP = 0, EMIT_LAVA = 1, EMIT_SQ = 2 };
 
 template <typename T, int D, int NB, int POOL, int KIND>
 __global__ __launch_bounds__(512) void score_emit_kernel(
@@ -364,6 +370,17 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
     smc[nb] = ok ? m : 0.f;          // padding rows: q = 0, weight 0
     sil[nb] = ok ? 1.0f / l : 0.f;
   }
+  // Squared weights: (exp2(z c2 - m) s)^2 = exp2(z (2 c2) - 2 m) s^2, the
+  // doubling exact, so the exponent argument is still one FMA.
+  float c2e = c2;
+  if (KIND == EMIT_SQ) {
+    c2e = 2.0f * c2;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      smc[nb] *= 2.0f;
+      sil[nb] *= sil[nb];
+    }
+  }
   // LAVa: max_k ||V[k]||_1 of the head from the value-norm kernel's block maxima
   float vscale = 0.f;
   if (KIND == EMIT_LAVA) {
@@ -389,11 +406,36 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 
     if (active) {
       const int kbase = k0 + 32 * gq;   // first key of this lane group
-      if (KIND == EMIT_SNAP) {
-        f32x4 acc[9][NB];
+      if (KIND != EMIT_LAVA && RHO == 0) {
+        // No pooling: each M-block is folded in as soon as its MFMAs finish.
+        float ks[32];
 #pragma unroll
-        for (int mb = 0; mb < 9; ++mb) logits_block<T, D, NB>(lds, mb, c, gq, qop, acc[mb]);
-        const bool interior = k0 >= 3 && k0 + TILE + 3 <= p;   // all pooled keys inside the prefix
+        for (int i = 0; i < 32; ++i) ks[i] = 0.f;
+        const bool interior = k0 + TILE <= p;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          f32x4 acc[NB];
+          logits_block<T, D, NB>(lds, mb, c, gq, qop, acc);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float e = fast_exp2(fmaf(acc[nb][j], c2e, -smc[nb]));
+              if (interior) ks[4 * mb + j] = fmaf(e, sil[nb], ks[4 * mb + j]);
+              else ks[4 * mb + j] += (kbase + 4 * mb + j < p) ? e * sil[nb] : 0.f;
+            }
+        }
+        float s0, s1;
+        reduce_scatter16(ks, c, s0, s1);
+        hs[h * TILE + 32 * gq + 2 * c] = s0;
+        hs[h * TILE + 32 * gq + 2 * c + 1] = s1;
+      } else if (KIND != EMIT_LAVA) {
+        // the halo M-block (mb = 8) only feeds the pooling
+        constexpr int NMB = RHO > 0 ? 9 : 8;
+        f32x4 acc[NMB][NB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) logits_block<T, D, NB>(lds, mb, c, gq, qop, acc[mb]);
+        const bool interior = k0 >= RHO && k0 + TILE + RHO <= p;   // all pooled keys inside the prefix
         float ks[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) ks[i] = 0.f;
@@ -405,12 +447,17 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
           for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[3 + 4 * mb + j] = acc[mb][nb][j];
+          if (RHO > 0) {
 #pragma unroll
-          for (int j = 0; j < 3; ++j) {
-            const float lft = shfl_lane(acc[7][nb][1 + j], (lane - 16) & 63);
-            const float rgt = shfl_lane(acc[0][nb][j], (lane + 16) & 63);
-            x[j] = (gq == 0) ? acc[8][nb][1 + j] : lft;
-            x[35 + j] = (gq == 3) ? acc[8][nb][j] : rgt;
+            for (int j = 0; j < 3; ++j) {
+              const float lft = shfl_lane(acc[7][nb][1 + j], (lane - 16) & 63);
+              const float rgt = shfl_lane(acc[0][nb][j], (lane + 16) & 63);
+              x[j] = (gq == 0) ? acc[NMB - 1][nb][1 + j] : lft;
+              x[35 + j] = (gq == 3) ? acc[NMB - 1][nb][j] : rgt;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) x[j] = x[35 + j] = -INFINITY;   // never read without pooling
           }
           if (!interior) {
 #pragma unroll
@@ -427,7 +474,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 #pragma unroll
             for (int kk = 0; kk < 32; ++kk) {
               const float pooled = fmax3(a3[kk], a3[kk + 2], a3[kk + 4]);
-              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
+              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2e, -mc)), il_row, ks[kk]);
             }
           } else {
 #pragma unroll
@@ -435,7 +482,7 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
               float pooled = x[kk + 3];
               if (RHO >= 1) pooled = fmax3(pooled, x[kk + 2], x[kk + 4]);
               if (RHO >= 2) pooled = fmax3(pooled, x[kk + 1], x[kk + 5]);
-              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
+              ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2e, -mc)), il_row, ks[kk]);
             }
           }
         }
@@ -490,7 +537,12 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
       }
     }
     __syncthreads();
-    if (KIND == EMIT_SNAP) {
+    if (KIND == EMIT_SQ) {
+      for (int idx = threadIdx.x; idx < G * TILE; idx += blockDim.x) {
+        const int hh = idx / TILE, t2 = idx % TILE, key = k0 + t2;
+        if (key < p) head_scores[(((size_t)il * hq) + (size_t)g * G + hh) * p + key] = hs[hh * TILE + t2];
+      }
+    } else if (KIND == EMIT_SNAP) {
       for (int t2 = threadIdx.x; t2 < TILE; t2 += blockDim.x) {
         const int key = k0 + t2;
         if (key < p) {
@@ -606,13 +658,15 @@ ScorePlan plan_score(const Geo& g) {
   if (ib < 1) ib = 1;
   if (ib > (size_t)g.I) ib = g.I;
   P.ib = (int)ib;
-  P.kend = (g.scorer == ADAKV_SCORE_LAVA) ? g.n : g.p;
+  const bool laprox = g.scorer == ADAKV_SCORE_LAPROX;
+  P.kend = (g.scorer == ADAKV_SCORE_LAVA || laprox) ? g.n : g.p;
   P.nchunk = (P.kend + TILE - 1) / TILE;   // the most chunks a launch can use (one tile each)
   const size_t Gw = (size_t)g.G * g.w;
   size_t off = 0;
   P.off_part = off;  off = align_up(off + (size_t)P.ib * g.hkv * P.nchunk * Gw * sizeof(float2), 256);
   P.off_heads = off;
-  if (g.scorer == ADAKV_SCORE_CRITICALKV) off = align_up(off + (size_t)P.ib * g.hq * g.p * sizeof(float), 256);
+  if (g.scorer == ADAKV_SCORE_CRITICALKV || laprox)
+    off = align_up(off + (size_t)P.ib * g.hq * g.p * sizeof(float), 256);
   P.off_vbar = off;
   if (g.scorer == ADAKV_SCORE_LAVA) off = align_up(off + (size_t)g.I * g.hkv * vbar_blocks(g) * sizeof(float), 256);
   P.total = off;
@@ -626,7 +680,8 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   using L = Lay<T, D>;
   const float c2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
   float2* part = reinterpret_cast<float2*>(ws + P.off_part);
-  float* heads = (g.scorer == ADAKV_SCORE_CRITICALKV) ? reinterpret_cast<float*>(ws + P.off_heads) : nullptr;
+  const bool laprox = g.scorer == ADAKV_SCORE_LAPROX;
+  float* heads = (g.scorer == ADAKV_SCORE_CRITICALKV || laprox) ? reinterpret_cast<float*>(ws + P.off_heads) : nullptr;
   float* vpart = reinterpret_cast<float*>(ws + P.off_vbar);
   const int nvblk = vbar_blocks(g);
   const T* qt = static_cast<const T*>(q);
@@ -675,15 +730,21 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
       score_emit_kernel<T, D, NB, POOLV, EMIT_SNAP><<<g2, threads, lds_emit, st>>>(                          \
           qt, kt, part, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
   } while (0)
-    switch (g.pool) {
+    if (laprox) {
+      if constexpr (sizeof(T) == 2 && D == 128)   // the only LaProx geometry the ABI accepts
+        score_emit_kernel<T, D, NB, 1, EMIT_SQ><<<g2, threads, lds_emit, st>>>(
+            qt, kt, part, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);
+      else
+        return hipErrorInvalidValue;
+    } else switch (g.pool) {
       case 1: EMIT(1); break;
       case 3: EMIT(3); break;
       case 5: EMIT(5); break;
       default: EMIT(7); break;
     }
 #undef EMIT
-    if (g.scorer == ADAKV_SCORE_CRITICALKV) {
-      hipError_t e = launch_vwo(g, i0, ni, v, w_o, heads, score2, st);
+    if (g.scorer == ADAKV_SCORE_CRITICALKV || laprox) {
+      hipError_t e = launch_vwo(g, i0, ni, v, w_o, heads, laprox ? score : score2, st);
       if (e != hipSuccess) return e;
     }
   }

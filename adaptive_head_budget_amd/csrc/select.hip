@@ -24,6 +24,9 @@
 //    and "基于不确定性的层预算分配" (entropy-proportional layer budgets).
 //  * CriticalKV notes, "两阶段贪心选择算法" (top-b' by attention, then top-b''
 //    of the rest by the composite score).
+//  * LaProx page, Algorithm 1 (TopK(p, B_total), window tokens at infinity)
+//    with the abstract's model-wide selection: one top-k over every head of
+//    every instance of the call.
 #include <algorithm>
 
 #include "common.hpp"
@@ -250,12 +253,13 @@ __device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* hg, int 
 
 // One digit pass over segments of seg_rows rows: the histogram of the digits
 // of pass ps among the candidates that match the segment's prefix.  Pass 0
-// takes k from kinit[segment], later passes continue from st[segment].  With
-// member flags, flagged scores are not candidates.
+// takes k from kinit[segment] (kconst when kinit is NULL), later passes
+// continue from st[segment].  With member flags, flagged scores are not
+// candidates.
 __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict__ score,
                                                         const uint8_t* __restrict__ member, int p, int cpr,
                                                         int ntile, int vec, int seg_rows, int ps,
-                                                        const int32_t* __restrict__ kinit,
+                                                        const int32_t* __restrict__ kinit, int kconst,
                                                         const RState* __restrict__ st, uint32_t* __restrict__ hist) {
   __shared__ uint32_t h[NBIN];
   const Chunk ch = chunk_of(cpr, ntile, p);
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict_
   RState cur;
   if (ps == 0) {
     cur.prefix = 0u;
-    cur.krem = kinit[s];
+    cur.krem = kinit ? kinit[s] : kconst;
   } else {
     cur = st[s];
   }
@@ -283,13 +287,14 @@ __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict_
 // The digit pick of pass ps for every segment, one workgroup each; pass 0
 // starts from kinit[segment].
 __global__ __launch_bounds__(SB) void radix_pick_kernel(uint32_t* __restrict__ hist, int ps,
-                                                        const int32_t* __restrict__ kinit, RState* __restrict__ st) {
+                                                        const int32_t* __restrict__ kinit, int kconst,
+                                                        RState* __restrict__ st) {
   __shared__ uint32_t sh[SW + 4];
   const int s = blockIdx.x;
   RState cur;
   if (ps == 0) {
     cur.prefix = 0u;
-    cur.krem = kinit[s];
+    cur.krem = kinit ? kinit[s] : kconst;
   } else {
     cur = st[s];
   }
@@ -420,13 +425,14 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
 // ---------------------------------------------------------------- layer counts and budgets
 enum { MODE_ADA = 0, MODE_LAVA = 1, MODE_CK = 2 };
 
-// Per row: entries above the instance's layer threshold T and equal to it.
+// Per row: entries above its segment's threshold T and equal to it (a segment
+// is seg_rows consecutive rows: one instance, or every row of the call).
 __global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict__ score, int p, int cpr, int ntile,
-                                                         int vec, int hkv, const RState* __restrict__ seg,
+                                                         int vec, int seg_rows, const RState* __restrict__ seg,
                                                          uint32_t* __restrict__ cnt) {
   __shared__ uint32_t sh[SW + 4];
   const Chunk ch = chunk_of(cpr, ntile, p);
-  const RState L = seg[ch.r / hkv];
+  const RState L = seg[ch.r / seg_rows];
   if (L.prefix == NONE) return;
   ChunkKeys K;
   load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
@@ -533,6 +539,43 @@ __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int k
   RState init = {0u, (int32_t)k1_sh};
   const RState x = pick_and_clear(rowhist + (size_t)r * NBIN, 0, init, sh);
   if (threadIdx.x == 0) rowst[r] = x;
+}
+
+// Model-wide top-k, one workgroup: from every row's counts above and at the
+// single threshold T, the ties T may still take are shared out in row order
+// (row r = instance * hkv + head, the flat index order); B_r = above + share,
+// rows' offsets in sel by an exclusive scan, sel_off at each instance's first
+// row.  The total is B' <= 2^31 - 1, so 32-bit sums of counts cannot wrap.
+__global__ __launch_bounds__(SB) void global_budget_kernel(int R, int hkv, int n_inst,
+                                                           const RState* __restrict__ seg,
+                                                           const uint32_t* __restrict__ cnt,
+                                                           int32_t* __restrict__ budgets, int64_t* __restrict__ rowbase,
+                                                           RState* __restrict__ rowst, int64_t* __restrict__ sel_off) {
+  __shared__ uint32_t sh[SW + 4];
+  const RState L = seg[0];
+  const uint32_t quota = (L.prefix == NONE) ? 0u : (uint32_t)L.krem;
+  uint32_t eq_carry = 0, f_carry = 0;
+  for (int r0 = 0; r0 < R; r0 += SB) {
+    const int r = r0 + (int)threadIdx.x;
+    const uint32_t gt = r < R ? cnt[2 * (size_t)r] : 0u;
+    const uint32_t eq = r < R ? cnt[2 * (size_t)r + 1] : 0u;
+    uint32_t eq_tot, f_tot;
+    const uint32_t eq_before = eq_carry + block_excl_scan(eq, sh, eq_tot);
+    const uint32_t share = quota > eq_before ? min(quota - eq_before, eq) : 0u;
+    const uint32_t f = gt + share;
+    const uint32_t base = f_carry + block_excl_scan(f, sh, f_tot);
+    if (r < R) {
+      budgets[r] = (int32_t)f;
+      rowbase[r] = (int64_t)base;
+      RState x = {L.prefix, (int32_t)share};
+      if (L.prefix == NONE) x.krem = 0;
+      rowst[r] = x;
+      if (r % hkv == 0) sel_off[r / hkv] = (int64_t)base;
+    }
+    eq_carry += eq_tot;
+    f_carry += f_tot;
+  }
+  if (threadIdx.x == 0) sel_off[n_inst] = (int64_t)f_carry;
 }
 
 // ---------------------------------------------------------------- per-chunk counts and emission
@@ -695,6 +738,8 @@ size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a) { return plan_alloc(g,
 //   per-chunk counts -> emission in index order
 //   [CriticalKV] stage 1 emits member flags; stage 2 runs the head top-k again on the
 //     composite score over non-members and emits the union.
+//   [model-wide] one segment of all rows: (histogram, pick) x 3, counts per row,
+//     budgets and offsets in one workgroup, per-chunk counts, emission.
 hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* score, const float* score2,
                            int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st) {
   const AllocPlan P = plan_alloc(g, a);
@@ -725,6 +770,21 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     const int blocks = (int)std::min<size_t>((n16 + SB - 1) / SB, 4096);
     sel_zero_kernel<<<blocks, SB, 0, st>>>(reinterpret_cast<u32x4*>(ws), n16);
   }
+  if (a.mode == ADAKV_ALLOC_GLOBAL) {
+    // One top-k over all R rows: three digit passes on a single segment, the
+    // rows' counts at its threshold, their budgets and offsets, emission.
+    const int Bp = (int)(a.budget - (int64_t)g.I * g.w * g.hkv);
+    for (int ps = 0; ps < 3; ++ps) {
+      radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, ps, nullptr, Bp, segst, seghist);
+      radix_pick_kernel<<<1, SB, 0, st>>>(seghist, ps, nullptr, Bp, segst);
+    }
+    layer_count_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, R, segst, cnt);
+    global_budget_kernel<<<1, SB, 0, st>>>(R, hkv, g.I, segst, cnt, budgets, rowbase, rowst, sel_off);
+    chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
+    emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets, sel, (int64_t)Bp,
+                                   nullptr);
+    return hipGetLastError();
+  }
   // Layer-wide top-k.
   layer_hist0_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, lava ? 1 : 0, rowhist, part);
   if (lava) {
@@ -734,8 +794,8 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   }
   layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, lava ? klist : nullptr, segst);
   for (int ps = 1; ps < 3; ++ps) {
-    radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, segst, seghist);
-    radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, segst);
+    radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist);
+    radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, 0, segst);
   }
   // Head budgets.
   layer_count_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, hkv, segst, cnt);
@@ -744,8 +804,8 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   // Every head's own top-k (LAVa keeps the layer threshold).
   if (!lava) {
     for (int ps = 1; ps < 3; ++ps) {
-      radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, rowst, rowhist);
-      radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, rowst);
+      radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, 0, rowst, rowhist);
+      radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, 0, rowst);
     }
   }
   chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
@@ -758,8 +818,8 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
                                  member);
   for (int ps = 0; ps < 3; ++ps) {
-    radix_hist_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, 1, ps, rowk2, rowst2, rowhist);
-    radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, rowk2, rowst2);
+    radix_hist_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, 1, ps, rowk2, 0, rowst2, rowhist);
+    radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, rowk2, 0, rowst2);
   }
   chunk_count_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc);
   emit_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc, rowbase, budgets, sel, sel_total,

@@ -1,9 +1,12 @@
-// CriticalKV projected value norms on gfx950.
+// Projected value norms on gfx950 (CriticalKV composite, LaProx score).
 //
 // CriticalKV notes, "损失函数 / 训练策略": the only new runtime quantity is the
 // L1 norm of every row of V W^O; "两阶段贪心选择算法": the composite score of an
 // entry is (A + eps) * ||(V W^O)_t||_1.  Under GQA the composite of a KV head is
 // the mean over its query heads i of (A_i[t] + eps) * ||(V_g W^O_i)[t]||_1.
+// LaProx page, Section 4.1, Algorithm 1: p[t] = ||A[:, t]||_2 * ||H[t, :]||_2
+// with H = V W_O; the group takes the mean over its query heads of
+// sqrt(sum_r A_i[r, t]^2) * ||(V_g W^O_i)[t]||_2 (L2 = true).
 //
 // For one KV head g and 256 keys, a workgroup forms V_g[t, :] W^O_i (K = d = 128,
 // N = hidden) for every query head i of the group on 16x16x32 bf16 MFMA tiles,
@@ -33,6 +36,7 @@ constexpr int MAXG = 8;
 // Workgroup barrier for LDS only: global loads issued before it stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+template <bool L2>
 __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __restrict__ v,
                                                           const uint16_t* __restrict__ w_o,
                                                           const float* __restrict__ head_scores,
@@ -72,7 +76,12 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
   if (total > 1) load_tile(rb, 1);
   for (int idx = threadIdx.x; idx < G * KEYS; idx += 256) {
     const int h = idx / KEYS, t = kwg + idx % KEYS;
-    ahs[h][idx % KEYS] = (t < p) ? head_scores[((size_t)il * hq + g * G + h) * p + t] + eps : 0.f;
+    float a = 0.f;
+    if (t < p) {
+      const float hsv = head_scores[((size_t)il * hq + g * G + h) * p + t];
+      a = L2 ? sqrtf(hsv) : hsv + eps;
+    }
+    ahs[h][idx % KEYS] = a;
   }
   // A operands: 4 M-blocks of 16 keys, held for the whole workgroup.
   bf16x8 aop[4][KSTEPS];
@@ -113,7 +122,7 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rsum[mb][j] += fabsf(acc[mb][j]);
+        for (int j = 0; j < 4; ++j) rsum[mb][j] = L2 ? fmaf(acc[mb][j], acc[mb][j], rsum[mb][j]) : rsum[mb][j] + fabsf(acc[mb][j]);
     }
     if ((T + 1) % ntiles == 0) {
       // head done: rsum[mb][j] is this lane's part of key key0 + 16mb + 4gq + j
@@ -127,6 +136,7 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
           x += shfl_xor(x, 4);
           x += shfl_xor(x, 2);
           x += shfl_xor(x, 1);
+          if (L2) x = sqrtf(x);
           cacc[mb][j] += ahs[h][64 * wv + 16 * mb + 4 * gq + j] * x;
           rsum[mb][j] = 0.f;
         }
@@ -157,8 +167,12 @@ hipError_t launch_vwo(const Geo& g, int inst0, int ni, const void* v, const void
                       float* score2, hipStream_t st) {
   if (g.dtype != ADAKV_BF16 || g.d != D || g.hidden % NT != 0 || g.G > MAXG) return hipErrorInvalidValue;
   dim3 grid((g.p + KEYS - 1) / KEYS, g.hkv, ni);
-  vwo_norm_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(w_o),
-                                        head_scores, score2, inst0, g.hq, g.hkv, g.G, g.n, g.p, g.hidden, g.eps);
+  if (g.scorer == ADAKV_SCORE_LAPROX)
+    vwo_norm_kernel<true><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(w_o),
+                                                head_scores, score2, inst0, g.hq, g.hkv, g.G, g.n, g.p, g.hidden, g.eps);
+  else
+    vwo_norm_kernel<false><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(w_o),
+                                                 head_scores, score2, inst0, g.hq, g.hkv, g.G, g.n, g.p, g.hidden, g.eps);
   return hipGetLastError();
 }
 

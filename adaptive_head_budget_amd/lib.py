@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(PKG, "libadakv.so")
 
 ADAKV_OK, ADAKV_EINVAL, ADAKV_EUNSUPPORTED, ADAKV_ECAPACITY, ADAKV_EWORKSPACE, ADAKV_EHIP = range(6)
 ADAKV_BF16, ADAKV_F32 = 0, 1
-ADAKV_SCORE_SNAPKV, ADAKV_SCORE_LAVA, ADAKV_SCORE_CRITICALKV = 0, 1, 2
-ADAKV_ALLOC_ADA, ADAKV_ALLOC_LAVA_LAYERS, ADAKV_ALLOC_ADA_CRITICALKV = 0, 1, 2
+ADAKV_SCORE_SNAPKV, ADAKV_SCORE_LAVA, ADAKV_SCORE_CRITICALKV, ADAKV_SCORE_LAPROX = 0, 1, 2, 3
+ADAKV_ALLOC_ADA, ADAKV_ALLOC_LAVA_LAYERS, ADAKV_ALLOC_ADA_CRITICALKV, ADAKV_ALLOC_GLOBAL = 0, 1, 2, 3
 
 EXPORTS = ("adakv_workspace_bytes", "adakv_score", "adakv_score_lse", "adakv_allocate", "adakv_compact",
            "adakv_decode_attn", "adakv_strerror", "adakv_version")

@@ -12,7 +12,10 @@ import numpy as np
 from . import lib
 from .configs import Workload
 
-_SCORERS = {"snapkv": lib.ADAKV_SCORE_SNAPKV, "lava": lib.ADAKV_SCORE_LAVA, "criticalkv": lib.ADAKV_SCORE_CRITICALKV}
+_SCORERS = {"snapkv": lib.ADAKV_SCORE_SNAPKV, "lava": lib.ADAKV_SCORE_LAVA, "criticalkv": lib.ADAKV_SCORE_CRITICALKV,
+            "laprox": lib.ADAKV_SCORE_LAPROX}
+_MODES = {"snapkv": lib.ADAKV_ALLOC_ADA, "lava": lib.ADAKV_ALLOC_LAVA_LAYERS,
+          "criticalkv": lib.ADAKV_ALLOC_ADA_CRITICALKV, "laprox": lib.ADAKV_ALLOC_GLOBAL}
 
 
 def make_shape(cfg: Workload, n_inst: Optional[int] = None, n: Optional[int] = None) -> lib.AdakvShape:
@@ -24,14 +27,13 @@ def make_shape(cfg: Workload, n_inst: Optional[int] = None, n: Optional[int] = N
 
 
 def make_alloc(cfg: Workload, budget: Optional[int] = None) -> lib.AdakvAlloc:
-    mode = {"snapkv": lib.ADAKV_ALLOC_ADA, "lava": lib.ADAKV_ALLOC_LAVA_LAYERS,
-            "criticalkv": lib.ADAKV_ALLOC_ADA_CRITICALKV}[cfg.scorer]
+    mode = _MODES[cfg.scorer]
     return lib.AdakvAlloc(mode=mode, alpha_num=cfg.alpha[0], alpha_den=cfg.alpha[1], ck_num=cfg.ck[0],
                           ck_den=cfg.ck[1], reserved0=0, budget=cfg.budget if budget is None else budget)
 
 
 def selected_rows(shape: lib.AdakvShape, alloc: lib.AdakvAlloc) -> int:
-    if alloc.mode == lib.ADAKV_ALLOC_LAVA_LAYERS:
+    if alloc.mode in (lib.ADAKV_ALLOC_LAVA_LAYERS, lib.ADAKV_ALLOC_GLOBAL):
         return alloc.budget - shape.n_inst * shape.w * shape.hkv
     return shape.n_inst * (alloc.budget - shape.w * shape.hkv)
 
@@ -87,7 +89,20 @@ class Eviction:
 
     def run_score(self, q_win, k, v=None, w_o=None, stream=None, row_lse=None):
         """Window scores; with row_lse [I, hq, w] (float32 log-sum-exp of each
-        window row over its domain) the single-pass entry point is used."""
+        window row over its domain) the single-pass entry point is used.  A
+        w_o with a leading instance dimension ([I, hidden, hq*d]: one output
+        projection per layer) is scored one instance per call."""
+        if w_o is not None and w_o.dim() == 3:
+            one = make_shape(self.cfg, 1, self.shape.n)
+            for i in range(self.shape.n_inst):
+                lse = None if row_lse is None else row_lse[i]
+                s2 = None if self.score2 is None else self.score2[i]
+                if lse is None:
+                    lib.adakv_score(one, q_win[i], k[i], v[i], w_o[i], self.score[i], s2, self.ws, stream)
+                else:
+                    lib.adakv_score_lse(one, q_win[i], k[i], v[i], w_o[i], lse, self.score[i], s2, self.ws,
+                                        stream)
+            return
         if row_lse is None:
             lib.adakv_score(self.shape, q_win, k, v, w_o, self.score, self.score2, self.ws, stream)
         else:

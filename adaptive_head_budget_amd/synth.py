@@ -11,7 +11,8 @@ Recipe (every array is a pure function of the workload name and the indices):
   * sink keys (first `sinks` rows of every KV head) point along the mean of the
     group's window queries: K[g, :sinks] = 4 * sqrt(d) * unit(mean_{i in g, r} Q_win[i, r])
   * decode queries q ~ N(0, 1) / tau_i; appended k_new, v_new ~ N(0, 1)
-  * CriticalKV output projection: o_proj weight [hidden, Hq*d] ~ N(0, 1/hidden)
+  * output projection (CriticalKV, LaProx): o_proj weight [hidden, Hq*d] ~
+    N(0, 1/hidden); LaProx instances are layers, each with its own projection
   * tau: a fixed list for the tiny case, else log-uniform in [0.1, 3] per
     (layer, query head); small tau gives a sharp (sparse) head, large tau a
     dispersed one.
@@ -98,7 +99,7 @@ def make_instance(cfg: Workload, inst: int = 0, n_override: int | None = None) -
         if cfg.append:
             out["k_new"] = _store(r.standard_normal((steps, hkv, d), dtype=np.float32), cfg.dtype)
             out["v_new"] = _store(r.standard_normal((steps, hkv, d), dtype=np.float32), cfg.dtype)
-    if cfg.scorer == "criticalkv":
+    if cfg.scorer in ("criticalkv", "laprox"):
         wo = r.standard_normal((cfg.hidden, hq * d), dtype=np.float32) / np.float32(math.sqrt(cfg.hidden))
         out["w_o"] = _store(wo, cfg.dtype)
     return out
@@ -139,4 +140,9 @@ def make_batch_torch(cfg: Workload, device, n_override: int | None = None, chunk
             out["v_new"] = torch.randn((st, I, hkv, d), generator=gen, device=device).to(tdt)
     if cfg.scorer == "criticalkv":
         out["w_o"] = (torch.randn((cfg.hidden, hq * d), generator=gen, device=device) / math.sqrt(cfg.hidden)).to(tdt)
+    elif cfg.scorer == "laprox":      # one projection per layer
+        out["w_o"] = torch.empty((I, cfg.hidden, hq * d), dtype=tdt, device=device)
+        for i in range(I):
+            out["w_o"][i] = (torch.randn((cfg.hidden, hq * d), generator=gen, device=device)
+                             / math.sqrt(cfg.hidden)).to(tdt)
     return out

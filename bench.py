@@ -71,7 +71,7 @@ def evict_bytes(cfg) -> int:
     if cfg.scorer != "snapkv":
         b += kv
     b += 2 * I * hkv * p * 4
-    retained = (cfg.budget if cfg.scorer == "lava" else I * cfg.budget)
+    retained = (cfg.budget if cfg.scorer in ("lava", "laprox") else I * cfg.budget)
     b += retained * 2 * d * el * 2
     return b
 
@@ -80,14 +80,14 @@ def compact_bytes(cfg) -> int:
     """Algorithmic HBM bytes of one compaction: every retained K and V row read
     once and written once."""
     el = 2 if cfg.dtype == "bf16" else 4
-    retained = (cfg.budget if cfg.scorer == "lava" else cfg.instances * cfg.budget)
+    retained = (cfg.budget if cfg.scorer in ("lava", "laprox") else cfg.instances * cfg.budget)
     return retained * 2 * cfg.d * el * 2
 
 
 def score_bytes(cfg) -> int:
-    """Algorithmic HBM bytes of one scoring pass: K read once (V too for LAVa and
-    CriticalKV), the window queries, the scores written (CriticalKV: W^O once and
-    the second score array too)."""
+    """Algorithmic HBM bytes of one scoring pass: K read once (V too for LAVa,
+    CriticalKV and LaProx), the window queries, the scores written (CriticalKV:
+    W^O once and the second score array too; LaProx: every layer's W^O once)."""
     el = 2 if cfg.dtype == "bf16" else 4
     I, hkv, hq, d, n, w, p = cfg.instances, cfg.hkv, cfg.hq, cfg.d, cfg.n, cfg.w, cfg.p
     kv = I * hkv * n * d * el
@@ -96,22 +96,24 @@ def score_bytes(cfg) -> int:
         b += kv
     if cfg.scorer == "criticalkv":
         b += hq * d * cfg.hidden * el + I * hkv * p * 4
+    if cfg.scorer == "laprox":
+        b += I * hq * d * cfg.hidden * el
     return b
 
 
 def device_row_lse(cfg, data):
     """Input preparation for the single-pass scorer (not timed): the natural-log
     log-sum-exp of every window row's logits / sqrt(d) over the row's domain
-    (prefix keys; LAVa: keys 0 .. p + r), the statistic an attention pass over
-    the window rows leaves behind.  Plain torch float32 on the device, one
-    instance at a time."""
+    (prefix keys; LAVa: keys 0 .. p + r; LaProx: all keys), the statistic an
+    attention pass over the window rows leaves behind.  Plain torch float32 on
+    the device, one instance at a time."""
     import math
     import torch
     I, hq, hkv, w, n, d, p = cfg.instances, cfg.hq, cfg.hkv, cfg.w, cfg.n, cfg.d, cfg.p
     G = hq // hkv
     out = torch.empty((I, hq, w), dtype=torch.float32, device=data["q_win"].device)
     causal = cfg.scorer == "lava"
-    keys = n if causal else p
+    keys = n if (causal or cfg.scorer == "laprox") else p
     if causal:
         pos = torch.arange(n, device=out.device)[None, :]
         lim = (p + torch.arange(w, device=out.device))[:, None]
@@ -155,6 +157,17 @@ def cpu_baseline(cfg):
         r = allocation.lava_allocate(s[None], share, cfg.w)
         r = {"sel": r["sel"][0]}
         tokens = cfg.n
+    elif cfg.scorer == "laprox":
+        # one layer with its share of the model-wide budget; the float64 V.W^O
+        # over every key takes minutes: a bounded slice of keys
+        keys = np.arange(min(cfg.p, 2048))
+        sk = scoring.laprox_scores(q, k, v, synth.widen(inst["w_o"], dt).T, keys=keys)
+        s = np.zeros((cfg.hkv, cfg.p))
+        s[:, keys] = sk
+        r = allocation.global_allocate(s[None], cfg.budget // cfg.instances, cfg.w)
+        r = {"sel": r["sel"][0]}
+        tokens = cfg.n
+        note = f"; projected norms over the first {keys.size} keys only, so the rate is an upper bound"
     else:
         # the float64 V.W^O over every key takes minutes: a bounded slice of keys
         keys = min(cfg.p, 2048)
@@ -282,7 +295,7 @@ def main():
         "score_hbm_gbps": score_bytes(cfg) / (sc * 1e-3) / 1e9,
         "compact_hbm_gbps": compact_bytes(cfg) / (co * 1e-3) / 1e9,
     }
-    if cfg.scorer == "criticalkv":
+    if cfg.scorer in ("criticalkv", "laprox"):
         # the projected-norm contraction bounds this workload: its flops over the
         # whole scoring call (window scores included, so a lower bound on the rate)
         vwo_flops = 2.0 * cfg.instances * cfg.hq * cfg.p * cfg.d * cfg.hidden

@@ -31,6 +31,8 @@
  *                  Allocation" (papercache.org notes)
  *   [CKV-notes]    "CriticalKV: Optimizing KV Cache Eviction from an Output
  *                  Perturbation Perspective" (papernotes.org)
+ *   [LaProx]       "重构长上下文 LLM 推理中的 KV 缓存淘汰问题" (a translation of
+ *                  arXiv 2605.07234, the LaProx paper)
  */
 #ifndef ADAKV_H
 #define ADAKV_H
@@ -56,13 +58,15 @@ typedef enum { ADAKV_BF16 = 0, ADAKV_F32 = 1 } adakv_dtype;
 typedef enum {
   ADAKV_SCORE_SNAPKV = 0,      /* Ada-KV / SnapKV window attention            */
   ADAKV_SCORE_LAVA = 1,        /* LAVa score (attention x value-norm maximum) */
-  ADAKV_SCORE_CRITICALKV = 2   /* Ada-KV score + CriticalKV composite         */
+  ADAKV_SCORE_CRITICALKV = 2,  /* Ada-KV score + CriticalKV composite         */
+  ADAKV_SCORE_LAPROX = 3       /* LaProx: ||A[:,t]||_2 x ||(V W_O)[t,:]||_2    */
 } adakv_scorer;
 
 typedef enum {
   ADAKV_ALLOC_ADA = 0,          /* Ada-KV budgets with safeguard, per-head top-k   */
   ADAKV_ALLOC_LAVA_LAYERS = 1,  /* LAVa entropy layer budgets, flattened top-k    */
-  ADAKV_ALLOC_ADA_CRITICALKV = 2/* Ada-KV budgets, CriticalKV two-stage selection */
+  ADAKV_ALLOC_ADA_CRITICALKV = 2,/* Ada-KV budgets, CriticalKV two-stage selection */
+  ADAKV_ALLOC_GLOBAL = 3        /* one top-k over every head of every instance    */
 } adakv_alloc_mode;
 
 /* Geometry of one call.  Enumerations are carried as int32_t fields. */
@@ -76,7 +80,7 @@ typedef struct {
   int32_t pool;    /* max-pool kernel, odd, 1 = off                           */
   int32_t dtype;   /* adakv_dtype of q, k, v, w_o and the flat cache           */
   int32_t scorer;  /* adakv_scorer                                            */
-  int32_t hidden;  /* CriticalKV: model hidden size D (columns of W^O)         */
+  int32_t hidden;  /* CriticalKV, LaProx: model hidden size D (rows of w_o)     */
   float eps;       /* CriticalKV: additive epsilon of the composite            */
   int32_t reserved0;
 } adakv_shape;
@@ -93,7 +97,9 @@ typedef struct {
                          included (w*hkv <= B <= n*hkv).
                          LAVA_LAYERS: total budget over all I instances (the
                          layers of one sequence), windows included; the part
-                         B' = budget - I*w*hkv must satisfy 0 <= B' <= hkv*p.  */
+                         B' = budget - I*w*hkv must satisfy 0 <= B' <= hkv*p.
+                         GLOBAL: total budget over all I instances, windows
+                         included; 0 <= B' = budget - I*w*hkv <= I*hkv*p.   */
 } adakv_alloc;
 
 /* Bytes of workspace every call below needs for this geometry (the maximum
@@ -118,11 +124,19 @@ size_t adakv_workspace_bytes(const adakv_shape* shape, const adakv_alloc* alloc,
  *   CRITICALKV  score = the SNAPKV score (for the budgets); score2 = the
  *               composite of [CKV-notes] "两阶段贪心选择算法", under GQA the mean
  *               over the group's query heads of (A_i[t] + eps) * ||(v W^O_i)[t]||_1.
+ *   LAPROX      [LaProx] Section 4.1, Algorithm 1: A_i = softmax of
+ *               q_win[i] . k[g]^T / sqrt(d) with every window row over all n
+ *               keys (no mask, as printed); score[i,g,t] = the mean over the
+ *               group's query heads of ||A_i[:, t]||_2 * ||(v W^O_i)[t, :]||_2
+ *               (window tokens score infinity there and are always kept, so
+ *               only the prefix is scored).  No pooling: shape.pool must be 1.
+ *               w_o is shared by every instance of the call: instances with
+ *               different projections (layers) are scored in separate calls.
  *
  *   q_win  [I, hq, w, d]   dtype         the window queries
  *   k      [I, hkv, n, d]  dtype
- *   v      [I, hkv, n, d]  dtype         LAVA and CRITICALKV only, else NULL
- *   w_o    [hidden, hq*d]  dtype         CRITICALKV only, else NULL: the output
+ *   v      [I, hkv, n, d]  dtype         LAVA, CRITICALKV and LAPROX, else NULL
+ *   w_o    [hidden, hq*d]  dtype         CRITICALKV and LAPROX, else NULL: the output
  *                                        projection in the nn.Linear layout
  *                                        (row c holds output feature c, so
  *                                        W^O_i of the pages is columns i*d..i*d+d-1
@@ -132,8 +146,8 @@ size_t adakv_workspace_bytes(const adakv_shape* shape, const adakv_alloc* alloc,
  *   ws     >= adakv_workspace_bytes() bytes of device scratch
  *
  * Supported: bf16 with d in {64, 128}; f32 with d in {16, 64}; w <= 64;
- * pool in {1, 3, 5, 7}; G <= 8; CRITICALKV needs bf16, d = 128 and hidden a
- * multiple of 64.  Other valid shapes return ADAKV_EUNSUPPORTED. */
+ * pool in {1, 3, 5, 7}; G <= 8; CRITICALKV and LAPROX need bf16, d = 128 and
+ * hidden a multiple of 64.  Other valid shapes return ADAKV_EUNSUPPORTED. */
 adakv_status adakv_score(const adakv_shape* shape, const void* q_win, const void* k, const void* v,
                          const void* w_o, float* score, float* score2, void* ws, size_t ws_bytes,
                          void* stream);
@@ -150,7 +164,8 @@ adakv_status adakv_score(const adakv_shape* shape, const void* q_win, const void
  *   row_lse [I, hq, w] float32   natural-log log-sum-exp of q_win[j,r].k[g,t]/sqrt(d)
  *                                over row r's domain: the prefix t < p for
  *                                SNAPKV and CRITICALKV (the domain adakv_score
- *                                normalises over), t <= p + r for LAVA.  Finite.
+ *                                normalises over), t <= p + r for LAVA, all
+ *                                n keys for LAPROX.  Finite.
  * Every other argument, the outputs and the supported shapes are those of
  * adakv_score; ws may be the same size. */
 adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const void* k, const void* v,
@@ -179,13 +194,20 @@ adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const 
  *   ADA_CRITICALKV  budgets as ADA on `score`; per head stage 1 keeps the top
  *               floor(B_g*ck_num/ck_den) by `score`, stage 2 the top rest by
  *               `score2` among the others ([CKV-notes] "两阶段贪心选择算法").
+ *   GLOBAL      [LaProx] Algorithm 1, TopK(p, B_total) with the window tokens
+ *               at infinity, and the abstract's model-wide selection: the top
+ *               B' = budget - I*w*hkv of all I*hkv*p scores, ranked by (-score,
+ *               flat index (i*hkv + g)*p + t); B_g is head g's share.  Pass
+ *               the layers of a sequence as the instances (n_inst = 1 gives a
+ *               per-layer top-k).  Needs I*hkv*p < 2^31 and I*hkv <= 2^20.
  *
  *   score   [I, hkv, p] float32         score2 [I, hkv, p] float32 (CK only, else NULL)
  *   budgets [I, hkv]    int32 out       prefix budget B_g of every head
  *   sel     int32 out, sum of all budgets entries: instance i starts at
  *           sel_off[i]; inside it head g's selected token indices (in [0,p))
  *           follow head g-1's, each head ascending.  Its length is
- *           I*(budget - w*hkv) for ADA / CK and budget - I*w*hkv for LAVA.
+ *           I*(budget - w*hkv) for ADA / CK and budget - I*w*hkv for LAVA
+ *           and GLOBAL.
  *   sel_off [I+1] int64 out
  */
 adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, const float* score,

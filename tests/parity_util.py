@@ -62,6 +62,8 @@ def oracle_scores(scorer, q, k, v, w_o, pool, eps, lse=None):
     if scorer == "lava":
         s, _ = scoring.lava_scores(q, k, v, pool, lse=lse)
         return s, None
+    if scorer == "laprox":   # w_o in the nn.Linear layout; the oracle takes its transpose
+        return scoring.laprox_scores(q, k, v, w_o.T, lse), None
     # criticalkv: w_o given in the nn.Linear layout [hidden, hq*d]; the oracle
     # takes the pages' W^O = its transpose.
     s, comp, _, _ = scoring.criticalkv_scores(q, k, v, w_o.T, pool, eps, lse)

@@ -186,3 +186,28 @@ def test_no_undefined_kernel_stubs(L):
     rejected by the host compilation pass)."""
     out = subprocess.run(["nm", "-D", "--undefined-only", lib.LIB_PATH], capture_output=True, text=True).stdout
     assert "device_stub" not in out
+
+
+def test_laprox_score_rejects(L):
+    lp = dict(scorer=lib.ADAKV_SCORE_LAPROX, hidden=4096, pool=1)
+    assert score_status(L, _shape(**{**lp, "pool": 7})) == lib.ADAKV_EINVAL       # no pooling in LaProx
+    assert score_status(L, _shape(**{**lp, "hidden": 0})) == lib.ADAKV_EINVAL
+    assert score_status(L, _shape(**{**lp, "hidden": 100})) == lib.ADAKV_EUNSUPPORTED
+    assert score_status(L, _shape(**{**lp, "d": 64})) == lib.ADAKV_EUNSUPPORTED
+    assert score_status(L, _shape(**lp), ptrs=FAKE + 4) == lib.ADAKV_EINVAL
+    assert score_status(L, _shape(**lp), ws_bytes=16) == lib.ADAKV_EWORKSPACE
+    assert score_status(L, _shape(scorer=4)) == lib.ADAKV_EINVAL
+
+
+def test_global_budget_range(L):
+    s = _shape(n_inst=4, scorer=lib.ADAKV_SCORE_LAPROX, hidden=4096, pool=1)
+    p = s.n - s.w
+    for budget in (4 * 32 * 8 - 1, 4 * 32 * 8 + 4 * 8 * p + 1):
+        a = _alloc(mode=lib.ADAKV_ALLOC_GLOBAL, budget=budget)
+        st = L.adakv_allocate(ctypes.byref(s), ctypes.byref(a), FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+        assert st == lib.ADAKV_EINVAL
+    big = _shape(n_inst=2048, n=200000)        # 2048 * 8 * 199968 scores: past 32-bit counts
+    a = _alloc(mode=lib.ADAKV_ALLOC_GLOBAL, budget=2048 * 32 * 8)
+    st = L.adakv_allocate(ctypes.byref(big), ctypes.byref(a), FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == lib.ADAKV_EUNSUPPORTED
+    assert lib.adakv_workspace_bytes(s, _alloc(mode=lib.ADAKV_ALLOC_GLOBAL, budget=4 * 32 * 8 + 100), 0) > 0

@@ -41,14 +41,21 @@ def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, sin
     q = pipeline.to_device(st["q_win"], dt)
     k = pipeline.to_device(st["k"], dt)
     v = pipeline.to_device(st["v"], dt)
-    w_o = pipeline.to_device(insts[0]["w_o"], dt) if cfg.scorer == "criticalkv" else None
+    if cfg.scorer == "criticalkv":
+        w_o = pipeline.to_device(insts[0]["w_o"], dt)
+    elif cfg.scorer == "laprox":                                  # one projection per layer
+        w_o = pipeline.to_device(np.stack([x["w_o"] for x in insts]), dt)
+    else:
+        w_o = None
+    wo_of = (lambda i: insts[i]["w_o"]) if cfg.scorer == "laprox" else (lambda i: insts[0]["w_o"])
     ev = pipeline.Eviction(cfg, n_inst=I, n=n, budget=budget, reserve=reserve)
     w = cfg.w
     k64 = [_w(x["k"], dt) for x in insts]
     v64 = [_w(x["v"], dt) for x in insts]
     lse32 = None
     if single_pass:
-        lse32 = np.stack([scoring.window_lse(_w(insts[i]["q_win"], dt), k64[i], causal=cfg.scorer == "lava")
+        lse32 = np.stack([scoring.window_lse(_w(insts[i]["q_win"], dt), k64[i], causal=cfg.scorer == "lava",
+                                             full=cfg.scorer == "laprox")
                           for i in range(I)]).astype(np.float32)
     ev.run_score(q, k, v if cfg.scorer != "snapkv" else None, w_o,
                  row_lse=None if lse32 is None else torch.from_numpy(lse32).cuda())
@@ -57,7 +64,7 @@ def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, sin
     score2 = ev.score2.cpu().numpy() if ev.score2 is not None else None
     for i in (range(I) if check_scores_of is None else check_scores_of):
         ref, ref2 = oracle_scores(cfg.scorer, _w(insts[i]["q_win"], dt), k64[i], v64[i],
-                                  _w(insts[0]["w_o"], dt) if w_o is not None else None, cfg.pool, cfg.eps,
+                                  _w(wo_of(i), dt) if w_o is not None else None, cfg.pool, cfg.eps,
                                   None if lse32 is None else lse32[i].astype(np.float64))
         worst = assert_scores_close(score[i], ref, f"{label} score inst {i}")
         if ref2 is not None:
@@ -76,6 +83,14 @@ def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, sin
         else:
             for l in range(I):
                 check_selection(b[l], off[l], sel[l], r["budgets"][l], r["sel"][l], f"{label} layer {l}")
+    elif cfg.scorer == "laprox":
+        r = allocation.global_allocate(score.astype(np.float64), budget, w)
+        base = 0
+        for i in range(I):
+            check_selection(b[i], int(off[i]), sel[i], r["budgets"][i], r["sel"][i], f"{label} inst {i}",
+                            off_ref=base)
+            base += int(r["budgets"][i].sum())
+        assert int(off[I]) == r["Bp"]
     else:
         P = budget - w * cfg.hkv
         for i in range(I):
@@ -149,6 +164,12 @@ def test_criticalkv_reduced(gpu_lib):
     run_case(cfg, 1, n, (40 * cfg.hkv * n) // 100, 0, 0, "criticalkv n2100 D1024")
 
 
+def test_laprox_reduced(gpu_lib):
+    cfg = scaled(configs.MISTRAL7B_LAPROX, layers=3, hidden=1024)
+    n = 2100                                   # 2068 prefix keys: 16 full tiles + a ragged tail
+    run_case(cfg, 3, n, 3 * 32 * 8 + (3 * 8 * (n - 32)) // 10, 0, 0, "laprox L3 n2100 D1024")
+
+
 # ------------------------------------------------------------------ single pass (row statistics supplied)
 def test_single_pass_tiny(gpu_lib):
     cfg = configs.TINY_MHA
@@ -171,6 +192,11 @@ def test_single_pass_criticalkv_reduced(gpu_lib):
     run_case(cfg, 1, n, (40 * cfg.hkv * n) // 100, 0, 0, "criticalkv n2100 D1024 single-pass", single_pass=True)
 
 
+def test_single_pass_laprox_reduced(gpu_lib):
+    cfg = scaled(configs.MISTRAL7B_LAPROX, layers=2, hidden=512)
+    run_case(cfg, 2, 1500, 2 * 32 * 8 + 900, 0, 0, "laprox L2 n1500 D512 single-pass", single_pass=True)
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("hq,hkv,w,pool,d,dtype", [
     (8, 8, 7, 5, 64, "bf16"),      # MHA, w < 16, pool 5, d 64
@@ -189,6 +215,42 @@ def test_budget_extremes(gpu_lib):
     n = 700
     run_case(base, 1, n, base.w * base.hkv, 1, 1, "window only")            # P = 0
     run_case(base, 1, n, base.n * 0 + n * base.hkv, 1, 1, "keep all")       # P = hkv * p
+
+
+def test_global_budget_extremes(gpu_lib):
+    cfg = scaled(configs.MISTRAL7B_LAPROX, layers=2, hidden=256, name="global_extremes")
+    n = 700
+    win = 2 * cfg.w * cfg.hkv
+    run_case(cfg, 2, n, win, 0, 0, "model-wide: windows only")                          # B' = 0
+    run_case(cfg, 2, n, win + 2 * cfg.hkv * (n - cfg.w), 0, 0, "model-wide: keep all")  # B' = I*hkv*p
+
+
+def test_global_ties_across_instances(gpu_lib):
+    """Two identical layers with constant keys and values: every score of a
+    head is the same, and the two layers tie entry for entry, so the
+    model-wide selection is decided by the flat-index tie-break alone (ties
+    shared out across heads and instances)."""
+    cfg = scaled(configs.MISTRAL7B_LAPROX, layers=2, hidden=256, name="global_ties", sinks=0)
+    n = 600
+    inst = synth.make_instance(cfg, 0, n_override=n)
+    kc = np.broadcast_to(inst["k"][:, :1, :], inst["k"].shape).copy()
+    vc = np.broadcast_to(inst["v"][:, :1, :], inst["v"].shape).copy()
+    q = pipeline.to_device(np.stack([inst["q_win"]] * 2), "bf16")
+    k = pipeline.to_device(np.stack([kc] * 2), "bf16")
+    v = pipeline.to_device(np.stack([vc] * 2), "bf16")
+    w_o = pipeline.to_device(np.stack([inst["w_o"]] * 2), "bf16")
+    budget = 2 * cfg.w * cfg.hkv + 3 * (n - cfg.w) + 123
+    ev = pipeline.Eviction(cfg, n_inst=2, n=n, budget=budget, reserve=0)
+    ev.evict(q, k, v, w_o)
+    torch.cuda.synchronize()
+    s = ev.score.cpu().numpy()
+    assert np.all(s == s[:, :, :1]) and np.array_equal(s[0], s[1])
+    b, off, sel = ev.host_selection()
+    r = allocation.global_allocate(s.astype(np.float64), budget, cfg.w)
+    base = 0
+    for i in range(2):
+        check_selection(b[i], int(off[i]), sel[i], r["budgets"][i], r["sel"][i], f"ties inst {i}", off_ref=base)
+        base += int(r["budgets"][i].sum())
 
 
 @pytest.mark.parametrize("alpha", [(0, 1), (1, 1), (1, 2), (4, 5)])   # (4, 5): the other reading of alpha = 0.2
@@ -366,3 +428,46 @@ def test_criticalkv_full_sampled(gpu_lib):
     check_flat(kf, vf, ev.seg_start.cpu().numpy(), ev.seg_len.cpu().numpy(), 0, hkv, k64, v64, sel[0], cfg.w,
                "criticalkv full")
     log(f"  scores worst rel {worst:.2e}, composite worst rel {worst2:.2e}; selection and flat segments exact")
+
+
+def test_laprox_full_sampled(gpu_lib):
+    """The 32-layer Mistral-7B LaProx workload at n = 32768, hidden 4096,
+    exactly as the benchmark launches it (one scoring call per layer, one
+    model-wide selection): the model-wide selection bit-exact against the
+    oracle's run on the GPU's own fp32 scores; two layers' scores at 512
+    sampled keys (the full V W^O in float64 would take minutes) and their flat
+    segments against the oracle."""
+    cfg = configs.MISTRAL7B_LAPROX
+    log("drawing full Mistral-7B LaProx inputs on the device")
+    data = synth.make_batch_torch(cfg, "cuda")
+    ev = pipeline.Eviction(cfg)
+    ev.evict(data["q_win"], data["k"], data["v"], data["w_o"])
+    torch.cuda.synchronize()
+    score = ev.score.cpu().numpy()
+    b, off, sel = ev.host_selection()
+    L, w, p = cfg.instances, cfg.w, cfg.p
+    r = allocation.global_allocate(score.astype(np.float64), cfg.budget, w)
+    assert int(off[L]) == r["Bp"]
+    base = 0
+    for l in range(L):
+        check_selection(b[l], int(off[l]), sel[l], r["budgets"][l], r["sel"][l], f"laprox full layer {l}",
+                        off_ref=base)
+        base += int(r["budgets"][l].sum())
+    log(f"  model-wide selection exact; layer budgets {r['layer_budgets'].min()}..{r['layer_budgets'].max()}")
+    kf = pipeline.to_host_f64(ev.k_flat)
+    vf = pipeline.to_host_f64(ev.v_flat)
+    ss = ev.seg_start.cpu().numpy()
+    sl = ev.seg_len.cpu().numpy()
+    rng = np.random.default_rng(11)
+    keys = np.unique(np.concatenate([[0, 1, p - 2, p - 1], rng.choice(p, 508, replace=False)]))
+    for l in (0, 19):
+        q64 = pipeline.to_host_f64(data["q_win"][l])
+        k64 = pipeline.to_host_f64(data["k"][l])
+        v64 = pipeline.to_host_f64(data["v"][l])
+        wo64 = pipeline.to_host_f64(data["w_o"][l])
+        ref = scoring.laprox_scores(q64, k64, v64, wo64.T, keys=keys)
+        worst = assert_scores_close(score[l][:, keys], ref, f"laprox full layer {l} (sampled keys)")
+        check_flat(kf, vf, ss, sl, l, cfg.hkv, k64, v64, sel[l], w, f"laprox full layer {l}")
+        log(f"  layer {l}: scores worst rel {worst:.2e} at {keys.size} keys; flat segments exact")
+    del data, ev
+    torch.cuda.empty_cache()
