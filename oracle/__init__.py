@@ -11,7 +11,8 @@ Modules
   scoring     observation-window scores: Ada-KV/SnapKV, LAVa, CriticalKV, LaProx
   allocation  Ada-KV budget allocation with the safeguard, per-head top-k,
               LAVa entropy layer budgets, CriticalKV two-stage selection,
-              the model-wide top-k of LaProx
+              the model-wide top-k of LaProx, the floor-then-global reading
+              of the safeguard, the StreamingLLM baseline
   cache       compaction into the retained cache and decode attention
   bounds      the pages' loss bounds and the renormalisation identity
 

@@ -187,3 +187,61 @@ def global_allocate(scores: np.ndarray, total: int, w: int) -> Dict:
     budgets = np.bincount(row, minlength=L * hkv).astype(np.int64).reshape(L, hkv)
     sel = [[np.sort(top[row == l * hkv + g] % p) for g in range(hkv)] for l in range(L)]
     return {"Bp": Bp, "budgets": budgets, "layer_budgets": budgets.sum(axis=1), "sel": sel}
+
+
+def ada_floor_allocate(score: np.ndarray, budget: int, w: int, alpha: Tuple[int, int] = (1, 5)) -> Dict:
+    """The floor-then-global reading of the Ada-KV safeguard.
+
+    Ada-KV notes, Algorithm 2 step 8 and the introduction: the safeguard keeps
+    highly sparse heads from receiving too small a budget.  Read as a floor:
+    every head first keeps its own top f0 = floor(alpha * P / h) entries, then
+    one top (P - h * f0) over all heads' remaining entries (Algorithm 1 on what
+    is left) decides the rest; B_g = f0 + head g's share.  Ranking everywhere
+    by (-score, flat index g*p + k).  Of all budget splits with B_g >= f0 and
+    sum P, this one keeps the largest total score.
+    """
+    score = np.asarray(score, dtype=np.float64)
+    hkv, p = score.shape
+    P = int(budget) - w * hkv
+    if P < 0 or P > hkv * p:
+        raise ValueError("budget outside [w*Hkv, n*Hkv]")
+    a, b = int(alpha[0]), int(alpha[1])
+    if not (0 <= a <= b and b > 0):
+        raise ValueError("alpha must be a/b with 0 <= a <= b, b > 0")
+    f0 = (a * P) // (b * hkv)
+    first = [top_indices(score[g], f0) for g in range(hkv)]
+    taken = np.zeros((hkv, p), dtype=bool)
+    for g in range(hkv):
+        taken[g, first[g]] = True
+    flat = score.ravel()
+    rest = np.flatnonzero(~taken.ravel())                      # ascending flat indices
+    second = rest[top_indices(flat[rest], P - hkv * f0)]
+    counts = np.bincount(second // p, minlength=hkv).astype(np.int64)
+    budgets = f0 + counts
+    sel = [np.sort(np.concatenate([first[g], second[second // p == g] % p])) for g in range(hkv)]
+    return {"P": P, "floor": f0, "counts": counts, "budgets": budgets, "sel": sel}
+
+
+def streaming_allocate(hkv: int, p: int, budget: int, w: int, sinks: int = 4) -> Dict:
+    """StreamingLLM baseline on the same cache layout.
+
+    Ada-KV notes, "缓存驱逐方法的分类与局限" item 1 and the Ada-KV paper,
+    "Baselines" / "Parameters": keep a few initial tokens (4 sinks) and the most
+    recent window.  Under a budget B the window tokens are kept as for every
+    other method, the prefix share P = B - w*Hkv is split evenly over the heads
+    (floors, one more for the lowest P mod Hkv heads), and head g keeps its
+    first min(sinks, B_g) prefix tokens and its most recent remaining ones.
+    """
+    P = int(budget) - w * hkv
+    if P < 0 or P > hkv * p:
+        raise ValueError("budget outside [w*Hkv, n*Hkv]")
+    if sinks < 0:
+        raise ValueError("sinks must be >= 0")
+    budgets = np.full(hkv, P // hkv, dtype=np.int64)
+    budgets[:P % hkv] += 1
+    sel = []
+    for g in range(hkv):
+        bg = int(budgets[g])
+        s = min(sinks, bg)
+        sel.append(np.concatenate([np.arange(s), np.arange(p - (bg - s), p)]).astype(np.int64))
+    return {"P": P, "budgets": budgets, "sel": sel}

@@ -338,3 +338,90 @@ def _global_per_layer(scores, total, w):
 
 def test_global_pins_catch_planted_mistakes():
     assert not check_global_brute_force(_global_per_layer)
+
+
+# ---------------------------------------------------------------- floor-then-global safeguard
+def check_floor_is_best_split_with_floor(fn) -> bool:
+    """Brute force over every budget split B_g >= f0 with sum P: the floor
+    reading keeps the largest total score, and its own split reaches it."""
+    r = np.random.default_rng(61)
+    hkv, p, w = 3, 7, 1
+    ok = True
+    for trial in range(6):
+        s = r.random((hkv, p)) ** (1 + 3 * trial)
+        for P in (0, 2, 5, 9, 14, hkv * p):
+            out = fn(s, P + w * hkv, w, (1, 2))
+            f0 = (P // 2) // hkv
+            srt = -np.sort(-s, axis=1)
+            best = max(sum(srt[g, :c[g]].sum() for g in range(hkv))
+                       for c in itertools.product(range(f0, p + 1), repeat=hkv) if sum(c) == P)
+            got = sum(s[g, out["sel"][g]].sum() for g in range(hkv))
+            ok &= bool(np.isclose(got, best, rtol=1e-12)) and all(out["budgets"] >= f0)
+            ok &= int(out["budgets"].sum()) == P
+    return ok
+
+
+def test_floor_reading_maximises_retained_score_under_the_floor():
+    assert check_floor_is_best_split_with_floor(allocation.ada_floor_allocate)
+
+
+def test_floor_reading_limits():
+    r = np.random.default_rng(62)
+    hkv, p, w = 4, 30, 2
+    s = r.random((hkv, p)) ** 3
+    for B in (w * hkv, w * hkv + 37, w * hkv + hkv * p):
+        z = allocation.ada_floor_allocate(s, B, w, (0, 1))      # no floor: Algorithm 1's counts
+        a = allocation.ada_allocate(s, B, w, (1, 1))
+        assert list(z["budgets"]) == list(a["budgets"]) and all(
+            list(x) == list(y) for x, y in zip(z["sel"], a["sel"]))
+    full = allocation.ada_floor_allocate(s, w * hkv + 41, w, (1, 1))   # floor P // h = 10
+    assert full["floor"] == 10 and sorted(full["budgets"])[0] >= 10 and full["budgets"].sum() == 41
+    # every head keeps its own top-f0 entries
+    for g in range(hkv):
+        assert set(allocation.top_indices(s[g], 10)) <= set(full["sel"][g])
+
+
+def test_floor_tie_order_brute_force():
+    """Integer scores with many ties: the result is the per-head first f0 of
+    (-score, k), then the first P - h*f0 of (-score, g, k) over the rest."""
+    r = np.random.default_rng(63)
+    hkv, p, w = 3, 8, 1
+    s = r.integers(0, 3, (hkv, p)).astype(np.float64)
+    for P in (0, 4, 11, 17, hkv * p):
+        out = allocation.ada_floor_allocate(s, P + w * hkv, w, (3, 4))
+        f0 = (3 * P) // (4 * hkv)
+        first = {(g, t) for g in range(hkv) for (_, t) in sorted((-s[g, t], t) for t in range(p))[:f0]}
+        rest = sorted((-s[g, t], g, t) for g in range(hkv) for t in range(p) if (g, t) not in first)
+        keep = first | {(g, t) for (_, g, t) in rest[:P - hkv * f0]}
+        for g in range(hkv):
+            assert list(out["sel"][g]) == sorted(t for (gg, t) in keep if gg == g)
+
+
+# ---------------------------------------------------------------- StreamingLLM
+def test_streaming_closed_form():
+    out = allocation.streaming_allocate(3, 20, 3 * 2 + 14, 2, sinks=4)
+    assert list(out["budgets"]) == [5, 5, 4]
+    assert list(out["sel"][0]) == [0, 1, 2, 3, 19] and list(out["sel"][2]) == [0, 1, 2, 3]
+    small = allocation.streaming_allocate(2, 10, 2 * 3 + 5, 3, sinks=4)     # B_g = 3, 2 < sinks
+    assert list(small["sel"][0]) == [0, 1, 2] and list(small["sel"][1]) == [0, 1]
+    none = allocation.streaming_allocate(2, 10, 2 * 3, 3)
+    assert all(x.size == 0 for x in none["sel"])
+    full = allocation.streaming_allocate(2, 10, 2 * 13, 3)
+    assert all(list(x) == list(range(10)) for x in full["sel"])
+    nos = allocation.streaming_allocate(2, 10, 2 * 3 + 8, 3, sinks=0)       # pure recency
+    assert list(nos["sel"][1]) == [6, 7, 8, 9]
+
+
+def _floor_overlapping_stages(score, budget, w, alpha):
+    """Planted: the global stage ranks every entry, the heads' floor entries
+    included, so the two stages can pick the same entry twice."""
+    hkv, p = score.shape
+    P = budget - w * hkv
+    f0 = (alpha[0] * P) // (alpha[1] * hkv)
+    second = allocation.top_indices(score.ravel(), P - hkv * f0)
+    sel = [np.union1d(allocation.top_indices(score[g], f0), second[second // p == g] % p) for g in range(hkv)]
+    return {"budgets": np.array([x.size for x in sel]), "sel": sel}
+
+
+def test_floor_pins_catch_planted_mistakes():
+    assert not check_floor_is_best_split_with_floor(_floor_overlapping_stages)
