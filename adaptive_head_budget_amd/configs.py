@@ -48,6 +48,10 @@ class Workload:
     reserve: int = 0                  # empty rows kept per head for appends
     decode_steps: int = 0             # decode queries run after eviction
     append: bool = True               # decode steps append one token per head
+    alloc: str = ""                   # allocation mode; "" = the scorer's own
+                                      # ("ada", "lava", "criticalkv", "global",
+                                      # "floor", "streaming")
+    stream_sinks: int = 4             # StreamingLLM: sink tokens kept per head
 
     @property
     def instances(self) -> int:

@@ -42,7 +42,7 @@ adakv_status check_shape(const adakv_shape* s, Geo& g) {
 
 adakv_status check_alloc(const adakv_alloc* a, const Geo& g) {
   if (a == nullptr) return ADAKV_EINVAL;
-  if (a->mode < ADAKV_ALLOC_ADA || a->mode > ADAKV_ALLOC_GLOBAL) return ADAKV_EINVAL;
+  if (a->mode < ADAKV_ALLOC_ADA || a->mode > ADAKV_ALLOC_STREAMING) return ADAKV_EINVAL;
   if (a->mode == ADAKV_ALLOC_LAVA_LAYERS) {
     const int64_t bp = a->budget - (int64_t)g.I * g.w * g.hkv;
     if (bp < 0 || bp > (int64_t)g.hkv * g.p) return ADAKV_EINVAL;
@@ -57,6 +57,7 @@ adakv_status check_alloc(const adakv_alloc* a, const Geo& g) {
     // the safeguard numerator a*h*f + (b-a)*P stays far inside int64
     if ((int64_t)a->alpha_den > ((int64_t)1 << 20)) return ADAKV_EUNSUPPORTED;
   }
+  if (a->mode == ADAKV_ALLOC_STREAMING && a->sinks < 0) return ADAKV_EINVAL;
   if (a->mode == ADAKV_ALLOC_ADA_CRITICALKV) {
     if (a->ck_den <= 0 || a->ck_num < 0 || a->ck_num > a->ck_den) return ADAKV_EINVAL;
     if ((int64_t)a->ck_den > ((int64_t)1 << 20)) return ADAKV_EUNSUPPORTED;
@@ -149,7 +150,8 @@ adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, 
   if (st != ADAKV_OK) return st;
   st = check_alloc(alloc, g);
   if (st != ADAKV_OK) return st;
-  if (!aligned16(score) || !aligned16(budgets) || !aligned16(sel_off) || !aligned16(ws)) return ADAKV_EINVAL;
+  if (!aligned16(budgets) || !aligned16(sel_off) || !aligned16(ws)) return ADAKV_EINVAL;
+  if (alloc->mode != ADAKV_ALLOC_STREAMING && !aligned16(score)) return ADAKV_EINVAL;
   if (selected_rows(*alloc, g) > 0 && !aligned16(sel)) return ADAKV_EINVAL;
   if (alloc->mode == ADAKV_ALLOC_ADA_CRITICALKV && !aligned16(score2)) return ADAKV_EINVAL;
   if (alloc->mode == ADAKV_ALLOC_LAVA_LAYERS && g.I > 4096) return ADAKV_EUNSUPPORTED;

@@ -27,6 +27,11 @@
 //  * LaProx page, Algorithm 1 (TopK(p, B_total), window tokens at infinity)
 //    with the abstract's model-wide selection: one top-k over every head of
 //    every instance of the call.
+//  * The safeguard read as a floor (Ada-KV notes, Algorithm 2 step 8: no head
+//    may get too small a budget): each head's own top floor(alpha*P/h) first,
+//    then Algorithm 1 over the remaining entries of all heads.
+//  * StreamingLLM (Ada-KV paper, "Baselines" / "Parameters"): sink tokens and
+//    the most recent ones, the prefix share split evenly over the heads.
 #include <algorithm>
 
 #include "common.hpp"
@@ -426,21 +431,26 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
 enum { MODE_ADA = 0, MODE_LAVA = 1, MODE_CK = 2 };
 
 // Per row: entries above its segment's threshold T and equal to it (a segment
-// is seg_rows consecutive rows: one instance, or every row of the call).
-__global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict__ score, int p, int cpr, int ntile,
-                                                         int vec, int seg_rows, const RState* __restrict__ seg,
-                                                         uint32_t* __restrict__ cnt) {
+// is seg_rows consecutive rows: one instance, or every row of the call).  With
+// member flags, flagged entries are not counted.
+__global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict__ score,
+                                                         const uint8_t* __restrict__ member, int p, int cpr,
+                                                         int ntile, int vec, int seg_rows,
+                                                         const RState* __restrict__ seg, uint32_t* __restrict__ cnt) {
   __shared__ uint32_t sh[SW + 4];
   const Chunk ch = chunk_of(cpr, ntile, p);
   const RState L = seg[ch.r / seg_rows];
   if (L.prefix == NONE) return;
   ChunkKeys K;
+  uint8_t m[NK];
   load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  if (member) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
-    gt += (j < K.n && K.k[j] > L.prefix) ? 1u : 0u;
-    eq += (j < K.n && K.k[j] == L.prefix) ? 1u : 0u;
+    const bool ok = j < K.n && (member == nullptr || m[j] == 0);
+    gt += (ok && K.k[j] > L.prefix) ? 1u : 0u;
+    eq += (ok && K.k[j] == L.prefix) ? 1u : 0u;
   }
   const uint32_t both = block_sum(gt | (eq << 16), sh);   // at most 4096 of each
   if (threadIdx.x == 0) {
@@ -541,41 +551,70 @@ __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int k
   if (threadIdx.x == 0) rowst[r] = x;
 }
 
-// Model-wide top-k, one workgroup: from every row's counts above and at the
-// single threshold T, the ties T may still take are shared out in row order
-// (row r = instance * hkv + head, the flat index order); B_r = above + share,
-// rows' offsets in sel by an exclusive scan, sel_off at each instance's first
-// row.  The total is B' <= 2^31 - 1, so 32-bit sums of counts cannot wrap.
-__global__ __launch_bounds__(SB) void global_budget_kernel(int R, int hkv, int n_inst,
-                                                           const RState* __restrict__ seg,
-                                                           const uint32_t* __restrict__ cnt,
-                                                           int32_t* __restrict__ budgets, int64_t* __restrict__ rowbase,
-                                                           RState* __restrict__ rowst, int64_t* __restrict__ sel_off) {
+// Budgets from one threshold per segment of seg_rows rows, one workgroup per
+// segment (the model-wide top-k: one segment of every row; the floor reading:
+// one segment per instance, its rows' floors added).  The ties the segment's
+// threshold T may still take are shared out in row order (the flat index
+// order); B_r = add + above + share; the rows' offsets in sel start at
+// segment * seg_stride (the floor reading: P per instance) or run on from
+// zero (one segment), sel_off gets each instance's first row.  A segment's
+// total is below 2^31, so 32-bit sums of counts cannot wrap.
+__global__ __launch_bounds__(SB) void segment_budget_kernel(int seg_rows, int hkv, int n_inst, int add,
+                                                            int64_t seg_stride, const RState* __restrict__ seg,
+                                                            const uint32_t* __restrict__ cnt,
+                                                            int32_t* __restrict__ budgets,
+                                                            int64_t* __restrict__ rowbase, RState* __restrict__ rowst,
+                                                            int64_t* __restrict__ sel_off) {
   __shared__ uint32_t sh[SW + 4];
-  const RState L = seg[0];
+  const RState L = seg[blockIdx.x];
   const uint32_t quota = (L.prefix == NONE) ? 0u : (uint32_t)L.krem;
+  const int64_t base0 = (int64_t)blockIdx.x * seg_stride;
+  const int rbeg = blockIdx.x * seg_rows;
   uint32_t eq_carry = 0, f_carry = 0;
-  for (int r0 = 0; r0 < R; r0 += SB) {
-    const int r = r0 + (int)threadIdx.x;
-    const uint32_t gt = r < R ? cnt[2 * (size_t)r] : 0u;
-    const uint32_t eq = r < R ? cnt[2 * (size_t)r + 1] : 0u;
+  for (int r0 = 0; r0 < seg_rows; r0 += SB) {
+    const int rl = r0 + (int)threadIdx.x;
+    const int r = rbeg + rl;
+    const bool in = rl < seg_rows;
+    const uint32_t gt = in ? cnt[2 * (size_t)r] : 0u;
+    const uint32_t eq = in ? cnt[2 * (size_t)r + 1] : 0u;
     uint32_t eq_tot, f_tot;
     const uint32_t eq_before = eq_carry + block_excl_scan(eq, sh, eq_tot);
     const uint32_t share = quota > eq_before ? min(quota - eq_before, eq) : 0u;
-    const uint32_t f = gt + share;
-    const uint32_t base = f_carry + block_excl_scan(f, sh, f_tot);
-    if (r < R) {
+    const uint32_t f = (in ? (uint32_t)add : 0u) + gt + share;
+    const uint32_t before = f_carry + block_excl_scan(f, sh, f_tot);
+    if (in) {
       budgets[r] = (int32_t)f;
-      rowbase[r] = (int64_t)base;
+      rowbase[r] = base0 + (int64_t)before;
       RState x = {L.prefix, (int32_t)share};
       if (L.prefix == NONE) x.krem = 0;
       rowst[r] = x;
-      if (r % hkv == 0) sel_off[r / hkv] = (int64_t)base;
+      if (r % hkv == 0) sel_off[r / hkv] = base0 + (int64_t)before;
     }
     eq_carry += eq_tot;
     f_carry += f_tot;
   }
-  if (threadIdx.x == 0) sel_off[n_inst] = (int64_t)f_carry;
+  if (threadIdx.x == 0 && blockIdx.x == gridDim.x - 1) sel_off[n_inst] = base0 + (int64_t)f_carry;
+}
+
+// StreamingLLM: B_g = P / h, one more for the lowest P mod h heads; head g
+// keeps its first min(sinks, B_g) prefix tokens and its last B_g - that many.
+// Grid (rows, chunks of SB selections); every row's budget and sel_off
+// entries come from its chunk-0 workgroup.
+__global__ __launch_bounds__(SB) void streaming_kernel(int hkv, int n_inst, int p, int kP, int sinks,
+                                                       int32_t* __restrict__ budgets, int32_t* __restrict__ sel,
+                                                       int64_t* __restrict__ sel_off) {
+  const int r = blockIdx.x, inst = r / hkv, g = r % hkv;
+  const int q = kP / hkv, rem = kP % hkv;
+  const int bg = q + (g < rem ? 1 : 0);
+  const int64_t base = (int64_t)inst * kP + (int64_t)g * q + min(g, rem);
+  const int s = min(sinks, bg);
+  const int j = blockIdx.y * SB + (int)threadIdx.x;
+  if (j < bg) sel[base + j] = (j < s) ? j : p - bg + j;
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
+    budgets[r] = bg;
+    if (g == 0) sel_off[inst] = (int64_t)inst * kP;
+    if (r == hkv * n_inst - 1) sel_off[n_inst] = (int64_t)n_inst * kP;
+  }
 }
 
 // ---------------------------------------------------------------- per-chunk counts and emission
@@ -717,7 +756,8 @@ AllocPlan plan_alloc(const Geo& g, const adakv_alloc& a) {
   P.off_rowbase = off;  off = align_up(off + (size_t)P.R * 8, 256);
   P.off_cc = off;       off = align_up(off + (size_t)P.nchunk * 8, 256);
   P.off_member = off;
-  if (a.mode == ADAKV_ALLOC_ADA_CRITICALKV) off = align_up(off + (size_t)P.R * g.p, 256);
+  if (a.mode == ADAKV_ALLOC_ADA_CRITICALKV || a.mode == ADAKV_ALLOC_ADA_FLOOR)
+    off = align_up(off + (size_t)P.R * g.p, 256);
   P.off_part = off;
   if (a.mode == ADAKV_ALLOC_LAVA_LAYERS) off = align_up(off + (size_t)P.nchunk * 16, 256);
   P.off_klist = off;    off = align_up(off + (size_t)g.I * 8, 256);
@@ -740,6 +780,9 @@ size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a) { return plan_alloc(g,
 //     composite score over non-members and emits the union.
 //   [model-wide] one segment of all rows: (histogram, pick) x 3, counts per row,
 //     budgets and offsets in one workgroup, per-chunk counts, emission.
+//   [floor reading] per-row top-f0 -> member flags; per-instance top over the
+//     rest; counts, budgets f0 + share, emission of both stages together.
+//   [StreamingLLM] one kernel writes budgets, offsets and indices; no scores.
 hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* score, const float* score2,
                            int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st) {
   const AllocPlan P = plan_alloc(g, a);
@@ -770,6 +813,39 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     const int blocks = (int)std::min<size_t>((n16 + SB - 1) / SB, 4096);
     sel_zero_kernel<<<blocks, SB, 0, st>>>(reinterpret_cast<u32x4*>(ws), n16);
   }
+  if (a.mode == ADAKV_ALLOC_STREAMING) {
+    const int kP = (int)(a.budget - (int64_t)g.w * g.hkv);
+    const int maxb = kP / hkv + 1;
+    dim3 grid(R, (maxb + SB - 1) / SB);
+    streaming_kernel<<<grid, SB, 0, st>>>(hkv, g.I, g.p, kP, a.sinks, budgets, sel, sel_off);
+    return hipGetLastError();
+  }
+  if (a.mode == ADAKV_ALLOC_ADA_FLOOR) {
+    // Stage 1: every head's own top-f0 as member flags.  Stage 2: per instance
+    // one top-(P - h*f0) over the non-members, their counts, budgets f0 + share,
+    // then emission of members and stage-2 entries together.
+    const int kP = (int)(a.budget - (int64_t)g.w * g.hkv);
+    const int f0 = (int)(((int64_t)a.alpha_num * kP) / ((int64_t)a.alpha_den * hkv));
+    for (int ps = 0; ps < 3; ++ps) {
+      radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, f0, rowst, rowhist);
+      radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, f0, rowst);
+    }
+    chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
+    emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
+                                   member);
+    const int k2 = kP - hkv * f0;
+    for (int ps = 0; ps < 3; ++ps) {
+      radix_hist_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, hkv, ps, nullptr, k2, segst, seghist);
+      radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, k2, segst);
+    }
+    layer_count_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, hkv, segst, cnt);
+    segment_budget_kernel<<<g.I, SB, 0, st>>>(hkv, hkv, g.I, f0, (int64_t)kP, segst, cnt, budgets, rowbase, rowst2,
+                                              sel_off);
+    chunk_count_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, rowst2, cc);
+    emit_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, rowst2, cc, rowbase, budgets, sel,
+                                   (int64_t)g.I * kP, nullptr);
+    return hipGetLastError();
+  }
   if (a.mode == ADAKV_ALLOC_GLOBAL) {
     // One top-k over all R rows: three digit passes on a single segment, the
     // rows' counts at its threshold, their budgets and offsets, emission.
@@ -778,8 +854,8 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
       radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, ps, nullptr, Bp, segst, seghist);
       radix_pick_kernel<<<1, SB, 0, st>>>(seghist, ps, nullptr, Bp, segst);
     }
-    layer_count_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, R, segst, cnt);
-    global_budget_kernel<<<1, SB, 0, st>>>(R, hkv, g.I, segst, cnt, budgets, rowbase, rowst, sel_off);
+    layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, segst, cnt);
+    segment_budget_kernel<<<1, SB, 0, st>>>(R, hkv, g.I, 0, 0, segst, cnt, budgets, rowbase, rowst, sel_off);
     chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
     emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets, sel, (int64_t)Bp,
                                    nullptr);
@@ -798,7 +874,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, 0, segst);
   }
   // Head budgets.
-  layer_count_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, hkv, segst, cnt);
+  layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, hkv, segst, cnt);
   row_budget_kernel<<<R, SB, 0, st>>>(hkv, mode, kP, a.alpha_num, a.alpha_den, a.ck_num, a.ck_den, g.I, segst, cnt,
                                       rowhist, budgets, rowbase, rowk2, rowst, sel_off);
   // Every head's own top-k (LAVa keeps the layer threshold).

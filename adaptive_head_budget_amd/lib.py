@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(PKG, "libadakv.so")
 ADAKV_OK, ADAKV_EINVAL, ADAKV_EUNSUPPORTED, ADAKV_ECAPACITY, ADAKV_EWORKSPACE, ADAKV_EHIP = range(6)
 ADAKV_BF16, ADAKV_F32 = 0, 1
 ADAKV_SCORE_SNAPKV, ADAKV_SCORE_LAVA, ADAKV_SCORE_CRITICALKV, ADAKV_SCORE_LAPROX = 0, 1, 2, 3
-ADAKV_ALLOC_ADA, ADAKV_ALLOC_LAVA_LAYERS, ADAKV_ALLOC_ADA_CRITICALKV, ADAKV_ALLOC_GLOBAL = 0, 1, 2, 3
+(ADAKV_ALLOC_ADA, ADAKV_ALLOC_LAVA_LAYERS, ADAKV_ALLOC_ADA_CRITICALKV, ADAKV_ALLOC_GLOBAL, ADAKV_ALLOC_ADA_FLOOR,
+ ADAKV_ALLOC_STREAMING) = range(6)
 
 EXPORTS = ("adakv_workspace_bytes", "adakv_score", "adakv_score_lse", "adakv_allocate", "adakv_compact",
            "adakv_decode_attn", "adakv_strerror", "adakv_version")
@@ -33,7 +34,7 @@ class AdakvShape(ctypes.Structure):
 
 class AdakvAlloc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("alpha_num", ctypes.c_int32), ("alpha_den", ctypes.c_int32),
-                ("ck_num", ctypes.c_int32), ("ck_den", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("ck_num", ctypes.c_int32), ("ck_den", ctypes.c_int32), ("sinks", ctypes.c_int32),
                 ("budget", ctypes.c_int64)]
 
 

@@ -16,6 +16,9 @@ _SCORERS = {"snapkv": lib.ADAKV_SCORE_SNAPKV, "lava": lib.ADAKV_SCORE_LAVA, "cri
             "laprox": lib.ADAKV_SCORE_LAPROX}
 _MODES = {"snapkv": lib.ADAKV_ALLOC_ADA, "lava": lib.ADAKV_ALLOC_LAVA_LAYERS,
           "criticalkv": lib.ADAKV_ALLOC_ADA_CRITICALKV, "laprox": lib.ADAKV_ALLOC_GLOBAL}
+_ALLOC_NAMES = {"ada": lib.ADAKV_ALLOC_ADA, "lava": lib.ADAKV_ALLOC_LAVA_LAYERS,
+                "criticalkv": lib.ADAKV_ALLOC_ADA_CRITICALKV, "global": lib.ADAKV_ALLOC_GLOBAL,
+                "floor": lib.ADAKV_ALLOC_ADA_FLOOR, "streaming": lib.ADAKV_ALLOC_STREAMING}
 
 
 def make_shape(cfg: Workload, n_inst: Optional[int] = None, n: Optional[int] = None) -> lib.AdakvShape:
@@ -27,9 +30,9 @@ def make_shape(cfg: Workload, n_inst: Optional[int] = None, n: Optional[int] = N
 
 
 def make_alloc(cfg: Workload, budget: Optional[int] = None) -> lib.AdakvAlloc:
-    mode = _MODES[cfg.scorer]
+    mode = _ALLOC_NAMES[cfg.alloc] if cfg.alloc else _MODES[cfg.scorer]
     return lib.AdakvAlloc(mode=mode, alpha_num=cfg.alpha[0], alpha_den=cfg.alpha[1], ck_num=cfg.ck[0],
-                          ck_den=cfg.ck[1], reserved0=0, budget=cfg.budget if budget is None else budget)
+                          ck_den=cfg.ck[1], sinks=cfg.stream_sinks, budget=cfg.budget if budget is None else budget)
 
 
 def selected_rows(shape: lib.AdakvShape, alloc: lib.AdakvAlloc) -> int:

@@ -66,7 +66,9 @@ typedef enum {
   ADAKV_ALLOC_ADA = 0,          /* Ada-KV budgets with safeguard, per-head top-k   */
   ADAKV_ALLOC_LAVA_LAYERS = 1,  /* LAVa entropy layer budgets, flattened top-k    */
   ADAKV_ALLOC_ADA_CRITICALKV = 2,/* Ada-KV budgets, CriticalKV two-stage selection */
-  ADAKV_ALLOC_GLOBAL = 3        /* one top-k over every head of every instance    */
+  ADAKV_ALLOC_GLOBAL = 3,       /* one top-k over every head of every instance    */
+  ADAKV_ALLOC_ADA_FLOOR = 4,    /* safeguard read as a per-head floor, then top-k */
+  ADAKV_ALLOC_STREAMING = 5     /* StreamingLLM: sinks + most recent, no scores    */
 } adakv_alloc_mode;
 
 /* Geometry of one call.  Enumerations are carried as int32_t fields. */
@@ -92,9 +94,9 @@ typedef struct {
   int32_t alpha_den;
   int32_t ck_num;     /* CriticalKV stage-1 share = ck_num / ck_den (0..1)        */
   int32_t ck_den;
-  int32_t reserved0;
-  int64_t budget;     /* ADA / CRITICALKV: budget B of every instance, window
-                         included (w*hkv <= B <= n*hkv).
+  int32_t sinks;      /* STREAMING: leading prefix tokens every head keeps (>= 0) */
+  int64_t budget;     /* ADA / CRITICALKV / ADA_FLOOR / STREAMING: budget B of
+                         every instance, window included (w*hkv <= B <= n*hkv).
                          LAVA_LAYERS: total budget over all I instances (the
                          layers of one sequence), windows included; the part
                          B' = budget - I*w*hkv must satisfy 0 <= B' <= hkv*p.
@@ -194,6 +196,17 @@ adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const 
  *   ADA_CRITICALKV  budgets as ADA on `score`; per head stage 1 keeps the top
  *               floor(B_g*ck_num/ck_den) by `score`, stage 2 the top rest by
  *               `score2` among the others ([CKV-notes] "两阶段贪心选择算法").
+ *   ADA_FLOOR   the safeguard read as a floor ([AdaKV-notes] Algorithm 2 step 8
+ *               keeps sparse heads from too small a budget): every head first
+ *               keeps its own top f0 = floor(alpha_num*P / (alpha_den*hkv)),
+ *               then the top P - hkv*f0 of all heads' remaining entries
+ *               (Algorithm 1 on the rest); B_g = f0 + head g's share.  Of all
+ *               splits with B_g >= f0 it keeps the largest total score.
+ *   STREAMING   StreamingLLM ([AdaKV-paper] "Baselines" / "Parameters": 4 sink
+ *               tokens and the most recent window): B_g = P/hkv (one more for
+ *               the lowest P mod hkv heads); head g keeps prefix tokens
+ *               0 .. min(sinks, B_g)-1 and its most recent remaining ones.
+ *               score may be NULL.
  *   GLOBAL      [LaProx] Algorithm 1, TopK(p, B_total) with the window tokens
  *               at infinity, and the abstract's model-wide selection: the top
  *               B' = budget - I*w*hkv of all I*hkv*p scores, ranked by (-score,

@@ -211,3 +211,19 @@ def test_global_budget_range(L):
     st = L.adakv_allocate(ctypes.byref(big), ctypes.byref(a), FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == lib.ADAKV_EUNSUPPORTED
     assert lib.adakv_workspace_bytes(s, _alloc(mode=lib.ADAKV_ALLOC_GLOBAL, budget=4 * 32 * 8 + 100), 0) > 0
+
+
+def test_floor_and_streaming_rejects(L):
+    s = _shape()
+    for kw in (dict(mode=lib.ADAKV_ALLOC_STREAMING, sinks=-1), dict(mode=6),
+               dict(mode=lib.ADAKV_ALLOC_ADA_FLOOR, alpha_num=2, alpha_den=1),
+               dict(mode=lib.ADAKV_ALLOC_ADA_FLOOR, budget=8 * 32 - 1)):
+        a = _alloc(**kw)
+        st = L.adakv_allocate(ctypes.byref(s), ctypes.byref(a), FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+        assert st == lib.ADAKV_EINVAL, kw
+    # StreamingLLM needs no scores, every other mode does
+    a = _alloc(mode=lib.ADAKV_ALLOC_ADA_FLOOR)
+    st = L.adakv_allocate(ctypes.byref(s), ctypes.byref(a), None, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == lib.ADAKV_EINVAL
+    assert lib.adakv_workspace_bytes(s, _alloc(mode=lib.ADAKV_ALLOC_ADA_FLOOR), 0) > \
+        lib.adakv_workspace_bytes(s, _alloc(mode=lib.ADAKV_ALLOC_ADA), 0) - 1

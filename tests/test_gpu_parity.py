@@ -94,7 +94,11 @@ def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, sin
     else:
         P = budget - w * cfg.hkv
         for i in range(I):
-            if cfg.scorer == "criticalkv":
+            if cfg.alloc == "floor":
+                r = allocation.ada_floor_allocate(score[i].astype(np.float64), budget, w, cfg.alpha)
+            elif cfg.alloc == "streaming":
+                r = allocation.streaming_allocate(cfg.hkv, n - w, budget, w, cfg.stream_sinks)
+            elif cfg.scorer == "criticalkv":
                 r = allocation.criticalkv_allocate(score[i].astype(np.float64), score2[i].astype(np.float64),
                                                    budget, w, cfg.alpha, cfg.ck)
             else:
@@ -257,6 +261,40 @@ def test_global_ties_across_instances(gpu_lib):
 def test_safeguard_settings(gpu_lib, alpha):
     cfg = scaled(configs.LLAMA8B_LAYER, alpha=alpha, name=f"alpha{alpha[0]}_{alpha[1]}", decode_steps=0)
     run_case(cfg, 2, 1500, 8 * 100, 0, 0, f"alpha {alpha}")
+
+
+@pytest.mark.parametrize("alpha", [(1, 5), (0, 1), (1, 1), (4, 5)])
+def test_floor_reading(gpu_lib, alpha):
+    cfg = scaled(configs.LLAMA8B_LAYER, alpha=alpha, alloc="floor", name=f"floor{alpha[0]}_{alpha[1]}",
+                 decode_steps=1, reserve=1)
+    run_case(cfg, 3, 1900, 8 * 32 + 8 * 150 + 5, 1, 1, f"floor alpha {alpha}")
+
+
+def test_floor_reading_ties(gpu_lib):
+    """Constant keys: every score of a head is equal, so both stages are
+    decided by the index tie-break alone."""
+    cfg = scaled(configs.LLAMA8B_LAYER, name="floor_ties", sinks=0, decode_steps=0, alloc="floor", alpha=(1, 2))
+    n = 600
+    inst = synth.make_instance(cfg, 0, n_override=n)
+    kconst = np.broadcast_to(inst["k"][:, :1, :], inst["k"].shape).copy()
+    q = pipeline.to_device(inst["q_win"][None], "bf16")
+    k = pipeline.to_device(kconst[None], "bf16")
+    v = pipeline.to_device(inst["v"][None], "bf16")
+    budget = 8 * 32 + 901
+    ev = pipeline.Eviction(cfg, n_inst=1, n=n, budget=budget, reserve=0)
+    ev.evict(q, k, v)
+    torch.cuda.synchronize()
+    s = ev.score.cpu().numpy()[0]
+    b, off, sel = ev.host_selection()
+    r = allocation.ada_floor_allocate(s.astype(np.float64), budget, cfg.w, cfg.alpha)
+    check_selection(b[0], int(off[0]), sel[0], r["budgets"], r["sel"], "floor ties")
+
+
+@pytest.mark.parametrize("sinks", [4, 0, 700])
+def test_streaming_baseline(gpu_lib, sinks):
+    cfg = scaled(configs.LLAMA8B_MODEL, layers=2, batch=2, alloc="streaming", stream_sinks=sinks,
+                 name=f"streaming{sinks}")
+    run_case(cfg, 4, 3000, 8 * 32 + 8 * 200 + 3, 2, 2, f"streaming sinks {sinks}")
 
 
 def test_ties_take_lower_index(gpu_lib):
