@@ -12,7 +12,8 @@ Modules
   allocation  Ada-KV budget allocation with the safeguard, per-head top-k,
               LAVa entropy layer budgets, CriticalKV two-stage selection,
               the model-wide top-k of LaProx, the floor-then-global reading
-              of the safeguard, the StreamingLLM baseline
+              of the safeguard, the StreamingLLM baseline, the LAVa
+              online-prefill budget schedule
   cache       compaction into the retained cache and decode attention
   bounds      the pages' loss bounds and the renormalisation identity
 

@@ -245,3 +245,46 @@ def streaming_allocate(hkv: int, p: int, budget: int, w: int, sinks: int = 4) ->
         s = min(sinks, bg)
         sel.append(np.concatenate([np.arange(s), np.arange(p - (bg - s), p)]).astype(np.int64))
     return {"P": P, "budgets": budgets, "sel": sel}
+
+
+def lava_online_steps(scores: np.ndarray, total: int, w: int) -> List[Dict]:
+    """LAVa online prefill: layer budgets after each layer's prefill.
+
+    LAVa notes, "在线预填充与层预算调整": prefill and eviction run layer by
+    layer; after layer l is prefilled the lower layers are compressed again
+    with the same LAVa scores, their budgets shrinking as the memory is shared
+    with more layers.  The pages leave the schedule open; the reading here:
+    after layer l the l + 1 layers present share B'(l) = total - (l+1)*w*Hkv
+    prefix entries by the entropy rule of "基于不确定性的层预算分配" (the same
+    e_j, from each layer's full scores, and the same largest-remainder split as
+    lava_layer_budgets), and no layer may grow: B_j(l) = min(split_j, B_j(l-1)),
+    with Hkv*p for a layer's first step.  Each layer keeps the top B_j(l) of its
+    flattened scores (no safeguard, "动态头预算的逐层缓存驱逐"); with the same
+    ranking every step's selection lies inside the previous one.  The sum of
+    the budgets may fall below B'(l) where a cap binds.
+    scores: [L, Hkv, p].  Returns one dict per step l with layer_budgets [l+1],
+    budgets [l+1, Hkv] and sel[j][g].
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    L, hkv, p = scores.shape
+    if int(total) < L * w * hkv:
+        raise ValueError("total budget smaller than the windows")
+    e = np.array([layer_entropy(scores[j]) for j in range(L)])
+    prev = np.zeros(0, dtype=np.int64)
+    steps = []
+    for l in range(L):
+        Bp = int(total) - (l + 1) * w * hkv
+        E = e[:l + 1].sum()
+        x = Bp * e[:l + 1] / E if E > 0 else np.full(l + 1, Bp / (l + 1))
+        split = largest_remainder(x, Bp)
+        cap = np.concatenate([prev, [hkv * p]])
+        lb = np.minimum(split, cap)
+        budgets = np.zeros((l + 1, hkv), dtype=np.int64)
+        sel = []
+        for j in range(l + 1):
+            top = top_indices(scores[j].ravel(), int(lb[j]))
+            budgets[j] = np.bincount(top // p, minlength=hkv)
+            sel.append([np.sort(top[top // p == g] % p) for g in range(hkv)])
+        steps.append({"layer_budgets": lb, "split": split, "budgets": budgets, "sel": sel, "Bp": Bp})
+        prev = lb
+    return steps

@@ -425,3 +425,53 @@ def _floor_overlapping_stages(score, budget, w, alpha):
 
 def test_floor_pins_catch_planted_mistakes():
     assert not check_floor_is_best_split_with_floor(_floor_overlapping_stages)
+
+
+# ---------------------------------------------------------------- LAVa online prefill
+def test_lava_online_nested_and_bounded():
+    r = np.random.default_rng(71)
+    L, hkv, p, w = 5, 3, 40, 2
+    s = r.random((L, hkv, p)) ** (1 + 4 * r.random((L, 1, 1)))
+    total = L * w * hkv + 150
+    steps = allocation.lava_online_steps(s, total, w)
+    for l, st in enumerate(steps):
+        assert len(st["layer_budgets"]) == l + 1
+        # memory: the layers present never hold more than the total
+        assert st["layer_budgets"].sum() + (l + 1) * w * hkv <= total
+        for j in range(l + 1):
+            assert st["budgets"][j].sum() == st["layer_budgets"][j]
+            if l > 0 and j < l:
+                # budgets only shrink and every selection lies inside the previous one
+                assert st["layer_budgets"][j] <= steps[l - 1]["layer_budgets"][j]
+                for g in range(hkv):
+                    assert set(st["sel"][j][g]) <= set(steps[l - 1]["sel"][j][g])
+
+
+def test_lava_online_last_step_is_offline_lava_when_no_cap_binds():
+    """Smooth score distributions: the shares fall at every step, no cap binds,
+    and the last step is the offline LAVa allocation of all layers."""
+    r = np.random.default_rng(72)
+    L, hkv, p, w = 4, 2, 60, 3
+    s = r.random((L, hkv, p)) + 0.5
+    total = L * w * hkv + 90
+    steps = allocation.lava_online_steps(s, total, w)
+    assert all(np.array_equal(st["layer_budgets"], st["split"]) for st in steps)
+    off = allocation.lava_allocate(s, total, w)
+    last = steps[-1]
+    assert np.array_equal(last["layer_budgets"], off["layer_budgets"])
+    for j in range(L):
+        assert all(list(a) == list(b) for a, b in zip(last["sel"][j], off["sel"][j]))
+
+
+def test_lava_online_first_step_keeps_at_most_the_layer():
+    r = np.random.default_rng(73)
+    L, hkv, p, w = 3, 2, 10, 1
+    s = r.random((L, hkv, p))
+    steps = allocation.lava_online_steps(s, L * w * hkv + 45, w)
+    assert steps[0]["layer_budgets"][0] == hkv * p            # capped: the whole prefix of layer 0
+    assert steps[1]["layer_budgets"].sum() <= (L * w * hkv + 45) - 2 * w * hkv   # B'(1)
+    # closed form of the split: uniform scores have equal entropy, so the shares are equal
+    u = np.ones((L, hkv, p))
+    st = allocation.lava_online_steps(u, L * w * hkv + 12, w)
+    assert list(st[-1]["layer_budgets"]) == [4, 4, 4]
+    assert list(st[1]["layer_budgets"]) == [7, 7]             # (12 + 3*2 - 2*2) / 2 = 7 each
