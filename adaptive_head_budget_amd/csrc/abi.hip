@@ -161,6 +161,50 @@ adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, 
                                     static_cast<hipStream_t>(stream)));
 }
 
+adakv_status adakv_lava_online_allocate(const adakv_shape* shape, int64_t total_budget, const float* score,
+                                        const int64_t* prev_sel_off, int32_t* budgets, int32_t* sel,
+                                        int64_t* sel_off, void* ws, size_t ws_bytes, void* stream) {
+  Geo g{};
+  adakv_status st = check_shape(shape, g);
+  if (st != ADAKV_OK) return st;
+  const int64_t bp = total_budget - (int64_t)g.I * g.w * g.hkv;
+  if (bp < 0) return ADAKV_EINVAL;
+  if (!aligned16(score) || !aligned16(budgets) || !aligned16(sel_off) || !aligned16(ws)) return ADAKV_EINVAL;
+  if (bp > 0 && !aligned16(sel)) return ADAKV_EINVAL;
+  if (g.I > 1 && !aligned16(prev_sel_off)) return ADAKV_EINVAL;
+  if (g.I > 4096) return ADAKV_EUNSUPPORTED;
+  if (bp > (int64_t)INT32_MAX) return ADAKV_EUNSUPPORTED;
+  adakv_alloc a{};
+  a.mode = ADAKV_ALLOC_LAVA_LAYERS;
+  a.alpha_den = 1;
+  a.ck_den = 1;
+  a.budget = total_budget;
+  if (ws_bytes < alloc_ws_bytes(g, a)) return ADAKV_EWORKSPACE;
+  return hip_status(launch_allocate(g, a, score, nullptr, budgets, sel, sel_off, static_cast<char*>(ws),
+                                   static_cast<hipStream_t>(stream), true, g.I > 1 ? prev_sel_off : nullptr));
+}
+
+adakv_status adakv_lava_online_compact(const adakv_shape* shape, const void* k_new, const void* v_new,
+                                       const void* k_old, const void* v_old, const int64_t* seg_start_old,
+                                       const int32_t* sel_old, const int64_t* sel_off_old, const int32_t* budgets,
+                                       const int32_t* sel, const int64_t* sel_off, int64_t max_rows, void* k_flat,
+                                       void* v_flat, int64_t* seg_start, int32_t* seg_len, void* stream) {
+  Geo g{};
+  adakv_status st = check_shape(shape, g);
+  if (st != ADAKV_OK) return st;
+  if (max_rows < 0) return ADAKV_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(budgets) || !aligned16(sel_off) ||
+      !aligned16(seg_start) || !aligned16(seg_len))
+    return ADAKV_EINVAL;
+  if (max_rows > 0 && (!aligned16(k_flat) || !aligned16(v_flat) || !aligned16(sel))) return ADAKV_EINVAL;
+  if (g.I > 1 && (!aligned16(k_old) || !aligned16(v_old) || !aligned16(seg_start_old) || !aligned16(sel_old) ||
+                  !aligned16(sel_off_old)))
+    return ADAKV_EINVAL;
+  return hip_status(launch_online_compact(g, max_rows, k_new, v_new, k_old, v_old, seg_start_old, sel_old,
+                                          sel_off_old, budgets, sel, sel_off, k_flat, v_flat, seg_start, seg_len,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, const void* k, const void* v,
                            const int32_t* budgets, const int32_t* sel, const int64_t* sel_off, int32_t reserve,
                            void* k_flat, void* v_flat, int64_t* seg_start, int32_t* seg_len, void* stream) {

@@ -140,7 +140,139 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(const char* __restric
   }
 }
 
+// LAVa online prefill: the flat cache of layers 0..I-1 after layer I-1's
+// prefill.  Rows of the newest layer (instance I-1) come from its dense K/V;
+// rows of the lower layers from the previous flat cache of layers 0..I-2
+// (no reserve rows), where every kept token still is: a prefix token is
+// found by binary search in the head's previous ascending selection, a window
+// token at its fixed place after it.  Rows past the device total or the
+// buffer, and tokens missing from the previous cache, are skipped.
+template <int ROWB>
+__global__ __launch_bounds__(256) void online_copy_kernel(
+    const char* __restrict__ k_new, const char* __restrict__ v_new, const char* __restrict__ k_old,
+    const char* __restrict__ v_old, const int64_t* __restrict__ seg_start_old, const int32_t* __restrict__ sel_old,
+    const int64_t* __restrict__ sel_off_old, const int32_t* __restrict__ budgets, const int32_t* __restrict__ sel,
+    const int64_t* __restrict__ sel_off, const int64_t* __restrict__ seg_start, int S, int hkv, int n, int w, int p,
+    int64_t flat_rows, char* __restrict__ kf, char* __restrict__ vf) {
+  __shared__ const char* src_k[RPW];
+  __shared__ const char* src_v[RPW];
+  __shared__ int64_t dst_row[RPW];
+  __shared__ int s_first;
+  const int64_t r0 = (int64_t)blockIdx.x * RPW;
+  const int64_t total = seg_start[S];
+  if (r0 >= total) return;                     // uniform across the workgroup
+  if (threadIdx.x < WAVE) {
+    const int lane = threadIdx.x;
+    int lo = 0, len = S;
+    while (len > 1) {
+      const int step = (len + WAVE - 1) / WAVE;
+      const bool ok = lane * step < len && seg_start[lo + lane * step] <= r0;
+      const uint64_t m = __ballot(ok);
+      const int j = 63 - __builtin_clzll(m);
+      lo += j * step;
+      len = min(step, len - j * step);
+    }
+    if (lane == 0) s_first = lo;
+  }
+  __syncthreads();
+  if (threadIdx.x < RPW) {
+    const int64_t r = r0 + threadIdx.x;
+    const char* sk = nullptr;
+    const char* sv = nullptr;
+    int64_t dst = -1;
+    if (r < total && r < flat_rows) {
+      int s = s_first;
+      while (s + 1 < S && seg_start[s + 1] <= r) ++s;
+      const int inst = s / hkv, g = s % hkv, s0 = inst * hkv;
+      const int64_t j = r - seg_start[s];
+      const int B = budgets[s];
+      int64_t tok;
+      if (j < B) tok = sel[sel_off[inst] + (seg_start[s] - seg_start[s0] - (int64_t)g * w) + j];
+      else tok = (int64_t)p + (j - B);
+      if (inst == S / hkv - 1) {
+        if (tok >= 0 && tok < n) {
+          const int64_t row = (int64_t)g * n + tok;
+          sk = k_new + row * ROWB;
+          sv = v_new + row * ROWB;
+        }
+      } else {
+        const int64_t ob = seg_start_old[s];
+        const int64_t bold = seg_start_old[s + 1] - ob - w;
+        int64_t pos = -1;
+        if (tok >= p) {
+          pos = bold + (tok - p);
+        } else {
+          const int32_t* hs = sel_old + sel_off_old[inst] + (ob - seg_start_old[s0] - (int64_t)g * w);
+          int64_t lo = 0, hi = bold;             // first index with hs[index] >= tok
+          while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (hs[mid] < tok) lo = mid + 1;
+            else hi = mid;
+          }
+          if (lo < bold && hs[lo] == tok) pos = lo;
+        }
+        if (pos >= 0 && pos < bold + w) {
+          sk = k_old + (ob + pos) * ROWB;
+          sv = v_old + (ob + pos) * ROWB;
+        }
+      }
+      if (sk != nullptr) dst = r;
+    }
+    src_k[threadIdx.x] = sk;
+    src_v[threadIdx.x] = sv;
+    dst_row[threadIdx.x] = dst;
+  }
+  __syncthreads();
+  constexpr int LPR = ROWB / 16;
+  constexpr int RPP = 256 / LPR;
+  constexpr int NP = RPW / RPP;
+  const int rr0 = threadIdx.x / LPR, ch = threadIdx.x % LPR;
+  u32x4 a[NP], b[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int64_t dst = dst_row[rr0 + i * RPP];
+    if (dst >= 0) {
+      a[i] = ld16_nt(src_k[rr0 + i * RPP] + ch * 16);
+      b[i] = ld16_nt(src_v[rr0 + i * RPP] + ch * 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int64_t dst = dst_row[rr0 + i * RPP];
+    if (dst >= 0) {
+      st16_nt(kf + dst * ROWB + ch * 16, a[i]);
+      st16_nt(vf + dst * ROWB + ch * 16, b[i]);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_online_compact(const Geo& g, int64_t max_rows, const void* k_new, const void* v_new,
+                                 const void* k_old, const void* v_old, const int64_t* seg_start_old,
+                                 const int32_t* sel_old, const int64_t* sel_off_old, const int32_t* budgets,
+                                 const int32_t* sel, const int64_t* sel_off, void* k_flat, void* v_flat,
+                                 int64_t* seg_start, int32_t* seg_len, hipStream_t st) {
+  const int S = g.I * g.hkv;
+  compact_layout_kernel<<<1, LT, 0, st>>>(budgets, S, g.w, 0, seg_start, seg_len);
+  const int rowb = g.d * (g.dtype == ADAKV_BF16 ? 2 : 4);
+  const int64_t blocks = (max_rows + RPW - 1) / RPW;
+  if (blocks == 0) return hipGetLastError();
+#define OCOPY(RB)                                                                                               \
+  online_copy_kernel<RB><<<(unsigned)blocks, 256, 0, st>>>(                                                       \
+      static_cast<const char*>(k_new), static_cast<const char*>(v_new), static_cast<const char*>(k_old),          \
+      static_cast<const char*>(v_old), seg_start_old, sel_old, sel_off_old, budgets, sel, sel_off, seg_start, S,  \
+      g.hkv, g.n, g.w, g.p, max_rows, static_cast<char*>(k_flat), static_cast<char*>(v_flat))
+  switch (rowb) {
+    case 64: OCOPY(64); break;
+    case 128: OCOPY(128); break;
+    case 256: OCOPY(256); break;
+    case 512: OCOPY(512); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef OCOPY
+  return hipGetLastError();
+}
 
 hipError_t launch_compact(const Geo& g, int64_t retained_rows, const void* k, const void* v,
                           const int32_t* budgets, const int32_t* sel, const int64_t* sel_off, int reserve,

@@ -26,13 +26,24 @@ hipError_t launch_vwo(const Geo& g, int inst0, int ni, const void* v, const void
 
 // ---- allocation (select.hip)
 size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a);
+// prev_off: LAVa online prefill only (a LAVA_LAYERS call whose layer budgets are
+// capped by the previous step's; NULL at the first step), else unused.
 hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* score, const float* score2,
-                           int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st);
+                           int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st,
+                           bool online = false, const int64_t* prev_off = nullptr);
 
 // ---- compaction (compact.hip)
 hipError_t launch_compact(const Geo& g, int64_t retained_rows, const void* k, const void* v,
                           const int32_t* budgets, const int32_t* sel, const int64_t* sel_off, int reserve,
                           void* k_flat, void* v_flat, int64_t* seg_start, int32_t* seg_len, hipStream_t st);
+
+// LAVa online prefill: flat cache of layers 0..I-1 from the newest layer's
+// dense K/V and the previous flat cache of layers 0..I-2 (no reserve rows).
+hipError_t launch_online_compact(const Geo& g, int64_t max_rows, const void* k_new, const void* v_new,
+                                 const void* k_old, const void* v_old, const int64_t* seg_start_old,
+                                 const int32_t* sel_old, const int64_t* sel_off_old, const int32_t* budgets,
+                                 const int32_t* sel, const int64_t* sel_off, void* k_flat, void* v_flat,
+                                 int64_t* seg_start, int32_t* seg_len, hipStream_t st);
 
 // ---- decode (decode.hip)
 size_t decode_ws_bytes(const Geo& g, int64_t max_rows);

@@ -379,9 +379,14 @@ __global__ __launch_bounds__(SB) void layer_pick0_kernel(const uint32_t* __restr
 // LAVa: per layer, S and Q from the chunk partials in a fixed order,
 // e_l = (ln S - Q / S) / (hkv * p); then B'_l = largest remainder of
 // B' * e_l / sum(e) (equal remainders: lower layer first) and sel_off = scan.
+// online: the LAVa online prefill (LAVa notes, "在线预填充与层预算调整"): each
+// layer's budget is capped by its budget of the previous step, read from that
+// step's offsets prev_off [L] (layers 0..L-2; NULL when L == 1), and by its
+// prefix hkv * p; the newest layer (L-1) only by hkv * p.
 __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restrict__ part, int L, int chunks_per_layer,
-                                                         int hkv, int p, int64_t Bp, int64_t* __restrict__ klist,
-                                                         int64_t* __restrict__ sel_off) {
+                                                         int hkv, int p, int64_t Bp, int online,
+                                                         const int64_t* __restrict__ prev_off,
+                                                         int64_t* __restrict__ klist, int64_t* __restrict__ sel_off) {
   extern __shared__ __align__(16) char smem[];
   double* rem = reinterpret_cast<double*>(smem);     // e_l first, then the remainders
   int64_t* fl = reinterpret_cast<int64_t*>(rem + L);
@@ -417,7 +422,13 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
   for (int l = threadIdx.x; l < L; l += SB) {
     int64_t rank = 0;
     for (int j = 0; j < L; ++j) rank += (rem[j] > rem[l] || (rem[j] == rem[l] && j < l)) ? 1 : 0;
-    klist[l] = fl[l] + (rank < def ? 1 : 0);
+    int64_t k = fl[l] + (rank < def ? 1 : 0);
+    if (online) {
+      int64_t cap = (int64_t)hkv * p;
+      if (l < L - 1 && prev_off != nullptr) cap = min(cap, prev_off[l + 1] - prev_off[l]);
+      k = min(k, cap);
+    }
+    klist[l] = k;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -784,7 +795,8 @@ size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a) { return plan_alloc(g,
 //     rest; counts, budgets f0 + share, emission of both stages together.
 //   [StreamingLLM] one kernel writes budgets, offsets and indices; no scores.
 hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* score, const float* score2,
-                           int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st) {
+                           int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st, bool online,
+                           const int64_t* prev_off) {
   const AllocPlan P = plan_alloc(g, a);
   uint32_t* rowhist = reinterpret_cast<uint32_t*>(ws + P.off_rowhist);
   uint32_t* seghist = reinterpret_cast<uint32_t*>(ws + P.off_seghist);
@@ -866,7 +878,8 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   if (lava) {
     const int64_t Bp = a.budget - (int64_t)g.I * g.w * g.hkv;
     const size_t sm = (size_t)g.I * (sizeof(double) + sizeof(int64_t));
-    lava_budget_kernel<<<1, SB, sm, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp, klist, sel_off);
+    lava_budget_kernel<<<1, SB, sm, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp, online ? 1 : 0, prev_off, klist,
+                                          sel_off);
   }
   layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, lava ? klist : nullptr, segst);
   for (int ps = 1; ps < 3; ++ps) {

@@ -22,7 +22,8 @@ ADAKV_SCORE_SNAPKV, ADAKV_SCORE_LAVA, ADAKV_SCORE_CRITICALKV, ADAKV_SCORE_LAPROX
  ADAKV_ALLOC_STREAMING) = range(6)
 
 EXPORTS = ("adakv_workspace_bytes", "adakv_score", "adakv_score_lse", "adakv_allocate", "adakv_compact",
-           "adakv_decode_attn", "adakv_strerror", "adakv_version")
+           "adakv_decode_attn", "adakv_strerror", "adakv_version", "adakv_lava_online_allocate",
+           "adakv_lava_online_compact")
 
 
 class AdakvShape(ctypes.Structure):
@@ -71,6 +72,11 @@ def load(path: Optional[str] = None):
     lib.adakv_decode_attn.argtypes = [S, A, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
                                       _vp, _vp, ctypes.c_size_t, _vp]
     lib.adakv_decode_attn.restype = ctypes.c_int
+    lib.adakv_lava_online_allocate.argtypes = [S, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.adakv_lava_online_allocate.restype = ctypes.c_int
+    lib.adakv_lava_online_compact.argtypes = [S, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+                                              _vp, _vp, _vp, _vp, _vp]
+    lib.adakv_lava_online_compact.restype = ctypes.c_int
     lib.adakv_strerror.argtypes = [ctypes.c_int]
     lib.adakv_strerror.restype = ctypes.c_char_p
     lib.adakv_version.argtypes = []
@@ -150,3 +156,18 @@ def adakv_decode_attn(shape, alloc, q, k_new, v_new, k_flat, v_flat, seg_start, 
                                   _p(k_flat), _p(v_flat), _p(seg_start), _p(seg_len), reserve, step, _p(out),
                                   _p(ws), _nbytes(ws), _stream(stream))
     _check(st, "adakv_decode_attn")
+
+
+def adakv_lava_online_allocate(shape, total_budget, score, prev_sel_off, budgets, sel, sel_off, ws, stream=None):
+    st = load().adakv_lava_online_allocate(ctypes.byref(shape), int(total_budget), _p(score), _p(prev_sel_off),
+                                           _p(budgets), _p(sel), _p(sel_off), _p(ws), _nbytes(ws), _stream(stream))
+    _check(st, "adakv_lava_online_allocate")
+
+
+def adakv_lava_online_compact(shape, k_new, v_new, k_old, v_old, seg_start_old, sel_old, sel_off_old, budgets, sel,
+                              sel_off, max_rows, k_flat, v_flat, seg_start, seg_len, stream=None):
+    st = load().adakv_lava_online_compact(ctypes.byref(shape), _p(k_new), _p(v_new), _p(k_old), _p(v_old),
+                                          _p(seg_start_old), _p(sel_old), _p(sel_off_old), _p(budgets), _p(sel),
+                                          _p(sel_off), int(max_rows), _p(k_flat), _p(v_flat), _p(seg_start),
+                                          _p(seg_len), _stream(stream))
+    _check(st, "adakv_lava_online_compact")

@@ -146,3 +146,80 @@ class Eviction:
                 pos += int(b[i, g])
             res.append(heads)
         return b, off, res
+
+
+class LavaOnline:
+    """LAVa's online prefill over the layers of one sequence: after each layer
+    is prefilled, score it, re-allocate every layer so far under the shared
+    total, and rebuild the flat cache from the new layer's dense K/V and the
+    previous flat cache (two buffers used in turn).  Only the newest layer's
+    dense cache is read at each step."""
+
+    def __init__(self, cfg: Workload, n: Optional[int] = None, total: Optional[int] = None, device="cuda"):
+        import torch
+        if cfg.scorer != "lava" or cfg.batch != 1:
+            raise ValueError("the online prefill runs the LAVa scorer on the layers of one sequence")
+        self.cfg = cfg
+        self.L = cfg.layers
+        self.n = cfg.n if n is None else n
+        self.total = cfg.budget if total is None else total
+        s = make_shape(cfg, self.L, self.n)
+        self.hkv, self.w, self.p = s.hkv, s.w, s.n - s.w
+        self.tdtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        lava = lib.AdakvAlloc(mode=lib.ADAKV_ALLOC_LAVA_LAYERS, alpha_num=0, alpha_den=1, ck_num=0, ck_den=1, sinks=0,
+                              budget=self.L * self.w * self.hkv)
+        ws = max(lib.adakv_workspace_bytes(s, lava, 0), lib.adakv_workspace_bytes(make_shape(cfg, 1, self.n), None, 0))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.score = torch.empty((self.L, self.hkv, self.p), dtype=torch.float32, device=device)
+        cap = max(self.total - self.w * self.hkv, 4)         # B'(0), the largest selection of any step
+        rows = max(self.total, 1)                            # B'(l) + (l+1)*w*hkv = total at every step
+        self.bufs = []
+        for _ in range(2):
+            self.bufs.append({
+                "budgets": torch.empty((self.L * self.hkv,), dtype=torch.int32, device=device),
+                "sel": torch.empty((cap,), dtype=torch.int32, device=device),
+                "sel_off": torch.empty((self.L + 1,), dtype=torch.int64, device=device),
+                "k_flat": torch.empty((rows, s.d), dtype=self.tdtype, device=device),
+                "v_flat": torch.empty((rows, s.d), dtype=self.tdtype, device=device),
+                "seg_start": torch.empty((self.L * self.hkv + 1,), dtype=torch.int64, device=device),
+                "seg_len": torch.empty((self.L * self.hkv,), dtype=torch.int32, device=device),
+            })
+        self.max_rows = rows
+        self.layers_done = 0
+
+    def current(self):
+        return self.bufs[(self.layers_done - 1) % 2]
+
+    def step(self, q_win, k, v, stream=None):
+        """Prefill-time eviction after the next layer: q_win [hq, w, d],
+        k, v [hkv, n, d] of that layer."""
+        l = self.layers_done
+        if l >= self.L:
+            raise ValueError("every layer is already prefilled")
+        one = make_shape(self.cfg, 1, self.n)
+        lib.adakv_score(one, q_win, k, v, None, self.score[l], None, self.ws, stream)
+        cur, prev = self.bufs[l % 2], self.bufs[(l + 1) % 2]
+        sh = make_shape(self.cfg, l + 1, self.n)
+        lib.adakv_lava_online_allocate(sh, self.total, self.score[:l + 1], prev["sel_off"] if l else None,
+                                       cur["budgets"], cur["sel"], cur["sel_off"], self.ws, stream)
+        old = (lambda key: prev[key] if l else None)
+        lib.adakv_lava_online_compact(sh, k, v, old("k_flat"), old("v_flat"), old("seg_start"), old("sel"),
+                                      old("sel_off"), cur["budgets"], cur["sel"], cur["sel_off"], self.max_rows,
+                                      cur["k_flat"], cur["v_flat"], cur["seg_start"], cur["seg_len"], stream)
+        self.layers_done = l + 1
+
+    def host_selection(self):
+        """Per layer present, per head: the selected token indices (numpy)."""
+        cur = self.current()
+        I = self.layers_done
+        b = cur["budgets"][:I * self.hkv].cpu().numpy().astype(np.int64).reshape(I, self.hkv)
+        sel = cur["sel"].cpu().numpy().astype(np.int64)
+        off = cur["sel_off"][:I + 1].cpu().numpy()
+        res = []
+        for i in range(I):
+            pos, heads = int(off[i]), []
+            for g in range(self.hkv):
+                heads.append(sel[pos:pos + b[i, g]])
+                pos += int(b[i, g])
+            res.append(heads)
+        return b, off, res

@@ -8,6 +8,8 @@
  *   adakv_allocate     layer-wide top-B -> per-head budgets -> per-head selection
  *   adakv_compact      selected rows + window rows -> one flat variable-length cache
  *   adakv_decode_attn  decode attention over the flat cache (optional append)
+ *   adakv_lava_online_allocate / adakv_lava_online_compact
+ *                      LAVa's layer-by-layer prefill with re-compression
  *
  * Conventions shared by every call
  *   - Every buffer argument is DEVICE memory owned by the caller.  The library
@@ -244,6 +246,53 @@ adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, c
                            const int32_t* budgets, const int32_t* sel, const int64_t* sel_off,
                            int32_t reserve, void* k_flat, void* v_flat, int64_t* seg_start,
                            int32_t* seg_len, void* stream);
+
+/* LAVa online prefill ([LAVa-notes] "在线预填充与层预算调整"): prefill and
+ * eviction run layer by layer, and after layer l is prefilled the lower layers
+ * are compressed again with their same scores under budgets that shrink as
+ * more layers share the memory.  The pages leave the schedule open; here,
+ * after layer l the I = l + 1 layers present share B'(l) = total_budget -
+ * I*w*hkv prefix entries by the LAVA_LAYERS entropy rule (same e_j, same
+ * largest-remainder split), each layer's budget capped by its budget of the
+ * previous step (and by hkv*p), so budgets never grow and every selection lies
+ * inside the previous one.  Each layer keeps the top B_j of its flattened
+ * scores (no safeguard).  The budgets may sum to less than B'(l) where a cap
+ * binds: sel_off[I] holds the count.
+ *
+ *   shape.n_inst  I = layers prefilled so far; scorer/pool as for the scores
+ *   score         [I, hkv, p] float32, the LAVa scores of layers 0..I-1 (each
+ *                 layer's own, as adakv_score wrote them when it was prefilled)
+ *   prev_sel_off  [I] int64: sel_off of the previous step (layers 0..I-2);
+ *                 NULL when I == 1.  Must not overlap sel_off.
+ *   budgets [I, hkv] int32 out, sel int32 out (capacity total_budget - I*w*hkv,
+ *   layout as adakv_allocate), sel_off [I+1] int64 out.
+ *   ws            >= adakv_workspace_bytes(shape, LAVA_LAYERS alloc, 0) bytes
+ * Needs I <= 4096. */
+adakv_status adakv_lava_online_allocate(const adakv_shape* shape, int64_t total_budget, const float* score,
+                                        const int64_t* prev_sel_off, int32_t* budgets, int32_t* sel,
+                                        int64_t* sel_off, void* ws, size_t ws_bytes, void* stream);
+
+/* The flat cache of layers 0..I-1 after an adakv_lava_online_allocate step:
+ * the newest layer's rows (instance I-1) are gathered from its dense cache,
+ * the lower layers' rows from the previous step's flat cache, where every kept
+ * token still is (selections only shrink).  Layout as adakv_compact with no
+ * reserve rows: segment s = i*hkv + g holds B_g selected rows then w window
+ * rows.  The copy is bit-exact.
+ *
+ *   k_new, v_new     [hkv, n, d] dtype: the dense cache of layer I-1
+ *   k_old, v_old     previous flat cache (layers 0..I-2), seg_start_old
+ *                    [(I-1)*hkv+1], sel_old and sel_off_old [I] of the previous
+ *                    step; all NULL when I == 1
+ *   budgets, sel, sel_off   this step's adakv_lava_online_allocate outputs
+ *   max_rows         rows of k_flat / v_flat; rows past it are not written
+ *                    (B'(l) + I*hkv*w always suffices)
+ *   k_flat, v_flat   [max_rows, d] out, must not overlap k_old / v_old
+ *   seg_start [I*hkv+1] int64 out, seg_len [I*hkv] int32 out (B_g + w) */
+adakv_status adakv_lava_online_compact(const adakv_shape* shape, const void* k_new, const void* v_new,
+                                       const void* k_old, const void* v_old, const int64_t* seg_start_old,
+                                       const int32_t* sel_old, const int64_t* sel_off_old, const int32_t* budgets,
+                                       const int32_t* sel, const int64_t* sel_off, int64_t max_rows, void* k_flat,
+                                       void* v_flat, int64_t* seg_start, int32_t* seg_len, void* stream);
 
 /* Decode attention over the flat cache.  Segment s holds seg_len[s] rows from
  * adakv_compact plus the `step` rows appended by earlier decode calls.  If
