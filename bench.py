@@ -191,6 +191,48 @@ def cpu_baseline(cfg):
                       f"compact {t1 - t0:.2f} s, one decode step {t2 - t1:.3f} s (float64 NumPy){note}"}
 
 
+def bench_lava_online(args, cfg, data):
+    """Timed region: the whole online prefill eviction of one sequence (every
+    layer: score, re-allocate all layers so far, rebuild the flat cache)."""
+    import torch
+    from adaptive_head_budget_amd import pipeline
+    on = pipeline.LavaOnline(cfg)
+    stream = torch.cuda.current_stream()
+
+    def one_pass():
+        on.layers_done = 0
+        for l in range(cfg.layers):
+            on.step(data["q_win"][l], data["k"][l], data["v"][l])
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        one_pass()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    tokens = cfg.layers * cfg.n
+    out = {
+        "metric": "evicted-layer KV tokens/s + flat-cache decode HBM GB/s, Llama-3.1-8B shape",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded device draws; shapes of the named model, no weights)",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d, "n": cfg.n,
+                   "w": cfg.w, "pool": cfg.pool, "budget": cfg.budget, "scorer": cfg.scorer,
+                   "eviction": "online layer-by-layer prefill with re-compression"},
+        "phases_ms": {"online_prefill_eviction": ms, "per_layer": ms / cfg.layers},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +243,9 @@ def main():
     ap.add_argument("--row-lse", action="store_true",
                     help="score with adakv_score_lse: the window rows' log-sum-exp is supplied (prepared before "
                          "timing), so the keys are read once")
+    ap.add_argument("--lava-online", action="store_true",
+                    help="LAVa workloads: evict during a layer-by-layer prefill (each layer scored, all layers so "
+                         "far re-allocated and their flat cache rebuilt after every layer)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, copy a buffer of this size once (a plain copy kernel of known size, "
                          "used to calibrate HBM byte counters in a profiled run)")
@@ -251,6 +296,12 @@ def main():
             dec.append((a, b))
         if rec is not None:
             rec.append((e, dec))
+
+    if args.lava_online:
+        if cfg.scorer != "lava":
+            print("--lava-online needs a LAVa workload", file=sys.stderr)
+            sys.exit(2)
+        return bench_lava_online(args, cfg, data)
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
