@@ -176,34 +176,39 @@ __device__ __forceinline__ float allsum16(float x) {
 }
 
 // Logits of M-block mb for the NB window-row blocks: Q_win K^T with the head
-// dimension split into two halves accumulated separately and added at the end.
+// dimension split into parts accumulated separately and added at the end.
 // The matrix units round their running sum every few products; with one
 // accumulator, the error of a logit of magnitude ~600 (a head with temperature
 // 0.1) reaches ~1e-4, which moves a softmax weight by ~1e-5 relative.  Two
-// half-length sums halve the magnitude the rounding works at.
+// half-length sums halve the magnitude the rounding works at.  fp32 inputs run
+// 4-product steps (16 of them for d = 64), so they take four quarter-length
+// sums, added pairwise.
 template <typename T, int D, int NB>
 __device__ __forceinline__ void logits_block(const char* lds, int mb, int c, int gq,
                                              const typename Mma<T>::op_t (&qop)[NB][Lay<T, D>::KSTEPS],
                                              f32x4 (&out)[NB]) {
   using L = Lay<T, D>;
   using M = Mma<T>;
-  constexpr int HALF = L::KSTEPS / 2;
-  f32x4 lo[NB], hi[NB];
+  constexpr int NPART = (sizeof(T) == 4 && L::KSTEPS >= 4) ? 4 : 2;
+  constexpr int PER = L::KSTEPS / NPART;
+  f32x4 part[NPART][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) { lo[nb] = zero4(); hi[nb] = zero4(); }
+  for (int i = 0; i < NPART; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) part[i][nb] = zero4();
 #pragma unroll
   for (int ks = 0; ks < L::KSTEPS; ++ks) {
     const typename M::op_t a = M::load(a_ptr<T, D>(lds, mb, ks, c, gq));
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (ks < HALF) lo[nb] = M::mma(a, qop[nb][ks], lo[nb]);
-      else hi[nb] = M::mma(a, qop[nb][ks], hi[nb]);
-    }
+    for (int nb = 0; nb < NB; ++nb) part[ks / PER][nb] = M::mma(a, qop[nb][ks], part[ks / PER][nb]);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[nb][j] = lo[nb][j] + hi[nb][j];
+    for (int j = 0; j < 4; ++j) {
+      if (NPART == 4) out[nb][j] = (part[0][nb][j] + part[1][nb][j]) + (part[2][nb][j] + part[3][nb][j]);
+      else out[nb][j] = part[0][nb][j] + part[1][nb][j];
+    }
 }
 
 // ---------------------------------------------------------------- pass 1

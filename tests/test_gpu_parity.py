@@ -563,3 +563,35 @@ def test_lava_online_prefill_caps(gpu_lib):
     cfg = scaled(configs.MISTRAL7B_LAVA, layers=3, name="lava_online_caps")
     n = 700
     run_online(cfg, n, 3 * 8 * 32 + 3 * 8 * (n - 32) // 2, "lava online caps L3 n700")
+
+
+# ------------------------------------------------------------------ limits of the supported shapes
+def test_widest_window_and_group(gpu_lib):
+    """The largest window (64 rows: four N-blocks) and group (G = 8) the
+    scorer builds, at bf16 d = 128 with 7-wide pooling, ragged prefix."""
+    cfg = scaled(configs.LLAMA8B_LAYER, hq=64, hkv=8, w=64, name="max_window_group", decode_steps=1, reserve=1)
+    n = 1100
+    run_case(cfg, 2, n, (25 * 8 * n) // 100, 1, 1, "w64 G8 pool7")
+
+
+@pytest.mark.parametrize("scorer", ["snapkv", "lava", "criticalkv", "laprox"])
+def test_one_token_prefix(gpu_lib, scorer):
+    """n = w + 1: a single evictable token per head (p = 1), and p = 5."""
+    base = {"snapkv": configs.LLAMA8B_LAYER, "lava": scaled(configs.MISTRAL7B_LAVA, layers=2),
+            "criticalkv": scaled(configs.QWEN32B_CK, hidden=128),
+            "laprox": scaled(configs.MISTRAL7B_LAPROX, layers=2, hidden=128)}[scorer]
+    cfg = scaled(base, name=f"tiny_prefix_{scorer}", decode_steps=0, reserve=0)
+    I = 2 if scorer in ("lava", "laprox") else 1
+    for p in (1, 5):
+        n = cfg.w + p
+        win = I * cfg.w * cfg.hkv
+        budget = (win + I * cfg.hkv * p // 2) if scorer in ("lava", "laprox") else cfg.w * cfg.hkv + cfg.hkv * p // 2
+        run_case(cfg, I, n, budget, 0, 0, f"{scorer} p={p}")
+
+
+def test_many_kv_heads(gpu_lib):
+    """256 KV heads (the most the ABI takes), MHA, fp32 d = 64."""
+    cfg = scaled(configs.LLAMA8B_LAYER, hq=256, hkv=256, d=64, dtype="f32", w=16, pool=3, name="hkv256",
+                 decode_steps=1, reserve=1)
+    n = 300
+    run_case(cfg, 1, n, 256 * 16 + 256 * 50 + 7, 1, 1, "hkv 256")
