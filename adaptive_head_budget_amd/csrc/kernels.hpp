@@ -21,8 +21,21 @@ size_t score_ws_bytes(const Geo& g);
 // row_lse: NULL (two passes over K) or the caller's per-row log-sum-exp [I, hq, w]
 hipError_t launch_score(const Geo& g, const void* q, const void* k, const void* v, const void* w_o,
                         const float* row_lse, float* score, float* score2, char* ws, hipStream_t st);
+// factor: w_o holds the two bf16 planes of the Gram factors written by
+// launch_factor (LaProx with a wide projection) instead of the projection.
 hipError_t launch_vwo(const Geo& g, int inst0, int ni, const void* v, const void* w_o,
-                      const float* head_scores, float* score2, hipStream_t st);
+                      const float* head_scores, float* score2, bool factor, hipStream_t st);
+// LaProx: the L2 value norms through the d x d Gram factor when the projection
+// is at least four times as wide as the head (hidden >= 4 d).
+inline bool use_factor(const Geo& g) { return g.scorer == ADAKV_SCORE_LAPROX && g.hidden >= 4 * g.d; }
+// slices of the hidden dimension summed separately for the Gram matrices
+inline int factor_slices(const Geo& g) {
+  for (int s = 8; s > 1; s >>= 1)
+    if (g.hidden % (32 * s) == 0) return s;
+  return 1;
+}
+size_t factor_ws_bytes(const Geo& g);
+hipError_t launch_factor(const Geo& g, const void* w_o, char* ws, hipStream_t st);
 
 // ---- allocation (select.hip)
 size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a);

@@ -653,7 +653,7 @@ struct ScorePlan {
   int ib;        // instances per batch
   int nchunk;    // stats chunks per head
   int kend;      // end of the widest row domain
-  size_t off_part, off_heads, off_vbar, total;
+  size_t off_part, off_heads, off_vbar, off_fac, total;
 };
 
 ScorePlan plan_score(const Geo& g) {
@@ -674,6 +674,8 @@ ScorePlan plan_score(const Geo& g) {
     off = align_up(off + (size_t)P.ib * g.hq * g.p * sizeof(float), 256);
   P.off_vbar = off;
   if (g.scorer == ADAKV_SCORE_LAVA) off = align_up(off + (size_t)g.I * g.hkv * vbar_blocks(g) * sizeof(float), 256);
+  P.off_fac = off;
+  off = align_up(off + factor_ws_bytes(g), 256);
   P.total = off;
   return P;
 }
@@ -696,6 +698,13 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   const size_t lds_stats = (size_t)TILE * L::STRIDE;
   const size_t lds_emit = (size_t)TROWS * L::STRIDE + (size_t)(g.G + 1) * TROWS * sizeof(float);
   const int ntiles = (g.p + TILE - 1) / TILE;
+  const bool factor = use_factor(g);
+  if (factor) {
+    // Gram factors of the call's shared projection, once for all instances
+    hipError_t e = launch_factor(g, w_o, ws + P.off_fac, st);
+    if (e != hipSuccess) return e;
+  }
+  const void* vw = factor ? static_cast<const void*>(ws + P.off_fac + align_up((size_t)g.hq * factor_slices(g) * 128 * 128 * sizeof(float), 256)) : w_o;
 
   if (lava) {
     dim3 grid(nvblk, g.hkv, g.I);
@@ -749,7 +758,7 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
     }
 #undef EMIT
     if (g.scorer == ADAKV_SCORE_CRITICALKV || laprox) {
-      hipError_t e = launch_vwo(g, i0, ni, v, w_o, heads, laprox ? score : score2, st);
+      hipError_t e = launch_vwo(g, i0, ni, v, vw, heads, laprox ? score : score2, factor, st);
       if (e != hipSuccess) return e;
     }
   }
