@@ -363,16 +363,30 @@ __global__ __launch_bounds__(SB) void layer_pick0_kernel(const uint32_t* __restr
     if (threadIdx.x == 0) { RState none = {NONE, 0}; seg[inst] = none; }
     return;
   }
+  // the instance's pass-0 histogram: its rows' histograms added bin by bin,
+  // 32 independent loads in flight per thread, into LDS
+  __shared__ uint32_t hsum[NBIN];
   const uint32_t* h0 = rowhist + (size_t)inst * hkv * NBIN;
+  uint32_t t[NBIN / SB];
+#pragma unroll
+  for (int j = 0; j < NBIN / SB; ++j) t[j] = 0u;
+  for (int g0 = 0; g0 < hkv; g0 += 4) {
+    uint32_t x[4][NBIN / SB];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < NBIN / SB; ++j)
+        x[u][j] = (g0 + u < hkv) ? h0[(size_t)(g0 + u) * NBIN + (int)threadIdx.x + SB * j] : 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < NBIN / SB; ++j) t[j] += x[u][j];
+  }
+#pragma unroll
+  for (int j = 0; j < NBIN / SB; ++j) hsum[(int)threadIdx.x + SB * j] = t[j];
+  __syncthreads();
   uint32_t d, above;
-  block_pick(
-      [&](int b) {
-        uint32_t t = 0;
-#pragma unroll 8
-        for (int g = 0; g < hkv; ++g) t += h0[(size_t)g * NBIN + b];
-        return t;
-      },
-      NBIN, (uint32_t)k, sh, d, above);
+  block_pick([&](int b) { return hsum[b]; }, NBIN, (uint32_t)k, sh, d, above);
   if (threadIdx.x == 0) { RState x = {d << 20, k - (int32_t)above}; seg[inst] = x; }
 }
 
