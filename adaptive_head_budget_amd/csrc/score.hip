@@ -86,7 +86,8 @@ __device__ __forceinline__ const T* a_ptr(const char* lds, int mb, int ks, int c
 
 // K tile staging in two halves so the global loads of tile t+1 are in
 // flight while tile t is multiplied: load() fills registers, store() moves
-// them to LDS.  Keys [k0 + KLO, k0 + KHI) of one head; keys outside [0, n)
+// them to LDS.  K is streamed (the second pass re-reads it from HBM), so the
+// loads are nontemporal.  Keys [k0 + KLO, k0 + KHI) of one head; keys outside [0, n)
 // become zero rows.  The per-thread chunk -> (source offset, LDS row) map is
 // the same for every tile and is computed once.  Needs >= 256 threads.
 template <typename T, int D, int KLO, int KHI>
@@ -114,13 +115,13 @@ struct TileRegs {
     if (k0 + KLO >= 0 && k0 + KHI <= n) {
 #pragma unroll
       for (int i = 0; i < PER; ++i)
-        if (dst[i] >= 0) r[i] = ld16(base + src[i]);
+        if (dst[i] >= 0) r[i] = ld16_nt(base + src[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int key = k0 + kof[i];
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (dst[i] >= 0 && key >= 0 && key < n) v = ld16(base + src[i]);
+        if (dst[i] >= 0 && key >= 0 && key < n) v = ld16_nt(base + src[i]);
         r[i] = v;
       }
     }
