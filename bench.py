@@ -252,7 +252,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the eviction path has no multi-GPU "
-              f"leg in this build", file=sys.stderr)
+              f"leg: instances shard across GPUs with no exchange, so one GPU's rate is the per-GPU figure",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
