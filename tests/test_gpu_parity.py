@@ -595,3 +595,74 @@ def test_many_kv_heads(gpu_lib):
                  decode_steps=1, reserve=1)
     n = 300
     run_case(cfg, 1, n, 256 * 16 + 256 * 50 + 7, 1, 1, "hkv 256")
+
+
+# ------------------------------------------------------------------ calling contract
+def _eviction_outputs(ev):
+    return [t.clone() for t in (ev.score, ev.budgets, ev.sel, ev.sel_off, ev.seg_start, ev.seg_len)]
+
+
+def test_concurrent_streams_match_sequential(gpu_lib):
+    """Calls are stateless: two evictions with their own workspaces on two
+    streams at once give the same bytes as the same calls one after the other."""
+    cfg = scaled(configs.LLAMA8B_MODEL, layers=1, batch=2, name="streams", decode_steps=0)
+    n = 3000
+    inputs = []
+    for seed in (0, 1):
+        insts = [synth.make_instance(cfg, 2 * seed + i, n_override=n) for i in range(2)]
+        inputs.append({k: pipeline.to_device(np.stack([x[k] for x in insts]), "bf16") for k in ("q_win", "k", "v")})
+    evs = [pipeline.Eviction(cfg, n_inst=2, n=n, budget=8 * 300, reserve=0) for _ in range(2)]
+    ref = []
+    for ev, x in zip(evs, inputs):
+        ev.evict(x["q_win"], x["k"], x["v"])
+        torch.cuda.synchronize()
+        ref.append(_eviction_outputs(ev))
+        for t in (ev.score, ev.sel, ev.budgets):
+            t.zero_()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for ev, x, s in zip(evs, inputs, streams):
+            with torch.cuda.stream(s):
+                ev.evict(x["q_win"], x["k"], x["v"])
+        torch.cuda.synchronize()
+        for ev, r in zip(evs, ref):
+            for a, b in zip(_eviction_outputs(ev), r):
+                assert torch.equal(a, b), f"concurrent run {rep} differs"
+    log("  two streams: every output identical to the sequential run, three times")
+
+
+def test_graph_replay_matches_eager(gpu_lib):
+    """The eviction calls launch on the caller's stream, need no host
+    synchronisation and issue no memset, so they can be captured: every replay
+    of the captured graph, with eager work between replays, matches the eager
+    result."""
+    cfg = scaled(configs.LLAMA8B_LAYER, name="graph", decode_steps=1, reserve=1)
+    n = 2500
+    inst = synth.make_instance(cfg, 0, n_override=n)
+    q, k, v = (pipeline.to_device(inst[x][None], "bf16") for x in ("q_win", "k", "v"))
+    qd = pipeline.to_device(inst["q_dec"][0][None], "bf16")
+    ev = pipeline.Eviction(cfg, n_inst=1, n=n, budget=8 * 400, reserve=1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ev.evict(q, k, v)
+        ev.run_decode(qd)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = _eviction_outputs(ev) + [ev.out.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ev.evict(q, k, v)
+        ev.run_decode(qd)
+    for rep in range(4):
+        for t in (ev.score, ev.sel, ev.budgets, ev.out):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(_eviction_outputs(ev) + [ev.out], ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager run"
+    log("  graph replays: four replays identical to the eager run")
