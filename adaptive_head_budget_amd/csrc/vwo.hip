@@ -230,8 +230,15 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
 // x_c x_c^T, x_c = w_o[c, i*d .. i*d + d) (row c of the nn.Linear weight
 // restricted to head i), as fp32 on 16x16x32 bf16 MFMA.  Slices are staged
 // through LDS transposed ([e][c], 32 rows of c per step) so both operands
-// read 8 consecutive c per lane.  Wave w computes output row blocks 2w, 2w+1.
+// read 8 consecutive c per lane; 16-byte chunk ch of row e sits at position
+// ch ^ ((e >> 4) & 3), so one transposed store instruction (rows 8k + q of 16
+// chunks k) touches 8 bank groups instead of 1, and the 16 rows of one operand
+// read keep one swizzle (reads stay conflict-free with the 80-byte pitch).
+// Wave w computes output row blocks 2w, 2w+1.  The loads of GDEPTH steps are in flight at once (one workgroup per CU, so
+// the slice streams at the rate of many outstanding loads, not of one
+// round trip per step), and the barrier leaves them in flight.
 constexpr int GSTEP = 32;                  // hidden rows per step
+constexpr int GDEPTH = 4;                  // steps of loads in flight
 __global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ w_o, float* __restrict__ part,
                                                    int hq, int hidden, int nslice) {
   __shared__ __align__(16) uint16_t t[2][D][GSTEP + 8];   // padded rows
@@ -246,35 +253,60 @@ __global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ 
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) acc[a][b] = zero4();
-  // each thread stages 2 chunks of 8 columns: rows c (32) x 16 chunks per step
-  auto stage = [&](int buf, int cs) {
+  // each thread moves 2 chunks of 8 columns per step: rows c (32) x 16 chunks
+  auto load = [&](u32x4 (&r)[2], int step) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int idx = threadIdx.x + 256 * q, r = idx >> 4, ch = idx & 15;
-      const u32x4 v = ld16(w_o + (size_t)(cs + r) * wrow + (size_t)i * D + ch * 8);
+      const int idx = threadIdx.x + 256 * q, rr = idx >> 4, ch = idx & 15;
+      r[q] = ld16(w_o + (size_t)(c0 + step * GSTEP + rr) * wrow + (size_t)i * D + ch * 8);
+    }
+  };
+  auto store = [&](const u32x4 (&r)[2], int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = threadIdx.x + 256 * q, rr = idx >> 4, ch = idx & 15;
+      const int col = (((rr >> 3) ^ ((ch >> 1) & 3)) << 3) + (rr & 7);   // rows ch*8.. share e >> 4 = ch >> 1
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        t[buf][ch * 8 + 2 * j][r] = (uint16_t)(v[j] & 0xffffu);
-        t[buf][ch * 8 + 2 * j + 1][r] = (uint16_t)(v[j] >> 16);
+        t[buf][ch * 8 + 2 * j][col] = (uint16_t)(r[q][j] & 0xffffu);
+        t[buf][ch * 8 + 2 * j + 1][col] = (uint16_t)(r[q][j] >> 16);
       }
     }
   };
   const int nsteps = per / GSTEP;
-  stage(0, c0);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) stage(buf ^ 1, c0 + (st + 1) * GSTEP);
-    bf16x8 aop[2], bop[8];
+  // rg[j] holds the loads of steps j, j + GDEPTH, j + 2 GDEPTH, ... in turn
+  u32x4 rg[GDEPTH][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) aop[a] = *reinterpret_cast<const bf16x8*>(&t[buf][16 * (2 * wv + a) + c][8 * gq]);
+  for (int j = 0; j < GDEPTH; ++j)
+    if (j < nsteps) load(rg[j], j);
+  store(rg[0], 0);
+  if (GDEPTH < nsteps) load(rg[0], GDEPTH);
+  lds_barrier();
+  for (int s0 = 0; s0 < nsteps; s0 += GDEPTH) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) bop[b] = *reinterpret_cast<const bf16x8*>(&t[buf][16 * b + c][8 * gq]);
+    for (int k = 0; k < GDEPTH; ++k) {
+      const int s = s0 + k;
+      if (s < nsteps) {
+        // step s + 1 into the other buffer (its readers, step s - 1, are past
+        // the last barrier), then its registers take step s + 1 + GDEPTH
+        if (s + 1 < nsteps) {
+          store(rg[(k + 1) % GDEPTH], (s + 1) & 1);
+          if (s + 1 + GDEPTH < nsteps) load(rg[(k + 1) % GDEPTH], s + 1 + GDEPTH);
+        }
+        const int buf = s & 1;
+        bf16x8 aop[2], bop[8];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
+          aop[a] = *reinterpret_cast<const bf16x8*>(&t[buf][16 * (2 * wv + a) + c][8 * (gq ^ ((2 * wv + a) & 3))]);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[a][b] = Mma<uint16_t>::mma(aop[a], bop[b], acc[a][b]);
-    __syncthreads();
+        for (int b = 0; b < 8; ++b) bop[b] = *reinterpret_cast<const bf16x8*>(&t[buf][16 * b + c][8 * (gq ^ (b & 3))]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 8; ++b) acc[a][b] = Mma<uint16_t>::mma(aop[a], bop[b], acc[a][b]);
+        lds_barrier();
+      }
+    }
   }
   float* out = part + ((size_t)i * nslice + sl) * D * D;
 #pragma unroll
