@@ -15,7 +15,10 @@
 // and writes M_i as two bf16 planes (M = hi + lo to ~2^-17 relative), and the
 // norm kernel forms u = v M_i from the two planes (2*d columns instead of D),
 // places v itself in the same accumulator layout with one MFMA against an
-// identity operand, and folds u . v.
+// identity operand, and folds u . v.  The form only depends on M + M^T, so the
+// planes hold M' with M'[c][e] = 2 M[c][e] where e lies in an earlier 32-block
+// than c, M[c][e] in the same block and 0 in a later one: output columns of
+// block t contract over k-steps 0..t only (10 of 16 steps per head).
 //
 // For one KV head g and 256 keys, a workgroup forms V_g[t, :] W^O_i (K = d = 128,
 // N = hidden) for every query head i of the group on 16x16x32 bf16 MFMA tiles,
@@ -82,7 +85,8 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
     for (int i = 0; i < CPT; ++i) {
       const int idx = threadIdx.x + 256 * i, r = idx >> 4;
       const size_t row = (size_t)(r / NT) * hidden + (r % NT);
-      reg[i] = ld16(wb + row * wrow + (idx & 15) * 8);
+      // MODE 2: tile T reads k-steps 0..T % 4 only (chunks 4 ks .. 4 ks + 3)
+      if (MODE != VWO_GRAM || ((idx & 15) >> 2) <= (T % ntiles)) reg[i] = ld16(wb + row * wrow + (idx & 15) * 8);
     }
   };
   auto store_tile = [&](const u32x4 (&reg)[CPT], char* slot) {
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
       for (int pl = 0; pl < NPLANE; ++pl) {
         const int r = pl * NT + 16 * nb + c;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
+        for (int ks = 0; ks < (MODE == VWO_GRAM ? KSID + 1 : KSTEPS); ++ks) {
           const bf16x8 bop = *reinterpret_cast<const bf16x8*>(slot + r * ROWB + (((ks * 4 + gq) ^ c) * 16));
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb) acc[mb] = Mma<uint16_t>::mma(aop[mb][ks], bop, acc[mb]);
@@ -323,10 +327,11 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// M_i = sum of the slice partials in fp64 (fixed order), written as two bf16
-// planes in the layout of a projection: fac[p*d + c][i*d + e] = plane p of
-// M_i[c][e] (M_i is symmetric up to the rounding order of its two halves,
-// and v M v^T = v M^T v^T in any case).
+// M_i = sum of the slice partials in fp64 (fixed order); M'_i (M_i doubled
+// where e lies in an earlier 32-block than c, zero in a later one: the same
+// v M' v^T) written as two bf16 planes in the layout of a projection:
+// fac[p*d + c][i*d + e] = plane p of M'_i[c][e]; scaling by 2 is exact in
+// both planes.
 __global__ __launch_bounds__(256) void gram_planes_kernel(const float* __restrict__ part, int hq, int nslice,
                                                           uint16_t* __restrict__ fac) {
   const int i = blockIdx.y;
@@ -339,6 +344,8 @@ __global__ __launch_bounds__(256) void gram_planes_kernel(const float* __restric
   double m = 0.0;
 #pragma unroll
   for (int sl = 0; sl < 8; ++sl) m += (double)v[sl];
+  if ((e >> 5) < (c >> 5)) m *= 2.0;
+  else if ((e >> 5) > (c >> 5)) m = 0.0;
   const uint16_t hi = bf16_rne((float)m);
   const uint16_t lo = bf16_rne((float)(m - (double)__uint_as_float((uint32_t)hi << 16)));
   const size_t wrow = (size_t)hq * D;
