@@ -97,19 +97,10 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
     }
   };
 
-  u32x4 ra[CPT], rb[CPT];
-  load_tile(ra, 0);
-  if (total > 1) load_tile(rb, 1);
-  for (int idx = threadIdx.x; idx < G * KEYS; idx += 256) {
-    const int h = idx / KEYS, t = kwg + idx % KEYS;
-    float a = 0.f;
-    if (t < p) {
-      const float hsv = head_scores[((size_t)il * hq + g * G + h) * p + t];
-      a = (MODE != VWO_L1) ? sqrtf(hsv) : hsv + eps;
-    }
-    ahs[h][idx % KEYS] = a;
-  }
-  // A operands: 4 M-blocks of 16 keys, held for the whole workgroup.
+  // Every prologue load is issued before the first wait: the A operands (4
+  // M-blocks of 16 keys, held for the whole workgroup), tiles 0 and 1, and the
+  // head scores of the workgroup's keys (thread = key).
+  static_assert(KEYS == 256, "one key per thread in the prologue");
   bf16x8 aop[4][KSTEPS];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -118,6 +109,17 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) aop[mb][ks] = Mma<uint16_t>::load(vb + (size_t)t * D + ks * 32 + 8 * gq);
   }
+  u32x4 ra[CPT], rb[CPT];
+  load_tile(ra, 0);
+  if (total > 1) load_tile(rb, 1);
+  const int tk = kwg + (int)threadIdx.x;
+  float hsv[MAXG];
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h)
+    hsv[h] = (h < G && tk < p) ? head_scores[((size_t)il * hq + g * G + h) * p + tk] : 0.f;
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h)
+    if (h < G) ahs[h][threadIdx.x] = (tk < p) ? ((MODE != VWO_L1) ? sqrtf(hsv[h]) : hsv[h] + eps) : 0.f;
   store_tile(ra, wt[0]);
   if (total > 2) load_tile(ra, 2);
   __syncthreads();     // ahs and tile 0 in LDS
