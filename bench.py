@@ -347,11 +347,16 @@ def main():
         "score_hbm_gbps": score_bytes(cfg) / (sc * 1e-3) / 1e9,
         "compact_hbm_gbps": compact_bytes(cfg) / (co * 1e-3) / 1e9,
     }
-    if cfg.scorer in ("criticalkv", "laprox"):
+    if cfg.scorer == "criticalkv" or (cfg.scorer == "laprox" and cfg.hidden < 4 * cfg.d):
         # the projected-norm contraction bounds this workload: its flops over the
         # whole scoring call (window scores included, so a lower bound on the rate)
         vwo_flops = 2.0 * cfg.instances * cfg.hq * cfg.p * cfg.d * cfg.hidden
         out["score_mfma_tflops_lower_bound"] = vwo_flops / (sc * 1e-3) / 1e12
+    elif cfg.scorer == "laprox":
+        # L2 value norms through the d x d Gram matrices: forming them (d^2 D per
+        # head) and one d x d product per (key, head), over the whole scoring call
+        gram_flops = 2.0 * cfg.instances * cfg.hq * cfg.d * cfg.d * (cfg.hidden + cfg.p)
+        out["score_gram_mfma_tflops_lower_bound"] = gram_flops / (sc * 1e-3) / 1e12
     if steps_dec:
         avg_launch_s = float(np.mean(dec_launch_ms)) * 1e-3
         per_launch_bytes = dec_bytes_total / steps_dec
