@@ -257,36 +257,68 @@ __device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* hg, int 
 }
 
 // One digit pass over segments of seg_rows rows: the histogram of the digits
-// of pass ps among the candidates that match the segment's prefix.  Pass 0
+// of pass PS among the candidates that match the segment's prefix.  Pass 0
 // takes k from kinit[segment] (kconst when kinit is NULL), later passes
-// continue from st[segment].  With member flags, flagged scores are not
-// candidates.
+// continue from st[segment].  With member flags (USE_M), flagged scores are not
+// candidates.  The pass and the flags are compile-time: with them at run time
+// the per-score loop compiles to a chain of divergent branches that costs more
+// than the chunk's load.
+template <int PS, bool USE_M>
 __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict__ score,
                                                         const uint8_t* __restrict__ member, int p, int cpr,
-                                                        int ntile, int vec, int seg_rows, int ps,
+                                                        int ntile, int vec, int seg_rows,
                                                         const int32_t* __restrict__ kinit, int kconst,
                                                         const RState* __restrict__ st, uint32_t* __restrict__ hist) {
   __shared__ uint32_t h[NBIN];
   const Chunk ch = chunk_of(cpr, ntile, p);
   const int s = ch.r / seg_rows;
+  ChunkKeys K;
+  uint8_t m[NK];
+  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  if (USE_M) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
   RState cur;
-  if (ps == 0) {
+  if (PS == 0) {
     cur.prefix = 0u;
     cur.krem = kinit ? kinit[s] : kconst;
   } else {
     cur = st[s];
   }
   if (cur.krem <= 0 || cur.prefix == NONE) return;
-  const int nb = pass_bins(ps);
-  ChunkKeys K;
-  uint8_t m[NK];
-  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
-  if (member) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
+  constexpr int nb = PS == 2 ? 512 : NBIN;
+  bool el[NK];
+  int any = 0;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    el[j] = j < K.n && (!USE_M || m[j] == 0) && in_prefix(K.k[j], cur.prefix, PS);
+    any |= el[j] ? 1 : 0;
+  }
+  // after the first digit most chunks hold no candidate: no histogram then
+  if (PS > 0 && !__syncthreads_or(any)) return;
   for (int b = threadIdx.x; b < nb; b += SB) h[b] = 0u;
   __syncthreads();
-  chunk_hist(h, K, m, member != nullptr, cur.prefix, ps);
+  if (PS == 0) {
+    chunk_hist(h, K, m, USE_M, 0u, 0);
+  } else {
+    // candidates are sparse: one masked atomic each, no run merging
+#pragma unroll
+    for (int j = 0; j < NK; ++j)
+      if (el[j]) atomicAdd(h + digit_of(K.k[j], PS), 1u);
+  }
   __syncthreads();
   flush_hist(h, hist + (size_t)s * NBIN, nb);
+}
+
+// Launches the digit pass ps (0..2) with or without member flags.
+void radix_hist(int nc, hipStream_t stream, const float* score, const uint8_t* member, int p, int cpr, int ntile,
+                int vec, int seg_rows, int ps, const int32_t* kinit, int kconst, const RState* st, uint32_t* hist) {
+#define RH(PSV, M)                                                                                       \
+  radix_hist_kernel<PSV, M><<<nc, SB, 0, stream>>>(score, member, p, cpr, ntile, vec, seg_rows, kinit, kconst, st, hist)
+  if (member != nullptr) {
+    if (ps == 0) RH(0, true); else if (ps == 1) RH(1, true); else RH(2, true);
+  } else {
+    if (ps == 0) RH(0, false); else if (ps == 1) RH(1, false); else RH(2, false);
+  }
+#undef RH
 }
 
 // The digit pick of pass ps for every segment, one workgroup each; pass 0
@@ -464,12 +496,12 @@ __global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict
                                                          const RState* __restrict__ seg, uint32_t* __restrict__ cnt) {
   __shared__ uint32_t sh[SW + 4];
   const Chunk ch = chunk_of(cpr, ntile, p);
-  const RState L = seg[ch.r / seg_rows];
-  if (L.prefix == NONE) return;
   ChunkKeys K;
   uint8_t m[NK];
   load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
   if (member) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
+  const RState L = seg[ch.r / seg_rows];
+  if (L.prefix == NONE) return;
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
@@ -853,7 +885,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     const int kP = (int)(a.budget - (int64_t)g.w * g.hkv);
     const int f0 = (int)(((int64_t)a.alpha_num * kP) / ((int64_t)a.alpha_den * hkv));
     for (int ps = 0; ps < 3; ++ps) {
-      radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, f0, rowst, rowhist);
+      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, f0, rowst, rowhist);
       radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, f0, rowst);
     }
     chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
@@ -861,7 +893,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
                                    member);
     const int k2 = kP - hkv * f0;
     for (int ps = 0; ps < 3; ++ps) {
-      radix_hist_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, hkv, ps, nullptr, k2, segst, seghist);
+      radix_hist(nc, st, score, member, g.p, cpr, nt, vec1, hkv, ps, nullptr, k2, segst, seghist);
       radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, k2, segst);
     }
     layer_count_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, hkv, segst, cnt);
@@ -877,7 +909,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     // rows' counts at its threshold, their budgets and offsets, emission.
     const int Bp = (int)(a.budget - (int64_t)g.I * g.w * g.hkv);
     for (int ps = 0; ps < 3; ++ps) {
-      radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, ps, nullptr, Bp, segst, seghist);
+      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, R, ps, nullptr, Bp, segst, seghist);
       radix_pick_kernel<<<1, SB, 0, st>>>(seghist, ps, nullptr, Bp, segst);
     }
     layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, segst, cnt);
@@ -897,7 +929,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   }
   layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, lava ? klist : nullptr, segst);
   for (int ps = 1; ps < 3; ++ps) {
-    radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist);
+    radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist);
     radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, 0, segst);
   }
   // Head budgets.
@@ -907,7 +939,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   // Every head's own top-k (LAVa keeps the layer threshold).
   if (!lava) {
     for (int ps = 1; ps < 3; ++ps) {
-      radix_hist_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, 0, rowst, rowhist);
+      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, 0, rowst, rowhist);
       radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, 0, rowst);
     }
   }
@@ -921,7 +953,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
                                  member);
   for (int ps = 0; ps < 3; ++ps) {
-    radix_hist_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, 1, ps, rowk2, 0, rowst2, rowhist);
+    radix_hist(nc, st, score2, member, g.p, cpr, nt, vec2, 1, ps, rowk2, 0, rowst2, rowhist);
     radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, rowk2, 0, rowst2);
   }
   chunk_count_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc);
