@@ -710,8 +710,9 @@ __global__ __launch_bounds__(SB) void chunk_count_kernel(const float* __restrict
 }
 
 // Writes the kept scores of the chunk in index order: as token indices at
-// sel[rowbase[r] + position] (at most cap[r] of them, never past sel_total), or
-// as member flags.
+// sel[rowbase[r] + position] (TO_SEL: at most cap[r] of them, never past
+// sel_total), or as member flags.  USE_M: flagged scores count as kept.
+template <bool USE_M, bool TO_SEL>
 __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ score, const uint8_t* __restrict__ member,
                                                   int p, int cpr, int ntile, int vec, const RState* __restrict__ rowst,
                                                   const uint32_t* __restrict__ cc, const int64_t* __restrict__ rowbase,
@@ -724,7 +725,7 @@ __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ scor
   ChunkKeys K;
   uint8_t m[NK];
   load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
-  if (member) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
+  if (USE_M) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
   // Kept scores and ties of the row's earlier chunks.
   uint32_t b2 = 0, b1 = 0;
   for (int c = threadIdx.x; c < ch.c; c += SB) {
@@ -741,33 +742,43 @@ __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ scor
   const uint32_t quota = (S.prefix == NONE) ? 0u : (uint32_t)S.krem;
   const uint32_t qrem = quota > B1 ? quota - B1 : 0u;
   const uint32_t pos0 = B2 + (quota < B1 ? quota : B1);
-  const int64_t base = rowbase ? rowbase[ch.r] : 0;
-  const uint32_t lim = cap ? (uint32_t)cap[ch.r] : 0xFFFFFFFFu;
+  const int64_t base = TO_SEL ? rowbase[ch.r] : 0;
+  const uint32_t lim = TO_SEL ? (uint32_t)cap[ch.r] : 0u;
 
   int kc[NK];
   uint32_t n2 = 0, n1 = 0;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
-    kc[j] = klass(K.k[j], j < K.n, member != nullptr && m[j] != 0, S.prefix);
+    kc[j] = klass(K.k[j], j < K.n, USE_M && m[j] != 0, S.prefix);
     n2 += kc[j] == 2 ? 1u : 0u;
     n1 += kc[j] == 1 ? 1u : 0u;
   }
   uint32_t tot;
   const uint32_t ex = block_excl_scan(n2 | (n1 << 16), sh, tot);
-  (void)tot;
   const uint32_t e2 = ex & 0xFFFFu, e1 = ex >> 16;
   uint32_t tie = e1;                                   // ties of the chunk before this thread's scores
-  uint32_t pos = pos0 + e2 + (e1 < qrem ? e1 : qrem);
+  uint32_t loc = e2 + (e1 < qrem ? e1 : qrem);         // position in the chunk's run of kept scores
   uint8_t take[NK];
+  // the chunk's kept indices occupy positions pos0 .. pos0 + cnt - 1: staged
+  // in LDS in order, then written with consecutive lanes on consecutive words
+  __shared__ int32_t stage[SB * NK];
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
     bool tk = kc[j] == 2;
     if (kc[j] == 1) { tk = tie < qrem; ++tie; }
     take[j] = tk ? 1 : 0;
-    if (tk && sel != nullptr && pos < lim && base + pos < sel_total) sel[base + pos] = K.e0 + j;
-    pos += tk ? 1u : 0u;
+    if (TO_SEL && tk) stage[loc] = K.e0 + j;
+    loc += tk ? 1u : 0u;
   }
-  if (member_out != nullptr) {
+  if (TO_SEL) {
+    const uint32_t cnt = (tot & 0xFFFFu) + ((tot >> 16) < qrem ? (tot >> 16) : qrem);
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < cnt; i += SB) {
+      const uint32_t pos = pos0 + i;
+      if (pos < lim && base + pos < sel_total) sel[base + pos] = stage[i];
+    }
+  }
+  if (!TO_SEL) {
     uint8_t* mo = member_out + (size_t)ch.r * p;
     if (vec && ch.e_end - ch.e_begin == ntile * TILE) {
 #pragma unroll
@@ -889,7 +900,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
       radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, f0, rowst);
     }
     chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
-    emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
+    emit_kernel<false, false><<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
                                    member);
     const int k2 = kP - hkv * f0;
     for (int ps = 0; ps < 3; ++ps) {
@@ -900,7 +911,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     segment_budget_kernel<<<g.I, SB, 0, st>>>(hkv, hkv, g.I, f0, (int64_t)kP, segst, cnt, budgets, rowbase, rowst2,
                                               sel_off);
     chunk_count_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, rowst2, cc);
-    emit_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, rowst2, cc, rowbase, budgets, sel,
+    emit_kernel<true, true><<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, rowst2, cc, rowbase, budgets, sel,
                                    (int64_t)g.I * kP, nullptr);
     return hipGetLastError();
   }
@@ -915,7 +926,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, segst, cnt);
     segment_budget_kernel<<<1, SB, 0, st>>>(R, hkv, g.I, 0, 0, segst, cnt, budgets, rowbase, rowst, sel_off);
     chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
-    emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets, sel, (int64_t)Bp,
+    emit_kernel<false, true><<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets, sel, (int64_t)Bp,
                                    nullptr);
     return hipGetLastError();
   }
@@ -945,19 +956,19 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   }
   chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
   if (!ck) {
-    emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets, sel, sel_total,
+    emit_kernel<false, true><<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets, sel, sel_total,
                                    nullptr);
     return hipGetLastError();
   }
   // CriticalKV: stage-1 members, then stage 2 on the composite score over the rest.
-  emit_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
+  emit_kernel<false, false><<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
                                  member);
   for (int ps = 0; ps < 3; ++ps) {
     radix_hist(nc, st, score2, member, g.p, cpr, nt, vec2, 1, ps, rowk2, 0, rowst2, rowhist);
     radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, rowk2, 0, rowst2);
   }
   chunk_count_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc);
-  emit_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc, rowbase, budgets, sel, sel_total,
+  emit_kernel<true, true><<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc, rowbase, budgets, sel, sel_total,
                                  nullptr);
   return hipGetLastError();
 }
