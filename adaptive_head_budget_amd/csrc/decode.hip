@@ -56,7 +56,17 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const T* __restrict__ q,
   __shared__ float Sc[4][GT];
   __shared__ float Mw[4][GT], Lw[4][GT];
 
-  const int s = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
+  // Workgroups are dealt round-robin to the 8 XCDs and then to an XCD's CUs, so
+  // with segment = block index every CU would hold segments of one KV head.  The
+  // [8][S/8] -> [S/8][8] transpose gives the workgroups sharing a CU different
+  // heads, whose unequal Ada-KV budgets then even out (split launches, with
+  // few segments, keep the identity).
+  int bx = blockIdx.x;
+  if (nsplit == 1 && gridDim.x % 8 == 0) {
+    const int Q = gridDim.x / 8;
+    bx = (bx % Q) * 8 + bx / Q;
+  }
+  const int s = bx / nsplit, split = bx % nsplit;
   const int inst = s / hkv, g = s % hkv;
   const int64_t base = seg_start[s];
   const int cap = (int)(seg_start[s + 1] - base);
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(const T* __restrict__ q,
     if (nsplit == 1) {
       if (e < D) out[((size_t)inst * hq + (size_t)g * G + h) * D + e] = acc2 / l2;
     } else {
-      part[((size_t)blockIdx.x * G + h) * (D + 2) + e] = (e < D) ? acc2 : (e == D ? Mx : l2);
+      part[((size_t)bx * G + h) * (D + 2) + e] = (e < D) ? acc2 : (e == D ? Mx : l2);
     }
   }
 }
