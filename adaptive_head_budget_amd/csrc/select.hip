@@ -160,11 +160,21 @@ __device__ __forceinline__ Chunk chunk_of(int cpr, int ntile, int p) {
 // before any is used: addresses past the chunk are clamped to its last score
 // (16-byte groups for rows of a multiple of 4 scores on a 16-byte aligned base,
 // single scores otherwise), so a partial chunk costs no more than a full one.
+// CHECK: `bad` is nonzero when a loaded score breaks the precondition
+// (negative other than -0, NaN or infinite); clamped duplicates repeat scores
+// of the chunk, so they need no mask.
 struct ChunkKeys {
   uint32_t k[NK];
   int e0, n;
+  uint32_t bad;
 };
+__device__ __forceinline__ uint32_t bad_score(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u > 0x80000000u || (u & 0x7FFFFFFFu) >= 0x7F800000u) ? 1u : 0u;
+}
+template <bool CHECK = false>
 __device__ __forceinline__ void load_chunk(const float* row, const Chunk& ch, int ntile, bool vec, ChunkKeys& K) {
+  K.bad = 0u;
   const int npt = 4 * ntile;
   K.e0 = ch.e_begin + npt * (int)threadIdx.x;
   K.n = max(0, min(npt, ch.e_end - K.e0));
@@ -176,14 +186,20 @@ __device__ __forceinline__ void load_chunk(const float* row, const Chunk& ch, in
 #pragma unroll
     for (int t = 0; t < MAXT; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) K.k[4 * t + j] = sel_key(v[t][j]);
+      for (int j = 0; j < 4; ++j) {
+        K.k[4 * t + j] = sel_key(v[t][j]);
+        if (CHECK) K.bad |= bad_score(v[t][j]);
+      }
     return;
   }
   float v[NK];
 #pragma unroll
   for (int j = 0; j < NK; ++j) v[j] = row[min(K.e0 + (j < npt ? j : 0), ch.e_end - 1)];
 #pragma unroll
-  for (int j = 0; j < NK; ++j) K.k[j] = sel_key(v[j]);
+  for (int j = 0; j < NK; ++j) {
+    K.k[j] = sel_key(v[j]);
+    if (CHECK) K.bad |= bad_score(v[j]);
+  }
 }
 
 // Member flags of the thread's scores (CriticalKV stage 1), clamped like the scores.
@@ -268,13 +284,15 @@ __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict_
                                                         const uint8_t* __restrict__ member, int p, int cpr,
                                                         int ntile, int vec, int seg_rows,
                                                         const int32_t* __restrict__ kinit, int kconst,
-                                                        const RState* __restrict__ st, uint32_t* __restrict__ hist) {
+                                                        const RState* __restrict__ st, uint32_t* __restrict__ hist,
+                                                        uint32_t* __restrict__ flag) {
   __shared__ uint32_t h[NBIN];
   const Chunk ch = chunk_of(cpr, ntile, p);
   const int s = ch.r / seg_rows;
   ChunkKeys K;
   uint8_t m[NK];
-  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  load_chunk<PS == 0>(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  if (PS == 0 && K.bad) atomicOr(flag, 1u);   // precondition broken somewhere in the chunk
   if (USE_M) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
   RState cur;
   if (PS == 0) {
@@ -310,9 +328,11 @@ __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict_
 
 // Launches the digit pass ps (0..2) with or without member flags.
 void radix_hist(int nc, hipStream_t stream, const float* score, const uint8_t* member, int p, int cpr, int ntile,
-                int vec, int seg_rows, int ps, const int32_t* kinit, int kconst, const RState* st, uint32_t* hist) {
+                int vec, int seg_rows, int ps, const int32_t* kinit, int kconst, const RState* st, uint32_t* hist,
+                uint32_t* flag) {
 #define RH(PSV, M)                                                                                       \
-  radix_hist_kernel<PSV, M><<<nc, SB, 0, stream>>>(score, member, p, cpr, ntile, vec, seg_rows, kinit, kconst, st, hist)
+  radix_hist_kernel<PSV, M><<<nc, SB, 0, stream>>>(score, member, p, cpr, ntile, vec, seg_rows, kinit, kconst, st, hist, \
+                                                   flag)
   if (member != nullptr) {
     if (ps == 0) RH(0, true); else if (ps == 1) RH(1, true); else RH(2, true);
   } else {
@@ -345,13 +365,14 @@ __global__ __launch_bounds__(SB) void radix_pick_kernel(uint32_t* __restrict__ h
 // partial sums S = sum s and Q = sum s ln s (fp64) for the layer entropy.
 __global__ __launch_bounds__(SB) void layer_hist0_kernel(const float* __restrict__ score, int p, int cpr, int ntile,
                                                          int vec, int lava, uint32_t* __restrict__ rowhist,
-                                                         double* __restrict__ part) {
+                                                         double* __restrict__ part, uint32_t* __restrict__ flag) {
   __shared__ uint32_t h[NBIN];
   __shared__ double dsh[2][SW];
   const Chunk ch = chunk_of(cpr, ntile, p);
   ChunkKeys K;
   uint8_t m[NK];
-  load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  load_chunk<true>(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
+  if (K.bad) atomicOr(flag, 1u);   // precondition broken somewhere in the chunk
   for (int b = threadIdx.x; b < NBIN; b += SB) h[b] = 0u;
   __syncthreads();
   chunk_hist(h, K, m, false, 0u, 0);
@@ -453,7 +474,9 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
   __syncthreads();
   const double E = Esh;
   for (int l = threadIdx.x; l < L; l += SB) {
-    const double x = (E > 0.0) ? ((double)Bp * rem[l]) / E : (double)Bp / (double)L;
+    // kept inside [0, B']: an entropy of exactly 0 can round to -tiny, and a NaN
+    // share (an infinite score breaking the precondition) counts as 0
+    const double x = fmin(fmax((E > 0.0) ? ((double)Bp * rem[l]) / E : (double)Bp / (double)L, 0.0), (double)Bp);
     const double f = floor(x);
     fl[l] = (int64_t)f;
     rem[l] = x - f;
@@ -800,7 +823,7 @@ __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ scor
 // ---------------------------------------------------------------- workspace plan
 struct AllocPlan {
   int R, cpr, ntile, nchunk;
-  size_t off_rowhist, off_seghist, off_cnt, zero_end;
+  size_t off_flag, off_rowhist, off_seghist, off_cnt, zero_end;
   size_t off_seg, off_row, off_row2, off_rowk2, off_rowbase, off_cc, off_member, off_part, off_klist, total;
 };
 
@@ -813,6 +836,7 @@ AllocPlan plan_alloc(const Geo& g, const adakv_alloc& a) {
   P.cpr = (g.p + P.ntile * TILE - 1) / (P.ntile * TILE);
   P.nchunk = P.R * P.cpr;
   size_t off = 0;
+  P.off_flag = off;     off = 256;   // int32: a score broke the precondition
   P.off_rowhist = off;  off = align_up(off + (size_t)P.R * NBIN * 4, 256);
   P.off_seghist = off;  off = align_up(off + (size_t)g.I * NBIN * 4, 256);
   P.off_cnt = off;      off = align_up(off + (size_t)P.R * 8, 256);
@@ -855,6 +879,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
                            int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st, bool online,
                            const int64_t* prev_off) {
   const AllocPlan P = plan_alloc(g, a);
+  uint32_t* flag = reinterpret_cast<uint32_t*>(ws + P.off_flag);
   uint32_t* rowhist = reinterpret_cast<uint32_t*>(ws + P.off_rowhist);
   uint32_t* seghist = reinterpret_cast<uint32_t*>(ws + P.off_seghist);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + P.off_cnt);
@@ -896,7 +921,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     const int kP = (int)(a.budget - (int64_t)g.w * g.hkv);
     const int f0 = (int)(((int64_t)a.alpha_num * kP) / ((int64_t)a.alpha_den * hkv));
     for (int ps = 0; ps < 3; ++ps) {
-      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, f0, rowst, rowhist);
+      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, f0, rowst, rowhist, flag);
       radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, f0, rowst);
     }
     chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
@@ -904,7 +929,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
                                    member);
     const int k2 = kP - hkv * f0;
     for (int ps = 0; ps < 3; ++ps) {
-      radix_hist(nc, st, score, member, g.p, cpr, nt, vec1, hkv, ps, nullptr, k2, segst, seghist);
+      radix_hist(nc, st, score, member, g.p, cpr, nt, vec1, hkv, ps, nullptr, k2, segst, seghist, flag);
       radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, k2, segst);
     }
     layer_count_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, hkv, segst, cnt);
@@ -920,7 +945,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     // rows' counts at its threshold, their budgets and offsets, emission.
     const int Bp = (int)(a.budget - (int64_t)g.I * g.w * g.hkv);
     for (int ps = 0; ps < 3; ++ps) {
-      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, R, ps, nullptr, Bp, segst, seghist);
+      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, R, ps, nullptr, Bp, segst, seghist, flag);
       radix_pick_kernel<<<1, SB, 0, st>>>(seghist, ps, nullptr, Bp, segst);
     }
     layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, segst, cnt);
@@ -931,7 +956,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     return hipGetLastError();
   }
   // Layer-wide top-k.
-  layer_hist0_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, lava ? 1 : 0, rowhist, part);
+  layer_hist0_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, lava ? 1 : 0, rowhist, part, flag);
   if (lava) {
     const int64_t Bp = a.budget - (int64_t)g.I * g.w * g.hkv;
     const size_t sm = (size_t)g.I * (sizeof(double) + sizeof(int64_t));
@@ -940,7 +965,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   }
   layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, lava ? klist : nullptr, segst);
   for (int ps = 1; ps < 3; ++ps) {
-    radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist);
+    radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist, flag);
     radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, 0, segst);
   }
   // Head budgets.
@@ -950,7 +975,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   // Every head's own top-k (LAVa keeps the layer threshold).
   if (!lava) {
     for (int ps = 1; ps < 3; ++ps) {
-      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, 0, rowst, rowhist);
+      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, 0, rowst, rowhist, flag);
       radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, 0, rowst);
     }
   }
@@ -964,7 +989,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   emit_kernel<false, false><<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, nullptr, nullptr, nullptr, 0,
                                  member);
   for (int ps = 0; ps < 3; ++ps) {
-    radix_hist(nc, st, score2, member, g.p, cpr, nt, vec2, 1, ps, rowk2, 0, rowst2, rowhist);
+    radix_hist(nc, st, score2, member, g.p, cpr, nt, vec2, 1, ps, rowk2, 0, rowst2, rowhist, flag);
     radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, rowk2, 0, rowst2);
   }
   chunk_count_kernel<<<nc, SB, 0, st>>>(score2, member, g.p, cpr, nt, vec2, rowst2, cc);

@@ -111,6 +111,14 @@ class Eviction:
         else:
             lib.adakv_score_lse(self.shape, q_win, k, v, w_o, row_lse, self.score, self.score2, self.ws, stream)
 
+    def scores_invalid(self) -> bool:
+        """Whether the last allocation read a negative, NaN or infinite score
+        (the int32 the library keeps at the start of the workspace).  Waits
+        for the device."""
+        import torch
+        torch.cuda.synchronize(self.ws.device)
+        return bool(self.ws[:4].view(torch.int32).item())
+
     def run_allocate(self, stream=None):
         lib.adakv_allocate(self.shape, self.alloc, self.score, self.score2, self.budgets, self.sel, self.sel_off,
                            self.ws, stream)

@@ -224,6 +224,13 @@ adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const 
  *           I*(budget - w*hkv) for ADA / CK and budget - I*w*hkv for LAVA
  *           and GLOBAL.
  *   sel_off [I+1] int64 out
+ *
+ * Precondition check: the int32 at the start of ws is cleared by the call and
+ * set to a nonzero value when a score it reads (score; score2 for CK) is
+ * negative (other than -0.0), NaN or infinite.  Such a selection is
+ * unspecified but stays inside its buffers.  Read the word after the stream
+ * has passed the call; the next call on the same ws overwrites it.  STREAMING
+ * reads no score and leaves it zero.
  */
 adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, const float* score,
                             const float* score2, int32_t* budgets, int32_t* sel, int64_t* sel_off,
@@ -266,7 +273,9 @@ adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, c
  *                 NULL when I == 1.  Must not overlap sel_off.
  *   budgets [I, hkv] int32 out, sel int32 out (capacity total_budget - I*w*hkv,
  *   layout as adakv_allocate), sel_off [I+1] int64 out.
- *   ws            >= adakv_workspace_bytes(shape, LAVA_LAYERS alloc, 0) bytes
+ *   ws            >= adakv_workspace_bytes(shape, LAVA_LAYERS alloc, 0) bytes;
+ *                 its first int32 reports broken score preconditions as for
+ *                 adakv_allocate.
  * Needs I <= 4096. */
 adakv_status adakv_lava_online_allocate(const adakv_shape* shape, int64_t total_budget, const float* score,
                                         const int64_t* prev_sel_off, int32_t* budgets, int32_t* sel,

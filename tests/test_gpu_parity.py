@@ -666,3 +666,59 @@ def test_graph_replay_matches_eager(gpu_lib):
         for a, b in zip(_eviction_outputs(ev) + [ev.out], ref):
             assert torch.equal(a, b), f"replay {rep} differs from the eager run"
     log("  graph replays: four replays identical to the eager run")
+
+
+@pytest.mark.parametrize("kind", ["ada", "floor", "global", "lava", "criticalkv"])
+def test_score_precondition_flag(gpu_lib, kind):
+    """The precondition word at the start of the allocation workspace: clear
+    for valid scores (-0.0 included), set by a negative, NaN or infinite score
+    in the first or the last chunk of the call, and the selection stays inside
+    its buffers either way (budgets sum to the prefix budget, every index in
+    [0, p))."""
+    n = 700
+    if kind == "ada":
+        cfg, I, budget = scaled(configs.LLAMA8B_LAYER, name="flag_ada", decode_steps=0), 1, 8 * 32 + 8 * 100
+    elif kind == "floor":
+        cfg, I, budget = (scaled(configs.LLAMA8B_LAYER, name="flag_floor", alloc="floor", alpha=(1, 2),
+                                 decode_steps=0), 1, 8 * 32 + 8 * 100)
+    elif kind == "global":
+        cfg, I, budget = scaled(configs.MISTRAL7B_LAPROX, layers=2, hidden=256, name="flag_global"), 2, 2 * 8 * 32 + 900
+    elif kind == "lava":
+        cfg, I, budget = scaled(configs.MISTRAL7B_LAVA, layers=3, name="flag_lava"), 3, 3 * 8 * 32 + 1500
+    else:
+        cfg, I, budget = scaled(configs.QWEN32B_CK, hidden=256, name="flag_ck", decode_steps=0), 1, 8 * 32 + 8 * 100
+    log(f"case precondition flag: {kind} I={I} n={n} budget={budget}")
+    insts, st = _stack(cfg, I, n)
+    dt = cfg.dtype
+    q, k, v = (pipeline.to_device(st[x], dt) for x in ("q_win", "k", "v"))
+    w_o = None
+    if kind == "criticalkv":
+        w_o = pipeline.to_device(insts[0]["w_o"], dt)
+    elif kind == "global":
+        w_o = pipeline.to_device(np.stack([x["w_o"] for x in insts]), dt)
+    ev = pipeline.Eviction(cfg, n_inst=I, n=n, budget=budget, reserve=0)
+    ev.run_score(q, k, v if cfg.scorer != "snapkv" else None, w_o)
+    ev.run_allocate()
+    assert not ev.scores_invalid()
+    p = n - cfg.w
+
+    def in_bounds():
+        b, off, sel = ev.host_selection()
+        assert (b >= 0).all() and int(b.sum()) == ev.n_sel
+        for heads in sel:
+            for idx in heads:
+                assert idx.size == 0 or (idx.min() >= 0 and idx.max() < p)
+
+    targets = [ev.score] + ([ev.score2] if kind == "criticalkv" else [])
+    for t in targets:
+        good = t.clone()
+        for pos in [(0, 1, 17), (I - 1, cfg.hkv - 1, p - 1)]:
+            for val, bad in [(-1.0, True), (float("nan"), True), (float("inf"), True), (-float("inf"), True),
+                             (-0.0, False), (0.0, False)]:
+                t.copy_(good)
+                t[pos] = val
+                ev.run_allocate()
+                assert ev.scores_invalid() == bad, (kind, pos, val)
+                in_bounds()
+        t.copy_(good)
+    log(f"  {kind}: flag clear on valid scores, set on -1, NaN, +-inf; selection in bounds")
