@@ -16,6 +16,11 @@
 // workgroup per segment then picks the digit and clears the histogram for the
 // next pass.  No workgroup ever waits for another.
 //
+// The first digit pass of every selection reads every score once; a negative
+// (other than -0), NaN or infinite one sets the int32 at the start of the
+// workspace (cleared at the start of the call).  Such keys stay plain uint32
+// patterns (negatives count as zero), so the selection stays in bounds.
+//
 // Definitions followed:
 //  * Ada-KV notes, Algorithm 1 (concatenate the heads, top-B, count per head)
 //    and Algorithm 2 steps 6-9 (window out of the budget, safeguard, per-head

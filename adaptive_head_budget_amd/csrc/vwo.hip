@@ -87,6 +87,7 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
       const size_t row = (size_t)(r / NT) * hidden + (r % NT);
       // MODE 2: tile T reads k-steps 0..T % 4 only (chunks 4 ks .. 4 ks + 3)
       if (MODE != VWO_GRAM || ((idx & 15) >> 2) <= (T % ntiles)) reg[i] = ld16(wb + row * wrow + (idx & 15) * 8);
+      else reg[i] = u32x4{0u, 0u, 0u, 0u};   // never read back
     }
   };
   auto store_tile = [&](const u32x4 (&reg)[CPT], char* slot) {
