@@ -175,6 +175,25 @@ def test_laprox_reduced(gpu_lib):
 
 
 # ------------------------------------------------------------------ single pass (row statistics supplied)
+@pytest.mark.parametrize("draw", range(3))
+@pytest.mark.parametrize("scorer", ["snapkv", "lava", "criticalkv", "laprox"])
+def test_fresh_draws(gpu_lib, scorer, draw):
+    """Every scorer on three more seeded draws (the seed follows the workload
+    name), at reduced sizes with a ragged last tile."""
+    if scorer == "snapkv":
+        cfg = scaled(configs.LLAMA8B_MODEL, layers=2, batch=2, name=f"draw{draw}_snapkv")
+        run_case(cfg, 4, 1500, 8 * 120, 2, 2, f"snapkv draw {draw}")
+    elif scorer == "lava":
+        cfg = scaled(configs.MISTRAL7B_LAVA, layers=3, name=f"draw{draw}_lava")
+        run_case(cfg, 3, 1300, 3 * 8 * (32 + 60), 0, 0, f"lava draw {draw}")
+    elif scorer == "criticalkv":
+        cfg = scaled(configs.QWEN32B_CK, hidden=512, name=f"draw{draw}_ck")
+        run_case(cfg, 1, 1300, (40 * cfg.hkv * 1300) // 100, 0, 0, f"criticalkv draw {draw}")
+    else:
+        cfg = scaled(configs.MISTRAL7B_LAPROX, layers=2, hidden=512, name=f"draw{draw}_laprox")
+        run_case(cfg, 2, 1300, 2 * 32 * 8 + (2 * 8 * 1268) // 10, 0, 0, f"laprox draw {draw}")
+
+
 def test_single_pass_tiny(gpu_lib):
     cfg = configs.TINY_MHA
     run_case(cfg, 1, cfg.n, cfg.budget, cfg.reserve, cfg.decode_steps, "tiny single-pass", single_pass=True)
