@@ -26,6 +26,7 @@
 //    factor ||(V W_O)[t, :]||_2 and the product come from the V W^O kernel).
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -418,19 +419,26 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 #pragma unroll
         for (int i = 0; i < 32; ++i) ks[i] = 0.f;
         const bool interior = k0 + TILE <= p;
+        // one copy per value of the interior test (a per-logit test compiled
+        // to a scalar branch per logit)
+        auto fold = [&](auto interior_tag) {
+          constexpr bool INTERIOR = decltype(interior_tag)::value;
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-          f32x4 acc[NB];
-          logits_block<T, D, NB>(lds, mb, c, gq, qop, acc);
+          for (int mb = 0; mb < 8; ++mb) {
+            f32x4 acc[NB];
+            logits_block<T, D, NB>(lds, mb, c, gq, qop, acc);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float e = fast_exp2(fmaf(acc[nb][j], c2e, -smc[nb]));
-              if (interior) ks[4 * mb + j] = fmaf(e, sil[nb], ks[4 * mb + j]);
-              else ks[4 * mb + j] += (kbase + 4 * mb + j < p) ? e * sil[nb] : 0.f;
-            }
-        }
+              for (int j = 0; j < 4; ++j) {
+                const float e = fast_exp2(fmaf(acc[nb][j], c2e, -smc[nb]));
+                if (INTERIOR) ks[4 * mb + j] = fmaf(e, sil[nb], ks[4 * mb + j]);
+                else ks[4 * mb + j] += (kbase + 4 * mb + j < p) ? e * sil[nb] : 0.f;
+              }
+          }
+        };
+        if (interior) fold(std::true_type{});
+        else fold(std::false_type{});
         float s0, s1;
         reduce_scatter16(ks, c, s0, s1);
         hs[h * TILE + 32 * gq + 2 * c] = s0;
@@ -507,28 +515,35 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) hsum[j] = 0.f;
         const int hkey0 = (gq == 0) ? k0 - HALO : ((gq == 3) ? k0 + TILE : -1);
+        // the interior test is a compile-time constant of each copy: tested
+        // per logit, it compiled to a scalar branch per logit
+        auto fold = [&](auto interior_tag) {
+          constexpr bool INTERIOR = decltype(interior_tag)::value;
 #pragma unroll
-        for (int mb = 0; mb < 9; ++mb) {
-          f32x4 acc[NB];
-          logits_block<T, D, NB>(lds, mb, c, gq, qop, acc);
+          for (int mb = 0; mb < 9; ++mb) {
+            f32x4 acc[NB];
+            logits_block<T, D, NB>(lds, mb, c, gq, qop, acc);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int r = 16 * nb + c;
-            const int lim = min(n - 1, p + r);
-            const float mc = smc[nb], il_row = sil[nb];
+            for (int nb = 0; nb < NB; ++nb) {
+              const int r = 16 * nb + c;
+              const int lim = min(n - 1, p + r);
+              const float mc = smc[nb], il_row = sil[nb];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float e = fast_exp2(fmaf(acc[nb][j], c2, -mc));
-              if (mb < 8) {
-                if (interior) ks[4 * mb + j] = fmaf(e, il_row, ks[4 * mb + j]);
-                else ks[4 * mb + j] += (kbase + 4 * mb + j <= lim) ? e * il_row : 0.f;
-              } else {
-                const int key = hkey0 + j;
-                hsum[j] += (hkey0 >= 0 && key >= 0 && key <= lim) ? e * il_row : 0.f;
+              for (int j = 0; j < 4; ++j) {
+                const float e = fast_exp2(fmaf(acc[nb][j], c2, -mc));
+                if (mb < 8) {
+                  if (INTERIOR) ks[4 * mb + j] = fmaf(e, il_row, ks[4 * mb + j]);
+                  else ks[4 * mb + j] += (kbase + 4 * mb + j <= lim) ? e * il_row : 0.f;
+                } else {
+                  const int key = hkey0 + j;
+                  hsum[j] += (hkey0 >= 0 && key >= 0 && key <= lim) ? e * il_row : 0.f;
+                }
               }
             }
           }
-        }
+        };
+        if (interior) fold(std::true_type{});
+        else fold(std::false_type{});
         float s0, s1;
         reduce_scatter16(ks, c, s0, s1);
 #pragma unroll
