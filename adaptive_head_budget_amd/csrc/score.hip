@@ -256,44 +256,50 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
     f32x4 acc[8][NB];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) logits_block<T, D, NB>(lds, mb, c, gq, qop, acc[mb]);
-    // every key of the tile inside every row's domain: no per-key test
+    // every key of the tile inside every row's domain: no per-key test (and a
+    // finite row maximum); one copy of the fold per value of the test
     const bool full = k0 + TILE - 1 <= (CAUSAL ? min(kend - 1, p) : kend - 1);
+    auto fold = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int r = 16 * nb + c;
-      const int lim = CAUSAL ? min(kend - 1, p + r) : kend - 1;   // last key of this row's domain
-      float lm = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-          lm = fmax3(lm, fmax3(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2]), acc[mb][nb][3]);
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (k0 + 32 * gq + 4 * mb + j <= lim) lm = fmaxf(lm, acc[mb][nb][j]);
-      }
-      if (lm != -INFINITY) {
-        const float lmc = lm * c2;
-        float ls = 0.f;
-        if (full) {
+      for (int nb = 0; nb < NB; ++nb) {
+        const int r = 16 * nb + c;
+        const int lim = CAUSAL ? min(kend - 1, p + r) : kend - 1;   // last key of this row's domain
+        float lm = -INFINITY;
+        if (FULL) {
 #pragma unroll
           for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ls += fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
+            lm = fmax3(lm, fmax3(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2]), acc[mb][nb][3]);
         } else {
 #pragma unroll
           for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float e = fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
-              ls += (k0 + 32 * gq + 4 * mb + j <= lim) ? e : 0.f;
-            }
+            for (int j = 0; j < 4; ++j)
+              if (k0 + 32 * gq + 4 * mb + j <= lim) lm = fmaxf(lm, acc[mb][nb][j]);
         }
-        merge_ml(rm[nb], rl[nb], lmc, ls);
+        if (FULL || lm != -INFINITY) {
+          const float lmc = lm * c2;
+          float ls = 0.f;
+          if (FULL) {
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) ls += fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
+          } else {
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float e = fast_exp2(fmaf(acc[mb][nb][j], c2, -lmc));
+                ls += (k0 + 32 * gq + 4 * mb + j <= lim) ? e : 0.f;
+              }
+          }
+          merge_ml(rm[nb], rl[nb], lmc, ls);
+        }
       }
-    }
+    };
+    if (full) fold(std::true_type{});
+    else fold(std::false_type{});
   }
   if (!active) return;
 #pragma unroll
