@@ -365,6 +365,23 @@ __global__ __launch_bounds__(SB) void radix_pick_kernel(uint32_t* __restrict__ h
 }
 
 // ---------------------------------------------------------------- layer pass 0
+// ln of a positive normal float v = 2^e m: with m_hi = 1 + k/256 (k the top 8
+// bits of the mantissa) and m = m_hi (1 + d), 0 <= d < 2^-8,
+// ln v = e ln 2 + ln m_hi + ln(1 + d); ln m_hi and 1/m_hi come from tables, and
+// ln(1 + d) from its Taylor series up to d^7 (the rest is below 2^-56
+// relative).  m - m_hi is exact; a subnormal v takes the library ln.
+__device__ __forceinline__ double ln_float(uint32_t u, double v, const double* __restrict__ ltab,
+                                           const double* __restrict__ itab) {
+  const int ex = (int)(u >> 23);
+  if (ex == 0) return log(v);
+  const uint32_t mb = u & 0x7FFFFFu;
+  const int k = (int)(mb >> 15);
+  const double d = (double)(mb & 0x7FFFu) * 0x1p-23 * itab[k];
+  const double l1p =
+      d * (1.0 + d * (-0.5 + d * (1.0 / 3.0 + d * (-0.25 + d * (0.2 + d * (-1.0 / 6.0 + d * (1.0 / 7.0)))))));
+  return (double)(ex - 127) * 0.69314718055994530942 + ltab[k] + l1p;
+}
+
 // First digit pass of the layer-wide top-k, kept per row (the row histograms
 // also serve each head's own top-k later).  For LAVa each chunk also leaves its
 // partial sums S = sum s and Q = sum s ln s (fp64) for the layer entropy.
@@ -373,12 +390,19 @@ __global__ __launch_bounds__(SB) void layer_hist0_kernel(const float* __restrict
                                                          double* __restrict__ part, uint32_t* __restrict__ flag) {
   __shared__ uint32_t h[NBIN];
   __shared__ double dsh[2][SW];
+  __shared__ double ltab[SB], itab[SB];   // ln(1 + k/256) and 1/(1 + k/256), k < 256 (LAVa)
+  static_assert(SB == 256, "one table entry per thread");
   const Chunk ch = chunk_of(cpr, ntile, p);
   ChunkKeys K;
   uint8_t m[NK];
   load_chunk<true>(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
   if (K.bad) atomicOr(flag, 1u);   // precondition broken somewhere in the chunk
   for (int b = threadIdx.x; b < NBIN; b += SB) h[b] = 0u;
+  if (lava) {
+    const double mh = 1.0 + (double)threadIdx.x * 0x1p-8;
+    ltab[threadIdx.x] = log(mh);
+    itab[threadIdx.x] = 1.0 / mh;
+  }
   __syncthreads();
   chunk_hist(h, K, m, false, 0u, 0);
   if (lava) {
@@ -388,7 +412,7 @@ __global__ __launch_bounds__(SB) void layer_hist0_kernel(const float* __restrict
       const double v = (double)__uint_as_float(K.k[j]);
       if (j < K.n && v > 0.0) {
         S += v;
-        Q += v * log(v);
+        Q += v * ln_float(K.k[j], v, ltab, itab);
       }
     }
 #pragma unroll
