@@ -488,11 +488,21 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
   int64_t* fl = reinterpret_cast<int64_t*>(rem + L);
   __shared__ double Esh;
   __shared__ int64_t def;
-  for (int l = threadIdx.x; l < L; l += SB) {
-    double S = 0.0, Q = 0.0;
-    const double* pl = part + 2 * (size_t)l * chunks_per_layer;
-    for (int c = 0; c < chunks_per_layer; ++c) { S += pl[2 * c]; Q += pl[2 * c + 1]; }
-    rem[l] = (S > 0.0) ? (log(S) - Q / S) / ((double)hkv * (double)p) : 0.0;
+  // one wave per layer: lane-strided sums over the layer's chunk partials,
+  // then a fixed butterfly (the same order on every run)
+  {
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    for (int l = wv; l < L; l += SW) {
+      double S = 0.0, Q = 0.0;
+      const double* pl = part + 2 * (size_t)l * chunks_per_layer;
+      for (int c = lane; c < chunks_per_layer; c += WAVE) { S += pl[2 * c]; Q += pl[2 * c + 1]; }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        S += __shfl_xor(S, off);
+        Q += __shfl_xor(Q, off);
+      }
+      if (lane == 0) rem[l] = (S > 0.0) ? (log(S) - Q / S) / ((double)hkv * (double)p) : 0.0;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
