@@ -7,7 +7,7 @@ the smaller flat index g*p + k (within one head: the smaller token index).
 from __future__ import annotations
 
 import math
-from typing import Dict, List, Sequence, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -115,24 +115,41 @@ def lava_layer_budgets(scores: np.ndarray, total: int, w: int) -> Tuple[np.ndarr
     return largest_remainder(x, Bp), e
 
 
-def lava_allocate(scores: np.ndarray, total: int, w: int) -> Dict:
+def lava_allocate(scores: np.ndarray, total: int, w: int, layer_budgets: np.ndarray | None = None) -> Dict:
     """LAVa layer-wise eviction with dynamic head budgets.
 
     LAVa notes, "动态头预算的逐层缓存驱逐": the scores of all heads in a layer
     are flattened into one array and the layer's B_l best entries are kept, so
     head budgets follow from the ranking; no safeguard is applied.
+    layer_budgets: the B_l to use instead of the entropy split (the selection
+    step alone, e.g. under another device's split of a float64 near-tie); they
+    must sum to B' = total - L*w*Hkv, each within [0, Hkv*p].
     Returns dict with layer budgets, e, per-layer head budgets [L, Hkv], sel[l][g].
     """
     scores = np.asarray(scores, dtype=np.float64)
     L, hkv, p = scores.shape
     bl, e = lava_layer_budgets(scores, total, w)
+    if layer_budgets is not None:
+        bl = np.asarray(layer_budgets, dtype=np.int64)
+        if bl.shape != (L,) or int(bl.sum()) != int(total) - L * w * hkv or (bl < 0).any() or (bl > hkv * p).any():
+            raise ValueError("layer budgets must be L values in [0, Hkv*p] summing to B'")
+    budgets, sel = layer_top_select(scores, bl)
+    return {"layer_budgets": bl, "entropy": e, "budgets": budgets, "sel": sel}
+
+
+def layer_top_select(scores: np.ndarray, layer_budgets: Sequence[int]):
+    """Each layer keeps the top B_l of its flattened [Hkv, p] scores, ranked by
+    (-score, g*p + t) (LAVa notes, "动态头预算的逐层缓存驱逐"); the head budgets
+    are the per-head counts.  Returns (budgets [L, Hkv], sel[l][g] ascending)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    L, hkv, p = scores.shape
     budgets = np.zeros((L, hkv), dtype=np.int64)
     sel: List[List[np.ndarray]] = []
     for l in range(L):
-        top = top_indices(scores[l].ravel(), int(bl[l]))
+        top = top_indices(scores[l].ravel(), int(layer_budgets[l]))
         budgets[l] = np.bincount(top // p, minlength=hkv)
         sel.append([np.sort(top[top // p == g] % p) for g in range(hkv)])
-    return {"layer_budgets": bl, "entropy": e, "budgets": budgets, "sel": sel}
+    return budgets, sel
 
 
 def criticalkv_allocate(score: np.ndarray, composite: np.ndarray, budget: int, w: int,
@@ -269,22 +286,28 @@ def lava_online_steps(scores: np.ndarray, total: int, w: int) -> List[Dict]:
     L, hkv, p = scores.shape
     if int(total) < L * w * hkv:
         raise ValueError("total budget smaller than the windows")
-    e = np.array([layer_entropy(scores[j]) for j in range(L)])
-    prev = np.zeros(0, dtype=np.int64)
     steps = []
+    prev = np.zeros(0, dtype=np.int64)
     for l in range(L):
-        Bp = int(total) - (l + 1) * w * hkv
-        E = e[:l + 1].sum()
-        x = Bp * e[:l + 1] / E if E > 0 else np.full(l + 1, Bp / (l + 1))
-        split = largest_remainder(x, Bp)
-        cap = np.concatenate([prev, [hkv * p]])
-        lb = np.minimum(split, cap)
-        budgets = np.zeros((l + 1, hkv), dtype=np.int64)
-        sel = []
-        for j in range(l + 1):
-            top = top_indices(scores[j].ravel(), int(lb[j]))
-            budgets[j] = np.bincount(top // p, minlength=hkv)
-            sel.append([np.sort(top[top // p == g] % p) for g in range(hkv)])
-        steps.append({"layer_budgets": lb, "split": split, "budgets": budgets, "sel": sel, "Bp": Bp})
-        prev = lb
+        st = lava_online_step(scores[:l + 1], total, w, prev)
+        steps.append(st)
+        prev = st["layer_budgets"]
     return steps
+
+
+def lava_online_step(scores: np.ndarray, total: int, w: int, prev: Sequence[int]) -> Dict:
+    """One step of lava_online_steps: the I = l + 1 layers present (scores
+    [I, Hkv, p]) share B'(l) = total - I*w*Hkv by the entropy split, each
+    capped by its budget of the previous step (`prev`, I - 1 values; Hkv*p for
+    the newest layer), then each keeps its flattened top B_j."""
+    scores = np.asarray(scores, dtype=np.float64)
+    I, hkv, p = scores.shape
+    e = np.array([layer_entropy(scores[j]) for j in range(I)])
+    Bp = int(total) - I * w * hkv
+    E = e.sum()
+    x = Bp * e / E if E > 0 else np.full(I, Bp / I)
+    split = largest_remainder(x, Bp)
+    cap = np.concatenate([np.asarray(prev, dtype=np.int64), [hkv * p]])
+    lb = np.minimum(split, cap)
+    budgets, sel = layer_top_select(scores, lb)
+    return {"layer_budgets": lb, "split": split, "budgets": budgets, "sel": sel, "Bp": Bp, "entropy": e}

@@ -97,11 +97,41 @@ def jaccard(a_sel, b_sel):
     return inter / union if union else 1.0
 
 
-def near_tie_in_layer_split(e: np.ndarray, Bp: int) -> bool:
-    """True when the largest-remainder split of B' * e / sum(e) is decided by
-    remainders closer than 1e-9 (float64 order differences can flip it)."""
+def near_tie_in_layer_split(e: np.ndarray, Bp: int, tol: float = 1e-9) -> bool:
+    """True when the largest-remainder split of B' * e / sum(e) can be changed
+    by float64 rounding differences of size `tol`: some share lies within tol of
+    an integer (its floor can flip), or the remainders at the cut-off rank (the
+    last one given an extra unit and the first one not) are within tol of each
+    other.  Remainder ties elsewhere decide nothing."""
+    e = np.asarray(e, dtype=np.float64)
     E = e.sum()
     x = Bp * e / E if E > 0 else np.full(e.size, Bp / e.size)
-    fr = np.sort(x - np.floor(x))[::-1]
-    dif = np.abs(np.diff(fr))
-    return bool((dif < 1e-9).any() or (np.abs(fr - 0.5) < 1e-9).any())
+    fl = np.floor(x)
+    fr = x - fl
+    if (np.minimum(fr, 1.0 - fr) < tol).any():
+        return True
+    deficit = int(round(Bp - fl.sum()))
+    if 0 < deficit < e.size:
+        srt = np.sort(fr)[::-1]
+        return bool(srt[deficit - 1] - srt[deficit] < tol)
+    return False
+
+
+def check_lava_layer_budgets(gpu_lb, ref_lb, e, Bp, what, same_sum: bool = True) -> bool:
+    """The device's LAVa layer budgets against the oracle's split.  Equal: True.
+    Different: only allowed at a float64 near-tie of the split, and then the
+    device's budgets must still be a valid split (non-negative, summing to B',
+    each within one unit of the oracle's; with same_sum=False, as under the
+    online prefill's caps, the sums may differ); returns False so the caller
+    checks the selections under the device's own budgets."""
+    gpu_lb = np.asarray(gpu_lb, dtype=np.int64)
+    ref_lb = np.asarray(ref_lb, dtype=np.int64)
+    if np.array_equal(gpu_lb, ref_lb):
+        return True
+    assert near_tie_in_layer_split(e, Bp), f"{what}: layer budgets {gpu_lb} vs {ref_lb} with no near-tie"
+    assert (gpu_lb >= 0).all() and (not same_sum or int(gpu_lb.sum()) == int(ref_lb.sum())), \
+        f"{what}: invalid layer budgets"
+    assert np.abs(gpu_lb - ref_lb).max() <= 1, f"{what}: layer budgets differ by more than one unit"
+    log(f"  {what}: layer budgets differ at a float64 near-tie (layers "
+        f"{np.flatnonzero(gpu_lb != ref_lb).tolist()}); selections checked under the device's budgets")
+    return False

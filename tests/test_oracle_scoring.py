@@ -340,3 +340,128 @@ def _laprox_l1_values(q_win, k, v, w_o):
 def test_laprox_pins_catch_planted_mistakes():
     assert not check_laprox_is_frobenius_norm(_laprox_causal)
     assert not check_laprox_uniform_closed_form(_laprox_l1_values)
+
+
+# ---------------------------------------------------------------- CriticalKV composite, entry by entry
+def _loop_composite(q, k, v, w_o, pool, eps):
+    """The CriticalKV composite written out with explicit loops, sharing nothing
+    with the oracle's scorer: for query head i of KV head g and prefix token t,
+    A_i[t] = mean over window rows of the max pooled softmax weight (math.exp,
+    the pooling window cut at the prefix ends), nrm_i[t] = sum over output
+    features c of |sum over e of V[g,t,e] W^O[i*d+e, c]|, and the KV head takes
+    the mean over its query heads of (A_i[t] + eps) * nrm_i[t]
+    (CriticalKV notes, "两阶段贪心选择算法"; GQA by the group mean)."""
+    hq, w, d = q.shape
+    hkv, n, _ = k.shape
+    D = w_o.shape[1]
+    G = hq // hkv
+    p = n - w
+    rho = (pool - 1) // 2
+    out = [[0.0] * p for _ in range(hkv)]
+    for i in range(hq):
+        g = i // G
+        wts = []
+        for r in range(w):
+            z = [sum(q[i, r, e] * k[g, t, e] for e in range(d)) / math.sqrt(d) for t in range(p)]
+            m = max(z)
+            ex = [math.exp(x - m) for x in z]
+            s = sum(ex)
+            wts.append([x / s for x in ex])
+        for t in range(p):
+            a = 0.0
+            for r in range(w):
+                a += max(wts[r][u] for u in range(max(0, t - rho), min(p, t + rho + 1)))
+            a /= w
+            nrm = 0.0
+            for c in range(D):
+                nrm += abs(sum(v[g, t, e] * w_o[i * d + e, c] for e in range(d)))
+            out[g][t] += (a + eps) * nrm / G
+    return np.array(out)
+
+
+def check_criticalkv_composite(fn) -> bool:
+    """fn(q, k, v, w_o, pool, eps) -> composite [Hkv, p] must equal the loop
+    form on a tiny GQA case (G = 2, pool 3, D != d so a transposed W^O shows),
+    at a small and at a large epsilon."""
+    r = rng(51)
+    hq, hkv, w, d, n, D = 4, 2, 3, 4, 13, 6
+    q = r.standard_normal((hq, w, d)) * 1.5
+    k = r.standard_normal((hkv, n, d))
+    v = r.standard_normal((hkv, n, d))
+    w_o = r.standard_normal((hq * d, D))
+    for eps in (1e-6, 0.25):
+        ref = _loop_composite(q, k, v, w_o, 3, eps)
+        if not np.allclose(fn(q, k, v, w_o, 3, eps), ref, rtol=1e-12, atol=0.0):
+            return False
+    return True
+
+
+def _oracle_composite(q, k, v, w_o, pool, eps):
+    return scoring.criticalkv_scores(q, k, v, w_o, pool, eps)[1]
+
+
+def _ck_eps_outside(q, k, v, w_o, pool, eps):
+    """Planted: A * nrm + eps instead of (A + eps) * nrm."""
+    hkv = k.shape[0]
+    a = scoring.snapkv_head_scores(q, k, pool)
+    nrm = scoring.projected_value_norms(v, w_o, q.shape[0], slice(0, a.shape[1]))
+    return scoring.group_mean(a * nrm + eps, hkv)
+
+
+def _ck_unpooled_attention(q, k, v, w_o, pool, eps):
+    """Planted: the attention factor without max pooling."""
+    hkv = k.shape[0]
+    a = scoring.snapkv_head_scores(q, k, 1)
+    nrm = scoring.projected_value_norms(v, w_o, q.shape[0], slice(0, a.shape[1]))
+    return scoring.group_mean((a + eps) * nrm, hkv)
+
+
+def _ck_group_first(q, k, v, w_o, pool, eps):
+    """Planted: (group-mean A + eps) * group-mean nrm (the alternative GQA rule)."""
+    hkv = k.shape[0]
+    a = scoring.snapkv_head_scores(q, k, pool)
+    nrm = scoring.projected_value_norms(v, w_o, q.shape[0], slice(0, a.shape[1]))
+    return (scoring.group_mean(a, hkv) + eps) * scoring.group_mean(nrm, hkv)
+
+
+def _ck_group_block(q, k, v, w_o, pool, eps):
+    """Planted: every head of a group projected with its group's first W^O block."""
+    hq, w, d = q.shape
+    hkv = k.shape[0]
+    G = hq // hkv
+    a = scoring.snapkv_head_scores(q, k, pool)
+    p = a.shape[1]
+    nrm = np.stack([np.abs(v[i // G, :p] @ w_o[(i // G) * G * d:((i // G) * G + 1) * d]).sum(axis=1)
+                    for i in range(hq)])
+    return scoring.group_mean((a + eps) * nrm, hkv)
+
+
+def test_criticalkv_composite_entry_by_entry():
+    assert check_criticalkv_composite(_oracle_composite)
+
+
+def check_criticalkv_closed_form(fn) -> bool:
+    """Constant keys: every pooled weight is 1/p; with W^O_i = c_i * I (D = d)
+    nrm_i = c_i ||V_g[t]||_1, so the KV head's composite is
+    (1/p + eps) * mean_i(c_i) * ||V_g[t]||_1."""
+    r = rng(52)
+    hq, hkv, w, d, n = 4, 2, 3, 8, 21
+    q = r.standard_normal((hq, w, d))
+    k = np.broadcast_to(r.standard_normal((hkv, 1, d)), (hkv, n, d)).copy()
+    v = r.standard_normal((hkv, n, d))
+    c = np.array([0.5, 2.0, 3.0, 7.0])
+    w_o = np.concatenate([c[i] * np.eye(d) for i in range(hq)], axis=0)
+    p = n - w
+    eps = 0.125
+    ref = np.stack([(1.0 / p + eps) * c[2 * g:2 * g + 2].mean() * np.abs(v[g, :p]).sum(axis=1) for g in range(hkv)])
+    return bool(np.allclose(fn(q, k, v, w_o, 5, eps), ref, rtol=1e-13, atol=0.0))
+
+
+def test_criticalkv_composite_closed_form():
+    assert check_criticalkv_closed_form(_oracle_composite)
+
+
+def test_criticalkv_pins_catch_planted_mistakes():
+    for planted in (_ck_eps_outside, _ck_unpooled_attention, _ck_group_first, _ck_group_block):
+        assert not check_criticalkv_composite(planted), planted.__name__
+    assert not check_criticalkv_closed_form(_ck_eps_outside)
