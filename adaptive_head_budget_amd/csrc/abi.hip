@@ -224,11 +224,11 @@ adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, c
                                    seg_len, static_cast<hipStream_t>(stream)));
 }
 
-adakv_status adakv_decode_attn(const adakv_shape* shape, const adakv_alloc* alloc, const void* q, const void* k_new,
-                               const void* v_new, void* k_flat, void* v_flat, const int64_t* seg_start,
-                               const int32_t* seg_len, int32_t reserve, int32_t step, float* out, void* ws,
-                               size_t ws_bytes, void* stream) {
-  Geo g{};
+namespace {
+// Argument checks shared by both decode entry points; fills g and the row count.
+adakv_status check_decode(const adakv_shape* shape, const adakv_alloc* alloc, const void* q, const void* k_new,
+                          const void* v_new, void* k_flat, void* v_flat, const int64_t* seg_start,
+                          const int32_t* seg_len, int32_t reserve, int32_t step, float* out, Geo& g, int64_t& rows) {
   adakv_status st = check_shape(shape, g);
   if (st != ADAKV_OK) return st;
   st = check_alloc(alloc, g);
@@ -236,15 +236,47 @@ adakv_status adakv_decode_attn(const adakv_shape* shape, const adakv_alloc* allo
   if (reserve < 0 || step < 0) return ADAKV_EINVAL;
   if ((k_new == nullptr) != (v_new == nullptr)) return ADAKV_EINVAL;
   if (!aligned16(q) || !aligned16(k_flat) || !aligned16(v_flat) || !aligned16(seg_start) || !aligned16(seg_len) ||
-      !aligned16(out) || !aligned16(ws))
+      !aligned16(out))
     return ADAKV_EINVAL;
   if (k_new != nullptr && (!aligned16(k_new) || !aligned16(v_new))) return ADAKV_EINVAL;
   if (g.G > 8) return ADAKV_EUNSUPPORTED;
   const bool append = k_new != nullptr;
   if (append && step >= reserve) return ADAKV_ECAPACITY;
   if (!append && step > reserve) return ADAKV_EINVAL;
-  const int64_t rows = selected_rows(*alloc, g) + (int64_t)g.I * g.hkv * ((int64_t)g.w + step + (append ? 1 : 0));
+  rows = selected_rows(*alloc, g) + (int64_t)g.I * g.hkv * ((int64_t)g.w + step + (append ? 1 : 0));
+  return ADAKV_OK;
+}
+}  // namespace
+
+adakv_status adakv_decode_attn_noalloc(const adakv_shape* shape, const adakv_alloc* alloc, const void* q,
+                                       const void* k_new, const void* v_new, void* k_flat, void* v_flat,
+                                       const int64_t* seg_start, const int32_t* seg_len, int32_t reserve,
+                                       int32_t step, float* out, void* stream) {
+  Geo g{};
+  int64_t rows = 0;
+  adakv_status st = check_decode(shape, alloc, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, reserve, step,
+                                 out, g, rows);
+  if (st != ADAKV_OK) return st;
+  if (decode_ws_bytes(g, rows) > decode_scratch_capacity()) return ADAKV_EWORKSPACE;
+  void* scratch = nullptr;
+  if (decode_scratch(&scratch) != hipSuccess) return ADAKV_EHIP;
+  const bool append = k_new != nullptr;
+  return hip_status(launch_decode(g, rows, step + (append ? 1 : 0), q, k_new, v_new, k_flat, v_flat, seg_start,
+                                  seg_len, out, static_cast<char*>(scratch), static_cast<hipStream_t>(stream)));
+}
+
+adakv_status adakv_decode_attn(const adakv_shape* shape, const adakv_alloc* alloc, const void* q, const void* k_new,
+                               const void* v_new, void* k_flat, void* v_flat, const int64_t* seg_start,
+                               const int32_t* seg_len, int32_t reserve, int32_t step, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  Geo g{};
+  int64_t rows = 0;
+  adakv_status st = check_decode(shape, alloc, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, reserve, step,
+                                 out, g, rows);
+  if (st != ADAKV_OK) return st;
+  if (!aligned16(ws)) return ADAKV_EINVAL;
   if (ws_bytes < decode_ws_bytes(g, rows)) return ADAKV_EWORKSPACE;
+  const bool append = k_new != nullptr;
   return hip_status(launch_decode(g, rows, step + (append ? 1 : 0), q, k_new, v_new, k_flat, v_flat, seg_start,
                                   seg_len, out, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
 }

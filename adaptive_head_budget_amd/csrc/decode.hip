@@ -17,6 +17,8 @@
 // k_new/v_new and also stored into the segment's reserved rows for later steps;
 // seg_len is never modified (a call attends over seg_len + step (+1) rows), so
 // a decode call carries no state from the previous one.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -297,7 +299,37 @@ hipError_t run_decode_g(const Geo& g, int64_t max_rows, int extra, const void* q
 #undef RUN
 }
 
+// Split partials of adakv_decode_attn_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code reaches it only
+// through the address hipGetSymbolAddress returns for the current device (the
+// array's name is a host-side stand-in, not a device address).
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+__device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+size_t decode_scratch_capacity() { return kDecodeScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t decode_ws_bytes(const Geo& g, int64_t max_rows) {
   const int S = g.I * g.hkv;

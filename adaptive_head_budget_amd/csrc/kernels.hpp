@@ -60,6 +60,10 @@ hipError_t launch_online_compact(const Geo& g, int64_t max_rows, const void* k_n
 
 // ---- decode (decode.hip)
 size_t decode_ws_bytes(const Geo& g, int64_t max_rows);
+// The allocation-free decode's scratch: the calling device's copy of a fixed
+// file-scope array (its address is looked up once per device).
+size_t decode_scratch_capacity();
+hipError_t decode_scratch(void** ptr);
 // extra = appends made before this call + 1 if this call appends
 hipError_t launch_decode(const Geo& g, int64_t max_rows, int extra, const void* q, const void* k_new,
                          const void* v_new, void* k_flat, void* v_flat, const int64_t* seg_start,

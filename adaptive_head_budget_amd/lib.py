@@ -22,8 +22,8 @@ ADAKV_SCORE_SNAPKV, ADAKV_SCORE_LAVA, ADAKV_SCORE_CRITICALKV, ADAKV_SCORE_LAPROX
  ADAKV_ALLOC_STREAMING) = range(6)
 
 EXPORTS = ("adakv_workspace_bytes", "adakv_score", "adakv_score_lse", "adakv_allocate", "adakv_compact",
-           "adakv_decode_attn", "adakv_strerror", "adakv_version", "adakv_lava_online_allocate",
-           "adakv_lava_online_compact")
+           "adakv_decode_attn", "adakv_decode_attn_noalloc", "adakv_strerror", "adakv_version",
+           "adakv_lava_online_allocate", "adakv_lava_online_compact")
 
 
 class AdakvShape(ctypes.Structure):
@@ -72,6 +72,9 @@ def load(path: Optional[str] = None):
     lib.adakv_decode_attn.argtypes = [S, A, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
                                       _vp, _vp, ctypes.c_size_t, _vp]
     lib.adakv_decode_attn.restype = ctypes.c_int
+    lib.adakv_decode_attn_noalloc.argtypes = [S, A, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                              ctypes.c_int32, _vp, _vp]
+    lib.adakv_decode_attn_noalloc.restype = ctypes.c_int
     lib.adakv_lava_online_allocate.argtypes = [S, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.adakv_lava_online_allocate.restype = ctypes.c_int
     lib.adakv_lava_online_compact.argtypes = [S, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
@@ -156,6 +159,14 @@ def adakv_decode_attn(shape, alloc, q, k_new, v_new, k_flat, v_flat, seg_start, 
                                   _p(k_flat), _p(v_flat), _p(seg_start), _p(seg_len), reserve, step, _p(out),
                                   _p(ws), _nbytes(ws), _stream(stream))
     _check(st, "adakv_decode_attn")
+
+
+def adakv_decode_attn_noalloc(shape, alloc, q, k_new, v_new, k_flat, v_flat, seg_start, seg_len, reserve, step, out,
+                              stream=None):
+    st = load().adakv_decode_attn_noalloc(ctypes.byref(shape), ctypes.byref(alloc), _p(q), _p(k_new), _p(v_new),
+                                          _p(k_flat), _p(v_flat), _p(seg_start), _p(seg_len), reserve, step, _p(out),
+                                          _stream(stream))
+    _check(st, "adakv_decode_attn_noalloc")
 
 
 def adakv_lava_online_allocate(shape, total_budget, score, prev_sel_off, budgets, sel, sel_off, ws, stream=None):

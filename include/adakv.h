@@ -8,6 +8,7 @@
  *   adakv_allocate     layer-wide top-B -> per-head budgets -> per-head selection
  *   adakv_compact      selected rows + window rows -> one flat variable-length cache
  *   adakv_decode_attn  decode attention over the flat cache (optional append)
+ *   adakv_decode_attn_noalloc  the same without a workspace argument
  *   adakv_lava_online_allocate / adakv_lava_online_compact
  *                      LAVa's layer-by-layer prefill with re-compression
  *
@@ -325,6 +326,26 @@ adakv_status adakv_decode_attn(const adakv_shape* shape, const adakv_alloc* allo
                                const void* k_new, const void* v_new, void* k_flat, void* v_flat,
                                const int64_t* seg_start, const int32_t* seg_len, int32_t reserve, int32_t step,
                                float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* adakv_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and checks as
+ * adakv_decode_attn; the split partials that adakv_decode_attn keeps in `ws`
+ * live instead in a fixed device array inside the library, one copy per GPU
+ * (8 MiB, held until the process ends; its address is looked up on the first
+ * call on each device).  Nothing is allocated or freed by this call.
+ *   - A shape whose partials would not fit returns ADAKV_EWORKSPACE (with the
+ *     current split rule every supported shape fits: at most about 6.4 MB).
+ *   - Every call on a GPU shares that GPU's array: calls that may overlap on
+ *     one device (two streams, two host threads) race and must be ordered by
+ *     the caller.  Each call writes every partial it reads, so nothing needs
+ *     clearing between calls.
+ *   - Errors: as adakv_decode_attn; ADAKV_EHIP also when the array's address
+ *     cannot be obtained on the current device. */
+adakv_status adakv_decode_attn_noalloc(const adakv_shape* shape, const adakv_alloc* alloc, const void* q,
+                                       const void* k_new, const void* v_new, void* k_flat, void* v_flat,
+                                       const int64_t* seg_start, const int32_t* seg_len, int32_t reserve,
+                                       int32_t step, float* out, void* stream);
 
 /* A short, static description of a status code. */
 const char* adakv_strerror(adakv_status status);

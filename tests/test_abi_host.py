@@ -180,6 +180,24 @@ def test_decode_rejects(L):
     assert dec(FAKE, FAKE, 2, 0, shape=_shape(hq=80, hkv=8)) == lib.ADAKV_EUNSUPPORTED
 
 
+def test_decode_noalloc_rejects(L):
+    """The allocation-free decode validates exactly as adakv_decode_attn
+    (before it touches the device)."""
+    s, a = _shape(), _alloc()
+
+    def dec(k_new, v_new, reserve, step, shape=s):
+        return L.adakv_decode_attn_noalloc(ctypes.byref(shape), ctypes.byref(a), FAKE, k_new, v_new, FAKE, FAKE,
+                                           FAKE, FAKE, reserve, step, FAKE, None)
+    assert dec(FAKE, FAKE, 2, 2) == lib.ADAKV_ECAPACITY
+    assert dec(FAKE, None, 2, 0) == lib.ADAKV_EINVAL
+    assert dec(None, None, 2, 3) == lib.ADAKV_EINVAL
+    assert dec(FAKE, FAKE, 2, 0, shape=_shape(hq=80, hkv=8)) == lib.ADAKV_EUNSUPPORTED
+    assert L.adakv_decode_attn_noalloc(None, ctypes.byref(a), FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 2, 0, FAKE,
+                                       None) == lib.ADAKV_EINVAL
+    assert L.adakv_decode_attn_noalloc(ctypes.byref(s), ctypes.byref(a), FAKE + 4, None, None, FAKE, FAKE, FAKE,
+                                       FAKE, 2, 0, FAKE, None) == lib.ADAKV_EINVAL
+
+
 def test_no_undefined_kernel_stubs(L):
     """Every kernel launched from host code has its host-side stub in the
     library (a stub can silently go missing when a device-only construct is
