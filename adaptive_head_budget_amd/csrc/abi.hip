@@ -53,9 +53,16 @@ adakv_status check_alloc(const adakv_alloc* a, const Geo& g) {
     if ((int64_t)g.I * g.hkv * g.p > (int64_t)INT32_MAX) return ADAKV_EUNSUPPORTED;
   } else {
     if (a->alpha_den <= 0 || a->alpha_num < 0 || a->alpha_num > a->alpha_den) return ADAKV_EINVAL;
-    if (a->budget < (int64_t)g.w * g.hkv || a->budget > (int64_t)g.n * g.hkv) return ADAKV_EINVAL;
+    if (a->inst_budget == nullptr && (a->budget < (int64_t)g.w * g.hkv || a->budget > (int64_t)g.n * g.hkv))
+      return ADAKV_EINVAL;
     // the safeguard numerator a*h*f + (b-a)*P stays far inside int64
     if ((int64_t)a->alpha_den > ((int64_t)1 << 20)) return ADAKV_EUNSUPPORTED;
+  }
+  if (a->inst_budget != nullptr) {
+    // per-instance budgets (preset layer budgets): Ada-KV allocation only
+    if (a->mode != ADAKV_ALLOC_ADA) return ADAKV_EUNSUPPORTED;
+    for (int i = 0; i < g.I; ++i)
+      if (a->inst_budget[i] < (int64_t)g.w * g.hkv || a->inst_budget[i] > (int64_t)g.n * g.hkv) return ADAKV_EINVAL;
   }
   if (a->mode == ADAKV_ALLOC_STREAMING && a->sinks < 0) return ADAKV_EINVAL;
   if (a->mode == ADAKV_ALLOC_ADA_CRITICALKV) {
@@ -68,6 +75,11 @@ adakv_status check_alloc(const adakv_alloc* a, const Geo& g) {
 // Rows the selection keeps over all instances (window rows excluded).
 int64_t selected_rows(const adakv_alloc& a, const Geo& g) {
   if (a.mode == ADAKV_ALLOC_LAVA_LAYERS || a.mode == ADAKV_ALLOC_GLOBAL) return a.budget - (int64_t)g.I * g.w * g.hkv;
+  if (a.inst_budget != nullptr) {
+    int64_t s = 0;
+    for (int i = 0; i < g.I; ++i) s += a.inst_budget[i] - (int64_t)g.w * g.hkv;
+    return s;
+  }
   return (int64_t)g.I * (a.budget - (int64_t)g.w * g.hkv);
 }
 

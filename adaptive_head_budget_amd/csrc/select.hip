@@ -587,8 +587,10 @@ __global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict
 //    the first digit pick of that top-k from the row's pass-0 histogram;
 //  * LAVa: B_g = f_g; the row keeps the layer threshold with its share of the ties.
 // Every workgroup of an instance computes the same head values.
-__global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int kP, int alpha_num, int alpha_den,
+__global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int kP0, int alpha_num, int alpha_den,
                                                         int ck_num, int ck_den, int n_inst,
+                                                        const int64_t* __restrict__ klist,
+                                                        const int64_t* __restrict__ kbase,
                                                         const RState* __restrict__ seg,
                                                         const uint32_t* __restrict__ cnt,
                                                         uint32_t* __restrict__ rowhist, int32_t* __restrict__ budgets,
@@ -599,6 +601,10 @@ __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int k
   __shared__ int64_t k1_sh, def_sh;
   const int r = blockIdx.x, inst = r / hkv, g = r % hkv, r0 = inst * hkv;
   const RState L = seg[inst];
+  // this instance's prefix budget and first position in sel (per-instance
+  // budgets: klist / kbase; else the same P for every instance)
+  const int64_t kP = klist ? klist[inst] : (int64_t)kP0;
+  const int64_t kb0 = kbase ? kbase[inst] : (int64_t)inst * kP0;
   for (int j = threadIdx.x; j < hkv; j += SB) {
     gt_sh[j] = cnt[2 * (size_t)(r0 + j)];
     eq_sh[j] = cnt[2 * (size_t)(r0 + j) + 1];
@@ -632,7 +638,7 @@ __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int k
   // plus one unit to the P - sum(floor) largest remainders (lower head first).
   const int64_t a = alpha_num, b = alpha_den, h = hkv;
   for (int j = threadIdx.x; j < hkv; j += SB) {
-    const int64_t num = a * h * f_sh[j] + (b - a) * (int64_t)kP;
+    const int64_t num = a * h * f_sh[j] + (b - a) * kP;
     const int64_t den = b * h;
     q_sh[j] = num / den;
     r_sh[j] = num % den;
@@ -641,7 +647,7 @@ __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int k
   if (threadIdx.x == 0) {
     int64_t sq = 0;
     for (int j = 0; j < hkv; ++j) sq += q_sh[j];
-    def_sh = (int64_t)kP - sq;
+    def_sh = kP - sq;
   }
   __syncthreads();
   for (int j = threadIdx.x; j < hkv; j += SB) {
@@ -651,7 +657,7 @@ __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int k
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int64_t base = (int64_t)inst * kP;
+    int64_t base = kb0;
     for (int j = 0; j < g; ++j) base += f_sh[j];
     const int64_t Bg = f_sh[g];
     const int64_t k1 = (mode == MODE_CK) ? (Bg * ck_num) / ck_den : Bg;
@@ -660,8 +666,8 @@ __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int k
     if (mode == MODE_CK) rowk2[r] = (int32_t)(Bg - k1);
     k1_sh = k1;
     if (g == 0) {
-      sel_off[inst] = (int64_t)inst * kP;
-      if (inst == n_inst - 1) sel_off[n_inst] = (int64_t)n_inst * kP;
+      sel_off[inst] = kb0;
+      if (inst == n_inst - 1) sel_off[n_inst] = kb0 + kP;
     }
   }
   __syncthreads();
@@ -734,6 +740,26 @@ __global__ __launch_bounds__(SB) void streaming_kernel(int hkv, int n_inst, int 
     if (g == 0) sel_off[inst] = (int64_t)inst * kP;
     if (r == hkv * n_inst - 1) sel_off[n_inst] = (int64_t)n_inst * kP;
   }
+}
+
+// Per-instance budgets handed over as kernel arguments (so the call stays
+// free of host-to-device copies and can be captured): instances [i0, i0 + n)
+// take prefix budget P[t] and first position base[t] in sel; the last chunk
+// also writes the total.
+constexpr int PRESET_CHUNK = 64;
+struct PresetArgs {
+  int64_t P[PRESET_CHUNK];
+  int64_t base[PRESET_CHUNK];
+  int64_t total;
+  int i0, n, last;
+};
+__global__ void preset_budget_kernel(PresetArgs a, int64_t* __restrict__ klist, int64_t* __restrict__ kbase) {
+  const int t = threadIdx.x;
+  if (t < a.n) {
+    klist[a.i0 + t] = a.P[t];
+    kbase[a.i0 + t] = a.base[t];
+  }
+  if (a.last && t == 0) kbase[a.i0 + a.n] = a.total;
 }
 
 // ---------------------------------------------------------------- per-chunk counts and emission
@@ -863,7 +889,7 @@ __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ scor
 struct AllocPlan {
   int R, cpr, ntile, nchunk;
   size_t off_flag, off_rowhist, off_seghist, off_cnt, zero_end;
-  size_t off_seg, off_row, off_row2, off_rowk2, off_rowbase, off_cc, off_member, off_part, off_klist, total;
+  size_t off_seg, off_row, off_row2, off_rowk2, off_rowbase, off_cc, off_member, off_part, off_klist, off_kbase, total;
 };
 
 AllocPlan plan_alloc(const Geo& g, const adakv_alloc& a) {
@@ -892,6 +918,7 @@ AllocPlan plan_alloc(const Geo& g, const adakv_alloc& a) {
   P.off_part = off;
   if (a.mode == ADAKV_ALLOC_LAVA_LAYERS) off = align_up(off + (size_t)P.nchunk * 16, 256);
   P.off_klist = off;    off = align_up(off + (size_t)g.I * 8, 256);
+  P.off_kbase = off;    off = align_up(off + (size_t)(g.I + 1) * 8, 256);
   P.total = off;
   return P;
 }
@@ -931,6 +958,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   uint8_t* member = reinterpret_cast<uint8_t*>(ws + P.off_member);
   double* part = reinterpret_cast<double*>(ws + P.off_part);
   int64_t* klist = reinterpret_cast<int64_t*>(ws + P.off_klist);
+  int64_t* kbase = reinterpret_cast<int64_t*>(ws + P.off_kbase);
 
   const bool vec1 = (g.p % 4 == 0) && (reinterpret_cast<uintptr_t>(score) % 16 == 0);
   const bool vec2 = (g.p % 4 == 0) && (reinterpret_cast<uintptr_t>(score2) % 16 == 0);
@@ -938,8 +966,9 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   const bool lava = a.mode == ADAKV_ALLOC_LAVA_LAYERS;
   const bool ck = a.mode == ADAKV_ALLOC_ADA_CRITICALKV;
   const int mode = lava ? MODE_LAVA : (ck ? MODE_CK : MODE_ADA);
-  const int kP = lava ? 0 : (int)(a.budget - (int64_t)g.w * g.hkv);
-  const int64_t sel_total = lava ? a.budget - (int64_t)g.I * g.w * g.hkv : (int64_t)g.I * kP;
+  const bool preset = a.inst_budget != nullptr;   // per-instance budgets (Ada-KV mode only)
+  const int kP = (lava || preset) ? 0 : (int)(a.budget - (int64_t)g.w * g.hkv);
+  int64_t sel_total = lava ? a.budget - (int64_t)g.I * g.w * g.hkv : (int64_t)g.I * kP;
 
   {
     const size_t n16 = P.zero_end / 16;
@@ -994,6 +1023,24 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
                                    nullptr);
     return hipGetLastError();
   }
+  if (preset) {
+    // the instances' prefix budgets P_i = B_i - w*hkv and their offsets in sel
+    int64_t run = 0;
+    for (int i0 = 0; i0 < g.I; i0 += PRESET_CHUNK) {
+      PresetArgs pa{};
+      pa.i0 = i0;
+      pa.n = std::min(PRESET_CHUNK, g.I - i0);
+      for (int t = 0; t < pa.n; ++t) {
+        pa.P[t] = a.inst_budget[i0 + t] - (int64_t)g.w * g.hkv;
+        pa.base[t] = run;
+        run += pa.P[t];
+      }
+      pa.last = i0 + pa.n == g.I;
+      pa.total = run;
+      preset_budget_kernel<<<1, PRESET_CHUNK, 0, st>>>(pa, klist, kbase);
+    }
+    sel_total = run;
+  }
   // Layer-wide top-k.
   layer_hist0_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, lava ? 1 : 0, rowhist, part, flag);
   if (lava) {
@@ -1002,15 +1049,16 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     lava_budget_kernel<<<1, SB, sm, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp, online ? 1 : 0, prev_off, klist,
                                           sel_off);
   }
-  layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, lava ? klist : nullptr, segst);
+  layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, (lava || preset) ? klist : nullptr, segst);
   for (int ps = 1; ps < 3; ++ps) {
     radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist, flag);
     radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, 0, segst);
   }
   // Head budgets.
   layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, hkv, segst, cnt);
-  row_budget_kernel<<<R, SB, 0, st>>>(hkv, mode, kP, a.alpha_num, a.alpha_den, a.ck_num, a.ck_den, g.I, segst, cnt,
-                                      rowhist, budgets, rowbase, rowk2, rowst, sel_off);
+  row_budget_kernel<<<R, SB, 0, st>>>(hkv, mode, kP, a.alpha_num, a.alpha_den, a.ck_num, a.ck_den, g.I,
+                                      preset ? klist : nullptr, preset ? kbase : nullptr, segst, cnt, rowhist, budgets,
+                                      rowbase, rowk2, rowst, sel_off);
   // Every head's own top-k (LAVa keeps the layer threshold).
   if (!lava) {
     for (int ps = 1; ps < 3; ++ps) {

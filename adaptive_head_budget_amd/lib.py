@@ -36,7 +36,7 @@ class AdakvShape(ctypes.Structure):
 class AdakvAlloc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("alpha_num", ctypes.c_int32), ("alpha_den", ctypes.c_int32),
                 ("ck_num", ctypes.c_int32), ("ck_den", ctypes.c_int32), ("sinks", ctypes.c_int32),
-                ("budget", ctypes.c_int64)]
+                ("budget", ctypes.c_int64), ("inst_budget", ctypes.POINTER(ctypes.c_int64))]
 
 
 class AdakvError(RuntimeError):

@@ -5,6 +5,7 @@ libadakv's kernels through the ctypes binding.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import numpy as np
@@ -29,15 +30,25 @@ def make_shape(cfg: Workload, n_inst: Optional[int] = None, n: Optional[int] = N
         hidden=cfg.hidden, eps=cfg.eps, reserved0=0)
 
 
-def make_alloc(cfg: Workload, budget: Optional[int] = None) -> lib.AdakvAlloc:
+def make_alloc(cfg: Workload, budget: Optional[int] = None, inst_budget=None) -> lib.AdakvAlloc:
+    """Allocation settings of a workload.  inst_budget: per-instance budgets
+    (preset layer budgets, Ada-KV mode); the ctypes array is kept on the
+    returned struct so it lives as long as the struct."""
     mode = _ALLOC_NAMES[cfg.alloc] if cfg.alloc else _MODES[cfg.scorer]
-    return lib.AdakvAlloc(mode=mode, alpha_num=cfg.alpha[0], alpha_den=cfg.alpha[1], ck_num=cfg.ck[0],
-                          ck_den=cfg.ck[1], sinks=cfg.stream_sinks, budget=cfg.budget if budget is None else budget)
+    a = lib.AdakvAlloc(mode=mode, alpha_num=cfg.alpha[0], alpha_den=cfg.alpha[1], ck_num=cfg.ck[0],
+                       ck_den=cfg.ck[1], sinks=cfg.stream_sinks, budget=cfg.budget if budget is None else budget)
+    if inst_budget is not None:
+        arr = (ctypes.c_int64 * len(inst_budget))(*[int(x) for x in inst_budget])
+        a.inst_budget = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64))
+        a._keep = arr
+    return a
 
 
 def selected_rows(shape: lib.AdakvShape, alloc: lib.AdakvAlloc) -> int:
     if alloc.mode in (lib.ADAKV_ALLOC_LAVA_LAYERS, lib.ADAKV_ALLOC_GLOBAL):
         return alloc.budget - shape.n_inst * shape.w * shape.hkv
+    if alloc.inst_budget:
+        return sum(int(alloc.inst_budget[i]) - shape.w * shape.hkv for i in range(shape.n_inst))
     return shape.n_inst * (alloc.budget - shape.w * shape.hkv)
 
 
@@ -62,11 +73,11 @@ class Eviction:
     compact -> decode over I instances."""
 
     def __init__(self, cfg: Workload, n_inst: Optional[int] = None, n: Optional[int] = None,
-                 budget: Optional[int] = None, reserve: Optional[int] = None, device="cuda"):
+                 budget: Optional[int] = None, reserve: Optional[int] = None, device="cuda", inst_budget=None):
         import torch
         self.cfg = cfg
         self.shape = make_shape(cfg, n_inst, n)
-        self.alloc = make_alloc(cfg, budget)
+        self.alloc = make_alloc(cfg, budget, inst_budget)
         self.reserve = cfg.reserve if reserve is None else reserve
         s = self.shape
         I, hkv, p = s.n_inst, s.hkv, s.n - s.w

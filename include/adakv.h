@@ -105,6 +105,16 @@ typedef struct {
                          B' = budget - I*w*hkv must satisfy 0 <= B' <= hkv*p.
                          GLOBAL: total budget over all I instances, windows
                          included; 0 <= B' = budget - I*w*hkv <= I*hkv*p.   */
+  const int64_t* inst_budget; /* ADA only; NULL or HOST memory: I per-instance
+                         budgets B_i (window included, w*hkv <= B_i <= n*hkv)
+                         used instead of `budget` for instance i, e.g. preset
+                         layer budgets (Pyramid: SnapKV with a per-layer budget
+                         and alpha = 0; Ada-Pyramid: the same with Ada-KV's
+                         allocation, [AdaKV-paper] Section 4 "Baselines",
+                         [AdaKV-notes] "集成到现有的缓存驱逐方法中").  Read during
+                         the call; the same array must be passed to
+                         adakv_compact and adakv_decode_attn.  Other modes
+                         return ADAKV_EUNSUPPORTED when it is set.            */
 } adakv_alloc;
 
 /* Bytes of workspace every call below needs for this geometry (the maximum
@@ -181,7 +191,8 @@ adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const 
  * treated as +0.0).  Ranking: a larger score first; equal scores by the smaller
  * flat index g*p + t.
  *
- *   ADA         [AdaKV-notes] Algorithm 1 inside Algorithm 2: P = B - w*hkv;
+ *   ADA         [AdaKV-notes] Algorithm 1 inside Algorithm 2: P = B - w*hkv
+ *               (B = inst_budget[i] for instance i when given);
  *               the top P of all hkv*p scores give counts f_g; the safeguard
  *               (Algorithm 2, step 8) alpha*f_g + (1-alpha)*P/hkv is made
  *               integer exactly (floors, then one extra unit to the largest
@@ -222,7 +233,8 @@ adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const 
  *   sel     int32 out, sum of all budgets entries: instance i starts at
  *           sel_off[i]; inside it head g's selected token indices (in [0,p))
  *           follow head g-1's, each head ascending.  Its length is
- *           I*(budget - w*hkv) for ADA / CK and budget - I*w*hkv for LAVA
+ *           I*(budget - w*hkv) for ADA / CK (the sum over instances of
+ *           inst_budget[i] - w*hkv when given) and budget - I*w*hkv for LAVA
  *           and GLOBAL.
  *   sel_off [I+1] int64 out
  *

@@ -48,14 +48,15 @@ def test_struct_layout_matches_header(tmp_path):
     src = tmp_path / "probe.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "adakv.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(adakv_shape), sizeof(adakv_alloc),"
-        " offsetof(adakv_shape, eps), offsetof(adakv_alloc, budget), offsetof(adakv_shape, hidden));return 0;}\n")
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(adakv_shape), sizeof(adakv_alloc),"
+        " offsetof(adakv_shape, eps), offsetof(adakv_alloc, budget), offsetof(adakv_shape, hidden),"
+        " offsetof(adakv_alloc, inst_budget));return 0;}\n")
     exe = tmp_path / "probe"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
                    check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [ctypes.sizeof(lib.AdakvShape), ctypes.sizeof(lib.AdakvAlloc), lib.AdakvShape.eps.offset,
-                   lib.AdakvAlloc.budget.offset, lib.AdakvShape.hidden.offset]
+                   lib.AdakvAlloc.budget.offset, lib.AdakvShape.hidden.offset, lib.AdakvAlloc.inst_budget.offset]
 
 
 def test_strerror_and_version(L):
@@ -156,6 +157,28 @@ def test_lava_budget_range(L):
     a = _alloc(mode=lib.ADAKV_ALLOC_LAVA_LAYERS, budget=4 * 32 * 8 - 1)
     st = L.adakv_allocate(ctypes.byref(s), ctypes.byref(a), FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == lib.ADAKV_EINVAL
+
+
+def test_preset_budgets_checked(L):
+    """Per-instance budgets (preset layer budgets): each within [w*hkv, n*hkv],
+    Ada-KV mode only; the workspace and the selection size follow them."""
+    cfg = configs.LLAMA8B_LAYER
+    s = _shape(n_inst=3)
+    good = [8 * 32 + 900, 8 * 32 + 500, 8 * 32 + 100]
+    a = pipeline.make_alloc(cfg, inst_budget=good)
+    assert L.adakv_workspace_bytes(ctypes.byref(s), ctypes.byref(a), 2) > 0
+    assert pipeline.selected_rows(s, a) == 1500
+    for bad in ([8 * 32 - 1, 900, 900], [900, 8 * 16384 + 1, 900]):
+        a = pipeline.make_alloc(cfg, inst_budget=bad)
+        st = L.adakv_allocate(ctypes.byref(s), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+        assert st == lib.ADAKV_EINVAL
+    for mode in (lib.ADAKV_ALLOC_ADA_CRITICALKV, lib.ADAKV_ALLOC_ADA_FLOOR, lib.ADAKV_ALLOC_STREAMING,
+                 lib.ADAKV_ALLOC_GLOBAL, lib.ADAKV_ALLOC_LAVA_LAYERS):
+        a = pipeline.make_alloc(cfg, inst_budget=good)
+        a.mode = mode
+        a.budget = 3 * 8 * 32 + 10
+        st = L.adakv_allocate(ctypes.byref(s), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+        assert st == lib.ADAKV_EUNSUPPORTED, mode
 
 
 def test_compact_rejects(L):

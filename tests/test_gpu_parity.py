@@ -30,11 +30,12 @@ def _w(x, dtype):
     return synth.widen(x, dtype)
 
 
-def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, single_pass=False):
+def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, single_pass=False, inst_budget=None):
     """Run score -> allocate -> compact -> decode on numpy-drawn inputs and
     check every stage.  Returns the Eviction object.  single_pass: score
     through adakv_score_lse with the oracle's window-row log-sum-exp (rounded
-    to float32, the same input for both sides)."""
+    to float32, the same input for both sides).  inst_budget: per-instance
+    budgets (preset layer budgets) instead of `budget`."""
     log(f"case {label}: {cfg.name} I={I} n={n} budget={budget} reserve={reserve} steps={steps}")
     if steps != cfg.decode_steps:
         cfg = scaled(cfg, decode_steps=steps)       # draws of q, k, v do not depend on this
@@ -50,7 +51,7 @@ def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, sin
     else:
         w_o = None
     wo_of = (lambda i: insts[i]["w_o"]) if cfg.scorer == "laprox" else (lambda i: insts[0]["w_o"])
-    ev = pipeline.Eviction(cfg, n_inst=I, n=n, budget=budget, reserve=reserve)
+    ev = pipeline.Eviction(cfg, n_inst=I, n=n, budget=budget, reserve=reserve, inst_budget=inst_budget)
     w = cfg.w
     k64 = [_w(x["k"], dt) for x in insts]
     v64 = [_w(x["v"], dt) for x in insts]
@@ -92,19 +93,21 @@ def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, sin
             base += int(r["budgets"][i].sum())
         assert int(off[I]) == r["Bp"]
     else:
-        P = budget - w * cfg.hkv
+        base = 0
         for i in range(I):
+            bi = budget if inst_budget is None else int(inst_budget[i])
             if cfg.alloc == "floor":
-                r = allocation.ada_floor_allocate(score[i].astype(np.float64), budget, w, cfg.alpha)
+                r = allocation.ada_floor_allocate(score[i].astype(np.float64), bi, w, cfg.alpha)
             elif cfg.alloc == "streaming":
-                r = allocation.streaming_allocate(cfg.hkv, n - w, budget, w, cfg.stream_sinks)
+                r = allocation.streaming_allocate(cfg.hkv, n - w, bi, w, cfg.stream_sinks)
             elif cfg.scorer == "criticalkv":
                 r = allocation.criticalkv_allocate(score[i].astype(np.float64), score2[i].astype(np.float64),
-                                                   budget, w, cfg.alpha, cfg.ck)
+                                                   bi, w, cfg.alpha, cfg.ck)
             else:
-                r = allocation.ada_allocate(score[i].astype(np.float64), budget, w, cfg.alpha)
-            check_selection(b[i], int(off[i]), sel[i], r["budgets"], r["sel"], f"{label} inst {i}", off_ref=i * P)
-        assert int(off[I]) == I * P
+                r = allocation.ada_allocate(score[i].astype(np.float64), bi, w, cfg.alpha)
+            check_selection(b[i], int(off[i]), sel[i], r["budgets"], r["sel"], f"{label} inst {i}", off_ref=base)
+            base += bi - w * cfg.hkv
+        assert int(off[I]) == base
 
     ev.run_compact(k, v)
     torch.cuda.synchronize()
@@ -308,6 +311,22 @@ def test_floor_reading_ties(gpu_lib):
     b, off, sel = ev.host_selection()
     r = allocation.ada_floor_allocate(s.astype(np.float64), budget, cfg.w, cfg.alpha)
     check_selection(b[0], int(off[0]), sel[0], r["budgets"], r["sel"], "floor ties")
+
+
+@pytest.mark.parametrize("alpha", [(0, 1), (1, 5)])
+def test_pyramid_preset_layer_budgets(gpu_lib, alpha):
+    """Pyramid (alpha = 0: SnapKV's even split inside each layer) and
+    Ada-Pyramid (alpha = 1/5) with preset per-layer budgets that fall from the
+    shallow layers to the deep ones, two sequences per layer: budgets,
+    selections and offsets bit-exact against the oracle's Ada-KV allocation
+    run per instance with its own budget, the flat cache exact, decode within
+    tolerance.  The pages leave the schedule's hyper-parameters open; any
+    caller-given schedule takes this path."""
+    cfg = scaled(configs.LLAMA8B_MODEL, layers=4, batch=2, alpha=alpha, name=f"pyramid{alpha[0]}_{alpha[1]}")
+    n = 2500
+    per_layer = [8 * 32 + p for p in (1900, 1300, 700, 101)]            # decreasing with depth
+    inst_budget = [per_layer[i // cfg.batch] for i in range(cfg.instances)]
+    run_case(cfg, cfg.instances, n, 0, 2, 2, f"pyramid alpha {alpha}", inst_budget=inst_budget)
 
 
 @pytest.mark.parametrize("sinks", [4, 0, 700])
