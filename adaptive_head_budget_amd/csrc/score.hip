@@ -369,10 +369,19 @@ __global__ __launch_bounds__(512) void score_emit_kernel(
     }
     float m = -INFINITY, l = 0.f;
     if (ok) {
+      // eight partials loaded before any is merged (a dependent load per
+      // merge made this prologue latency-bound for small launches); the merge
+      // order is unchanged
       const float2* pr = part + ((size_t)il * hkv + g) * nchunk * (size_t)Gw + h * w + r;
-      for (int ch = gq; ch < nchunk; ch += 4) {
-        const float2 v = pr[(size_t)ch * Gw];
-        merge_ml(m, l, v.x, v.y);
+      for (int ch0 = gq; ch0 < nchunk; ch0 += 32) {
+        float2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int ch = ch0 + 4 * u;
+          v[u] = ch < nchunk ? pr[(size_t)ch * Gw] : make_float2(-INFINITY, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) merge_ml(m, l, v[u].x, v[u].y);
       }
     }
 #pragma unroll
