@@ -885,6 +885,337 @@ __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ scor
   }
 }
 
+// ---------------------------------------------------------------- one workgroup per instance
+// Small instances (at most XMAXH KV heads and XMAXE scores): the whole Ada-KV
+// allocation of an instance in one 1024-thread workgroup, histograms in LDS,
+// the instance's scores re-read for each of its seven passes (they stay in
+// the caches at this size): the layer-wide top-P (three digit passes), the
+// heads' counts and budgets, every head's own top-B_g (three digit passes, one
+// wave picking each head's digit), and the emission.  Same digits, same
+// order (-score, index) and the same integer safeguard as the multi-kernel
+// path, so the selection is identical; one launch instead of thirteen.
+// Bigger instances stay on the chunked path: one CU adding 2^17 top digits
+// (pooled scores share a few exponents) into one LDS histogram serialises on
+// the atomics (measured 205 us for a 130,816-score layer, against 61 us for
+// thirteen chunked launches spreading them over the chip).
+constexpr int XB = 1024;
+constexpr int XW = XB / WAVE;
+constexpr int XMAXH = 16;
+constexpr int XMAXE = 1 << 14;
+
+__device__ __forceinline__ uint32_t xblock_excl_scan(uint32_t x, uint32_t* sh, uint32_t& total) {
+  const uint32_t ex = wave_excl_scan(x);
+  const int wv = threadIdx.x / WAVE;
+  if ((threadIdx.x & (WAVE - 1)) == WAVE - 1) sh[wv] = ex + x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < XW; ++i) {
+    const uint32_t t = sh[i];
+    before += (i < wv) ? t : 0u;
+    all += t;
+  }
+  __syncthreads();
+  total = all;
+  return before + ex;
+}
+
+// Digit pick by one wave over nb bins (2048 or 512) of an LDS histogram: the
+// digit d with count(> d) < krem <= count(>= d), and count(> d).
+__device__ __forceinline__ void wave_pick(const uint32_t* h, int nb, uint32_t krem, uint32_t& dig,
+                                          uint32_t& above_out) {
+  const int lane = (int)__lane_id();
+  const int bpl = nb / WAVE;
+  uint32_t s = 0;
+  for (int j = 0; j < bpl; ++j) s += h[nb - 1 - (lane * bpl + j)];
+  const uint32_t ex = wave_excl_scan(s);
+  const bool mine = ex < krem && krem <= ex + s;
+  const uint64_t bal = __ballot(mine);
+  uint32_t d = 0, ab = 0;
+  if (mine) {
+    uint32_t a = ex;
+    for (int j = 0; j < bpl; ++j) {
+      const uint32_t c = h[nb - 1 - (lane * bpl + j)];
+      if (a < krem && krem <= a + c) {
+        d = (uint32_t)(nb - 1 - (lane * bpl + j));
+        ab = a;
+        break;
+      }
+      a += c;
+    }
+  }
+  const int src = bal ? (__ffsll((unsigned long long)bal) - 1) : 0;
+  dig = (uint32_t)__shfl((int)d, src);
+  above_out = (uint32_t)__shfl((int)ab, src);
+}
+
+// The thread's scores: flat indices [e0, e1) of the instance (head after
+// head), read four at a time; fn(e, row, key) is called in index order.
+template <class F>
+__device__ __forceinline__ void x_each(const float* sc, int e0, int e1, int p, bool vec, F fn) {
+  int row = e0 / p, k = e0 - row * p;
+  for (int e = e0; e < e1; e += 4) {
+    float v[4];
+    if (vec) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(sc + e);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = x[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (e + j < e1) ? sc[e + j] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (e + j < e1) {
+        fn(e + j, row, k, v[j]);
+        if (++k == p) { k = 0; ++row; }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(XB) void ada_small_kernel(const float* __restrict__ score, int hkv, int p, int kP0,
+                                                       const int64_t* __restrict__ klist,
+                                                       const int64_t* __restrict__ kbase, int alpha_num,
+                                                       int alpha_den, int n_inst, int32_t* __restrict__ budgets,
+                                                       int32_t* __restrict__ sel, int64_t* __restrict__ sel_off,
+                                                       uint32_t* __restrict__ flag) {
+  extern __shared__ uint32_t rowhist[];               // [hkv][NBIN]
+  __shared__ uint32_t lhist[NBIN];
+  __shared__ uint32_t sh[XW + 4];
+  __shared__ uint32_t rgt[XMAXH], req[XMAXH], reqT[XMAXH], tiepre[XMAXH];
+  __shared__ RState lst, rst[XMAXH];
+  __shared__ int64_t rbase[XMAXH];
+  const int inst = blockIdx.x;
+  const int E = hkv * p;
+  const float* sc = score + (size_t)inst * E;
+  const int64_t kP = klist ? klist[inst] : (int64_t)kP0;
+  const int64_t base0 = kbase ? kbase[inst] : (int64_t)inst * kP0;
+  const int npt = ((E + XB - 1) / XB + 3) & ~3;
+  const int e0 = min(E, (int)threadIdx.x * npt), e1 = min(E, e0 + npt);
+  const bool vec = (E % 4) == 0;     // every e0 and the instance base on 16 bytes
+  const int wv = threadIdx.x / WAVE;
+
+  // pass 0: the heads' top-digit histograms (their sum is the instance's)
+  for (int i = threadIdx.x; i < hkv * NBIN; i += XB) rowhist[i] = 0u;
+  __syncthreads();
+  {
+    uint32_t bad = 0u, cur = NONE, run = 0;
+    x_each(sc, e0, e1, p, vec, [&](int, int row, int, float x) {
+      bad |= bad_score(x);
+      const uint32_t b = (uint32_t)row * NBIN + (sel_key(x) >> 20);
+      if (b != cur) {
+        if (cur != NONE) atomicAdd(rowhist + cur, run);
+        cur = b;
+        run = 0;
+      }
+      ++run;
+    });
+    if (cur != NONE) atomicAdd(rowhist + cur, run);
+    if (bad) atomicOr(flag, 1u);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < NBIN; b += XB) {
+    uint32_t t = 0;
+    for (int g = 0; g < hkv; ++g) t += rowhist[g * NBIN + b];
+    lhist[b] = t;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    RState x = {NONE, 0};
+    if (kP > 0) {
+      uint32_t d, above;
+      wave_pick(lhist, NBIN, (uint32_t)kP, d, above);
+      x.prefix = d << 20;
+      x.krem = (int32_t)(kP - above);
+    }
+    if (threadIdx.x == 0) lst = x;
+  }
+  __syncthreads();
+  // passes 1, 2 of the instance's top-P
+  for (int ps = 1; ps < 3; ++ps) {
+    const RState L = lst;
+    if (L.prefix == NONE) break;
+    for (int b = threadIdx.x; b < NBIN; b += XB) lhist[b] = 0u;
+    __syncthreads();
+    x_each(sc, e0, e1, p, vec, [&](int, int, int, float x) {
+      const uint32_t u = sel_key(x);
+      if (in_prefix(u, L.prefix, ps)) atomicAdd(lhist + digit_of(u, ps), 1u);
+    });
+    __syncthreads();
+    if (wv == 0) {
+      uint32_t d, above;
+      wave_pick(lhist, pass_bins(ps), (uint32_t)L.krem, d, above);
+      if (threadIdx.x == 0) {
+        RState x = {L.prefix | (d << digit_shift(ps)), L.krem - (int32_t)above};
+        lst = x;
+      }
+    }
+    __syncthreads();
+  }
+  // pass 3: each head's entries above the instance's threshold T and equal to it
+  if (threadIdx.x < XMAXH) { rgt[threadIdx.x] = 0u; req[threadIdx.x] = 0u; }
+  __syncthreads();
+  const RState L = lst;
+  if (L.prefix != NONE) {
+    int crow = -1;
+    uint32_t gt = 0, eq = 0;
+    x_each(sc, e0, e1, p, vec, [&](int, int row, int, float x) {
+      if (row != crow) {
+        if (crow >= 0) { if (gt) atomicAdd(rgt + crow, gt); if (eq) atomicAdd(req + crow, eq); }
+        crow = row;
+        gt = eq = 0;
+      }
+      const uint32_t u = sel_key(x);
+      gt += u > L.prefix ? 1u : 0u;
+      eq += u == L.prefix ? 1u : 0u;
+    });
+    if (crow >= 0) { if (gt) atomicAdd(rgt + crow, gt); if (eq) atomicAdd(req + crow, eq); }
+  }
+  __syncthreads();
+  // budgets: counts f_g (ties at T shared out in head order), then the
+  // safeguard in exact integers (floors, one more to the largest remainders,
+  // lower head first), offsets in sel; then each head's first digit
+  if (threadIdx.x == 0) {
+    const int64_t quota = (L.prefix == NONE) ? 0 : L.krem;
+    int64_t f[XMAXH], q[XMAXH], r[XMAXH];
+    int64_t before = 0, sq = 0;
+    const int64_t a = alpha_num, b = alpha_den, h = hkv;
+    for (int g = 0; g < hkv; ++g) {
+      int64_t share = quota - before;
+      share = share < 0 ? 0 : (share > (int64_t)req[g] ? (int64_t)req[g] : share);
+      before += req[g];
+      f[g] = (int64_t)rgt[g] + share;
+      const int64_t num = a * h * f[g] + (b - a) * kP;
+      q[g] = num / (b * h);
+      r[g] = num % (b * h);
+      sq += q[g];
+    }
+    const int64_t def = kP - sq;
+    int64_t run = base0;
+    for (int g = 0; g < hkv; ++g) {
+      int rank = 0;
+      for (int i = 0; i < hkv; ++i) rank += (r[i] > r[g] || (r[i] == r[g] && i < g)) ? 1 : 0;
+      const int64_t Bg = q[g] + (rank < def ? 1 : 0);
+      budgets[(size_t)inst * hkv + g] = (int32_t)Bg;
+      rbase[g] = run;
+      run += Bg;
+      RState x = {0u, (int32_t)Bg};
+      rst[g] = x;
+    }
+    sel_off[inst] = base0;
+    if (inst == n_inst - 1) sel_off[n_inst] = base0 + kP;
+  }
+  __syncthreads();
+  for (int g = wv; g < hkv; g += XW) {
+    const RState x = rst[g];
+    RState y = {NONE, 0};
+    if (x.krem > 0) {
+      uint32_t d, above;
+      wave_pick(rowhist + g * NBIN, NBIN, (uint32_t)x.krem, d, above);
+      y.prefix = d << 20;
+      y.krem = x.krem - (int32_t)above;
+    }
+    if (__lane_id() == 0) rst[g] = y;
+  }
+  __syncthreads();
+  // passes 4, 5: every head's own top-B_g
+  for (int ps = 1; ps < 3; ++ps) {
+    for (int i = threadIdx.x; i < hkv * NBIN; i += XB) rowhist[i] = 0u;
+    __syncthreads();
+    x_each(sc, e0, e1, p, vec, [&](int, int row, int, float x) {
+      const RState R = rst[row];
+      const uint32_t u = sel_key(x);
+      if (R.prefix != NONE && in_prefix(u, R.prefix, ps)) atomicAdd(rowhist + row * NBIN + digit_of(u, ps), 1u);
+    });
+    __syncthreads();
+    for (int g = wv; g < hkv; g += XW) {
+      const RState x = rst[g];
+      RState y = {NONE, 0};
+      uint32_t eqT = 0u;
+      if (x.prefix != NONE) {
+        uint32_t d, above;
+        wave_pick(rowhist + g * NBIN, pass_bins(ps), (uint32_t)x.krem, d, above);
+        y.prefix = x.prefix | (d << digit_shift(ps));
+        y.krem = x.krem - (int32_t)above;
+        if (ps == 2) eqT = rowhist[g * NBIN + d];   // entries equal to the head's threshold
+      }
+      if (__lane_id() == 0) {
+        rst[g] = y;
+        if (ps == 2) reqT[g] = eqT;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int g = 0; g < hkv; ++g) { tiepre[g] = t; t += reqT[g]; }
+  }
+  __syncthreads();
+  // pass 6: emission in index order.  Kept: above the head's threshold, or
+  // equal to it within the first krem ties of the head (index order).  The
+  // class of every score (0 dropped, 1 tie, 2 kept) is parked in LDS, two
+  // bits each in words the thread owns (the head histograms are done with).
+  uint32_t* cls = rowhist;
+  const int cwpt = (npt + 15) / 16;
+  uint32_t* mine = cls + (size_t)threadIdx.x * cwpt;
+  const int cnt = e1 - e0;
+  uint32_t nties = 0;
+  {
+    uint32_t word = 0u;
+    int filled = 0, wi = 0;
+    x_each(sc, e0, e1, p, vec, [&](int, int row, int, float x) {
+      const RState R = rst[row];
+      const uint32_t u = sel_key(x);
+      uint32_t code = 0u;
+      if (R.prefix != NONE) code = u > R.prefix ? 2u : (u == R.prefix ? 1u : 0u);
+      nties += code == 1u ? 1u : 0u;
+      word |= code << (2 * filled);
+      if (++filled == 16) { mine[wi++] = word; word = 0u; filled = 0; }
+    });
+    if (filled) mine[wi] = word;
+  }
+  uint32_t tall;
+  uint32_t tb = xblock_excl_scan(nties, sh, tall);
+  uint32_t nkept = 0;
+  {
+    int row = e0 / (p > 0 ? p : 1), k = e0 - row * p;
+    for (int wi = 0; wi < cwpt; ++wi) {
+      const uint32_t word = mine[wi];
+      uint32_t nw = 0u;
+      for (int b = 0; b < 16; ++b) {
+        if (wi * 16 + b >= cnt) break;
+        uint32_t code = (word >> (2 * b)) & 3u;
+        if (code == 1u) {
+          code = (tb - tiepre[row] < (uint32_t)rst[row].krem) ? 2u : 0u;
+          ++tb;
+        }
+        nkept += code == 2u ? 1u : 0u;
+        nw |= code << (2 * b);
+        if (++k == p) { k = 0; ++row; }
+      }
+      mine[wi] = nw;
+    }
+  }
+  uint32_t kall;
+  uint32_t pos = xblock_excl_scan(nkept, sh, kall);
+  {
+    int row = e0 / (p > 0 ? p : 1), k = e0 - row * p;
+    for (int wi = 0; wi < cwpt; ++wi) {
+      const uint32_t word = mine[wi];
+      for (int b = 0; b < 16; ++b) {
+        if (wi * 16 + b >= cnt) break;
+        if (((word >> (2 * b)) & 3u) == 2u) {
+          if (pos < (uint32_t)kP) sel[base0 + pos] = k;
+          ++pos;
+        }
+        if (++k == p) { k = 0; ++row; }
+      }
+    }
+  }
+  (void)rbase;
+}
+
 // ---------------------------------------------------------------- workspace plan
 struct AllocPlan {
   int R, cpr, ntile, nchunk;
@@ -970,8 +1301,11 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   const int kP = (lava || preset) ? 0 : (int)(a.budget - (int64_t)g.w * g.hkv);
   int64_t sel_total = lava ? a.budget - (int64_t)g.I * g.w * g.hkv : (int64_t)g.I * kP;
 
+  // small instances: one workgroup per instance does the whole Ada-KV allocation
+  const bool small = a.mode == ADAKV_ALLOC_ADA && hkv <= XMAXH && (int64_t)hkv * g.p <= XMAXE;
   {
-    const size_t n16 = P.zero_end / 16;
+    // the precondition word, and the histograms and counts the chunked path adds into
+    const size_t n16 = small ? 1 : P.zero_end / 16;
     const int blocks = (int)std::min<size_t>((n16 + SB - 1) / SB, 4096);
     sel_zero_kernel<<<blocks, SB, 0, st>>>(reinterpret_cast<u32x4*>(ws), n16);
   }
@@ -1040,6 +1374,14 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
       preset_budget_kernel<<<1, PRESET_CHUNK, 0, st>>>(pa, klist, kbase);
     }
     sel_total = run;
+  }
+  if (small) {
+    // one workgroup per instance (the zero fill above cleared the flag)
+    const int npt = (int)((((int64_t)hkv * g.p + XB - 1) / XB + 3) & ~3);
+    const size_t lds = std::max((size_t)hkv * NBIN, (size_t)XB * ((npt + 15) / 16)) * sizeof(uint32_t);
+    ada_small_kernel<<<g.I, XB, lds, st>>>(score, hkv, g.p, kP, preset ? klist : nullptr, preset ? kbase : nullptr,
+                                          a.alpha_num, a.alpha_den, g.I, budgets, sel, sel_off, flag);
+    return hipGetLastError();
   }
   // Layer-wide top-k.
   layer_hist0_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, lava ? 1 : 0, rowhist, part, flag);

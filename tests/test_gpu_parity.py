@@ -313,8 +313,9 @@ def test_floor_reading_ties(gpu_lib):
     check_selection(b[0], int(off[0]), sel[0], r["budgets"], r["sel"], "floor ties")
 
 
+@pytest.mark.parametrize("n", [2500, 1200])      # the chunked selection path, and one workgroup per instance
 @pytest.mark.parametrize("alpha", [(0, 1), (1, 5)])
-def test_pyramid_preset_layer_budgets(gpu_lib, alpha):
+def test_pyramid_preset_layer_budgets(gpu_lib, alpha, n):
     """Pyramid (alpha = 0: SnapKV's even split inside each layer) and
     Ada-Pyramid (alpha = 1/5) with preset per-layer budgets that fall from the
     shallow layers to the deep ones, two sequences per layer: budgets,
@@ -323,8 +324,7 @@ def test_pyramid_preset_layer_budgets(gpu_lib, alpha):
     tolerance.  The pages leave the schedule's hyper-parameters open; any
     caller-given schedule takes this path."""
     cfg = scaled(configs.LLAMA8B_MODEL, layers=4, batch=2, alpha=alpha, name=f"pyramid{alpha[0]}_{alpha[1]}")
-    n = 2500
-    per_layer = [8 * 32 + p for p in (1900, 1300, 700, 101)]            # decreasing with depth
+    per_layer = [8 * 32 + p * n // 2500 for p in (1900, 1300, 700, 101)]   # decreasing with depth
     inst_budget = [per_layer[i // cfg.batch] for i in range(cfg.instances)]
     run_case(cfg, cfg.instances, n, 0, 2, 2, f"pyramid alpha {alpha}", inst_budget=inst_budget)
 
