@@ -13,6 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libadakv.so")
+PEAKS_SRC = os.path.join(PKG, "peaks.hip")
+PEAKS = os.path.join(PKG, "adakv_peaks")   # measured MFMA / HBM peaks, run by bench.py
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -44,8 +46,14 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", PEAKS_SRC, "-o", PEAKS + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAKS_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(PEAKS + ".tmp", PEAKS)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS}")
     return LIB
 
 

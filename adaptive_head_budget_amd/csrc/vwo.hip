@@ -65,10 +65,27 @@ __global__ __launch_bounds__(256, 2) void vwo_norm_kernel(const uint16_t* __rest
                                                           int n, int p, int hidden, float eps) {
   __shared__ __align__(16) char wt[2][SLOT];
   __shared__ float ahs[MAXG][KEYS];     // (A_i + eps) of the workgroup's keys
-  const int g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
+  // Workgroups are dealt round-robin to the 8 XCDs (workgroup b to XCD b % 8),
+  // and each XCD has its own L2.  Work item (key block, head) is therefore
+  // chosen so that XCD x takes a contiguous run of the (head, key block) order:
+  // the CUs of one XCD stream the same head's W^O tiles through their shared
+  // L2 instead of every XCD streaming every head's.  One instance per launch
+  // plane (blockIdx.z); a grid whose size is not a multiple of 8 keeps the
+  // plain order.
+  int kb = blockIdx.x, g = blockIdx.y;
+  {
+    const int nkb = gridDim.x, items = gridDim.x * gridDim.y;
+    if (items % 8 == 0) {
+      const int b = blockIdx.y * nkb + blockIdx.x;
+      const int w = (b % 8) * (items / 8) + b / 8;
+      g = w / nkb;
+      kb = w % nkb;
+    }
+  }
+  const int il = blockIdx.z, inst = inst0 + il;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int gq = lane >> 4, c = lane & 15;
-  const int kwg = blockIdx.x * KEYS;
+  const int kwg = kb * KEYS;
   const int key0 = kwg + 64 * wv;
   const uint16_t* vb = v + ((size_t)inst * hkv + g) * (size_t)n * D;
   constexpr int NPLANE = (MODE == VWO_GRAM) ? 2 : 1;

@@ -129,6 +129,21 @@ def device_row_lse(cfg, data):
     return out
 
 
+def measured_peaks():
+    """The chip's dense bf16 MFMA rate (with its shader clock), HBM read and
+    HBM copy bandwidth, measured by the small program the build makes from
+    adaptive_head_budget_amd/peaks.hip (a child process, run before this one
+    touches the GPU).  Reported beside the published peaks the rooflines use."""
+    import subprocess
+    exe = os.path.join(ROOT, "adaptive_head_budget_amd", "adakv_peaks")
+    if not os.path.exists(exe):
+        return {"error": "adakv_peaks not built"}
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip()[-200:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def cpu_baseline(cfg, target_s: float = 10.0):
     """The oracle, untuned, on the host cores: its own scorer, allocation and
     compaction on instances 0, 1, ... of the workload until about target_s
@@ -246,6 +261,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true",
                     help="do not overwrite 512 MiB before each step's eviction (workloads whose K and V fit "
                          "in 1 GiB are otherwise re-read from the 256 MB infinity cache)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA / HBM peaks (a separate small program run before timing)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, copy a buffer of this size once (a plain copy kernel of known size, "
                          "used to calibrate HBM byte counters in a profiled run)")
@@ -255,6 +272,10 @@ def main():
               f"leg: instances shard across GPUs with no exchange, so one GPU's rate is the per-GPU figure",
               file=sys.stderr)
         sys.exit(2)
+
+    measured = None
+    if not args.no_peaks:
+        measured = measured_peaks()
 
     import torch
     from adaptive_head_budget_amd import configs, lib, pipeline, synth
@@ -386,6 +407,8 @@ def main():
     out["roofline_evict"] = {"kernels": "adakv_score + adakv_allocate + adakv_compact", "bound": "hbm",
                              "achieved": ev_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ev_gbs / HBM_PEAK_GBS,
                              "algorithmic_bytes": evict_bytes(cfg), "median_ms": evict_ms}
+    if measured is not None:
+        out["measured_peaks"] = measured
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)
