@@ -315,6 +315,385 @@ __global__ __launch_bounds__(512) void score_stats_kernel(
   }
 }
 
+// ---------------------------------------------------------------- register-K path
+// bf16 keys, d = 128, G query heads of w <= 32 rows per KV head.  The window
+// queries of the workgroup's KV head sit in LDS for its whole life (the B
+// operand, read 16 bytes per lane per k-step); every wave streams its own
+// 64-key blocks of K from global memory straight into the A-operand registers.
+// No K tile goes through LDS and no barrier follows the prologue, so the
+// waves of a CU drift apart and hide each other's load latency.  The MFMA
+// inputs and their order (two half-length accumulations of the head
+// dimension, added at the end) are those of logits_block, so the logits are
+// bit-identical to the LDS-tiled kernels'.
+constexpr int KB = 64;          // keys per block: 4 M-blocks
+constexpr int KR_WAVES = 4;     // waves per workgroup
+constexpr int KR_QROWB = 256;   // bytes per query row in LDS (d = 128 bf16)
+
+// M-row m of M-block mb holds block key 16*(m/4) + 4*mb + (m%4): lane group gq
+// of the result owns the 16 consecutive keys 16*gq .. 16*gq + 15.
+__device__ __forceinline__ int kr_key(int mb, int m) { return 16 * (m >> 2) + 4 * mb + (m & 3); }
+
+// LDS row R = 16*nb + c (nb over the G heads' NBW blocks of 16 window rows,
+// rows past w zero); 16-byte chunk ch of row R at position ch ^ (R % 16), so
+// the 16 rows of one B-operand read fall in 16 distinct bank groups.
+template <int G, int NBW>
+__device__ __forceinline__ void kr_stage_q(char* lds, const uint16_t* q, int inst, int hq, int g, int w) {
+  constexpr int ROWS = G * NBW * 16;
+  for (int idx = threadIdx.x; idx < ROWS * 16; idx += blockDim.x) {
+    const int R = idx >> 4, ch = idx & 15;
+    const int h = R / (NBW * 16), r = R % (NBW * 16);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < w) v = ld16(q + (((size_t)inst * hq + (size_t)g * G + h) * w + r) * 128 + ch * 8);
+    st16(lds + R * KR_QROWB + ((ch ^ (R & 15)) << 4), v);
+  }
+}
+
+// Per-lane byte offsets of the B operand of k-step ks (window-row block 0);
+// block nb adds the constant 4096*nb.
+__device__ __forceinline__ int kr_qoff(int ks, int c, int gq) { return c * KR_QROWB + (((4 * ks + gq) ^ c) << 4); }
+
+// A operands of M-blocks [0, NMB) of the block starting at key kb0: [mb][ks],
+// lane (c, gq) holds elements 32*ks + 8*gq .. +8 of key row kb0 + key(mb, c)
+// (koff[mb] = byte offset of that row relative to kb0, plus 16*gq).  Buffer
+// loads whose whole offset is per lane, so the hardware range check covers it:
+// rows outside the head's n keys (past the end, or before key 0: the offset
+// wraps to a huge value) read as zeros, masked by the caller.
+template <int NMB>
+__device__ __forceinline__ void kr_load(bf16x8 (&kf)[NMB][4], __amdgpu_buffer_rsrc_t rs, const int (&koff)[NMB], int kb0) {
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int off = koff[mb] + kb0 * KR_QROWB;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[mb][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * ks, 0, 0));
+  }
+}
+
+// Logits of M-block mb against the window-row block whose operands are qo.
+template <int NMB>
+__device__ __forceinline__ f32x4 kr_logits(const bf16x8 (&kf)[NMB][4], int mb, const bf16x8 (&qo)[4]) {
+  f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mb][0], qo[0], zero4(), 0, 0, 0);
+  f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mb][2], qo[2], zero4(), 0, 0, 0);
+  p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mb][1], qo[1], p0, 0, 0, 0);
+  p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mb][3], qo[3], p1, 0, 0, 0);
+  f32x4 z;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) z[j] = p0[j] + p1[j];
+  return z;
+}
+
+// Pass 1 on the register-K path: the workgroup covers keys [chunk*kpw,
+// +kpw) of one KV head, wave v its blocks v, v+4, ... (kpw a multiple of
+// 4*KB).  Per window row each lane sums exp2(z*c2 - m) over its keys against a
+// reference m fixed at its first block (the largest scaled logit there), so a
+// block costs one FMA, one exp and one add per logit and no maximum.  Only
+// when a block's sum leaves the safe range (a logit more than 2^6 above the
+// reference, or the first block, whose reference is still -inf) does the lane
+// take the maximum of the block, raise m and rescale its sum.  Every wave
+// writes its own partial per row: sub-chunk chunk*4 + wave.
+template <int G, int NBW, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kr_stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                      float2* __restrict__ part, int inst0, int hq, int hkv, int n,
+                                                      int w, int p, int kend, int nsub, int kpw, float c2) {
+  constexpr int NBT = G * NBW;
+  extern __shared__ __align__(16) char lds[];
+  const int chunk = blockIdx.x, g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: block offsets stay scalar
+  const int gq = lane >> 4, c = lane & 15;
+  kr_stage_q<G, NBW>(lds, q, inst, hq, g, w);
+  __syncthreads();
+  const uint16_t* kh = k + ((size_t)inst * hkv + g) * (size_t)n * 128;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kh), 0, n * KR_QROWB, 0x00020000);
+  int koff[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) koff[mb] = kr_key(mb, c) * KR_QROWB + 16 * gq;
+  int qoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qoff[ks] = kr_qoff(ks, c, gq);
+
+  float rm[NBT], rl[NBT];
+#pragma unroll
+  for (int nb = 0; nb < NBT; ++nb) { rm[nb] = -INFINITY; rl[nb] = 0.f; }
+  const int c0 = chunk * kpw, c1 = min(c0 + kpw, kend);
+  const int full_end = CAUSAL ? min(kend - 1, p) : kend - 1;   // last key inside every row's domain
+  auto block = [&](const bf16x8 (&kf)[4][4], int b0) {
+    const int kl = b0 + 16 * gq;   // first key of this lane's 16
+    auto fold = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+#pragma unroll
+      for (int nb = 0; nb < NBT; ++nb) {
+        bf16x8 qo[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qo[ks] = *reinterpret_cast<const bf16x8*>(lds + qoff[ks] + 4096 * nb);
+        f32x4 z[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) z[mb] = kr_logits(kf, mb, qo);
+        const int r = (nb % NBW) * 16 + c;
+        const int lim = CAUSAL ? min(kend - 1, p + r) : kend - 1;
+        auto sum = [&](float mref) {
+          float ls = 0.f;
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float e = fast_exp2(fmaf(z[mb][j], c2, -mref));
+              if (FULL) ls += e;
+              else ls += (kl + 4 * mb + j <= lim) ? e : 0.f;
+            }
+          return ls;
+        };
+        float ls = sum(rm[nb]);
+        // first block, a much larger logit, or (invalid input) NaN; taken by the
+        // whole wave (a lane whose reference stands recomputes the same sum)
+        if (__builtin_amdgcn_ballot_w64(!(ls < 0x1p64f)) != 0) {
+          float lm = -INFINITY;
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (FULL || kl + 4 * mb + j <= lim) lm = fmaxf(lm, z[mb][j]);
+          const float lmc = lm * c2;
+          if (lmc > rm[nb]) {
+            rl[nb] *= fast_exp2(rm[nb] - lmc);   // exp2(-inf) = 0 at the first block
+            rm[nb] = lmc;
+          }
+          ls = (lm == -INFINITY) ? 0.f : sum(rm[nb]);
+        }
+        rl[nb] += ls;
+      }
+    };
+    if (b0 + KB - 1 <= full_end) fold(std::true_type{});
+    else fold(std::false_type{});
+  };
+  // Two register sets: the next block's loads are in flight while a block is
+  // folded.  The loads are unconditional (past the wave's last block they
+  // re-read its current block, an L2 hit) so the waits stay exact.
+  int b0 = c0 + wv * KB;
+  if (b0 < c1) {
+    bf16x8 ka[4][4], kb[4][4];
+    kr_load(ka, rs, koff, b0);
+    while (true) {
+      int b1 = b0 + KR_WAVES * KB;
+      bool more = b1 < c1;
+      kr_load(kb, rs, koff, more ? b1 : b0);
+      block(ka, b0);
+      if (!more) break;
+      b0 = b1;
+      b1 = b0 + KR_WAVES * KB;
+      more = b1 < c1;
+      kr_load(ka, rs, koff, more ? b1 : b0);
+      block(kb, b0);
+      if (!more) break;
+      b0 = b1;
+    }
+  }
+  const int Gw = G * w;
+#pragma unroll
+  for (int nb = 0; nb < NBT; ++nb) {
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const float om = shfl_xor(rm[nb], mask), ol = shfl_xor(rl[nb], mask);
+      merge_ml(rm[nb], rl[nb], om, ol);
+    }
+    const int h = nb / NBW, r = (nb % NBW) * 16 + c;
+    if (gq == 0 && r < w)
+      part[(((size_t)il * hkv + g) * nsub + (size_t)chunk * KR_WAVES + wv) * (size_t)Gw + h * w + r] =
+          make_float2(rm[nb], rl[nb]);
+  }
+}
+
+// Sum 16 per-lane values over the 16 lanes of each lane group; afterwards lane
+// c holds the total of entry c.  The butterfly of reduce_scatter16, one step
+// shorter.
+__device__ __forceinline__ float reduce16(const float (&x)[16], int c) {
+  float z[8], u[4], t[2], o[1];
+  rs_step<DPP_MIRROR, 8>(x, z, (c >> 3) & 1);
+  rs_step<DPP_HALF_MIRROR, 4>(z, u, (c >> 2) & 1);
+  rs_step<DPP_XOR2, 2>(u, t, (c >> 1) & 1);
+  rs_step<DPP_XOR1, 1>(t, o, c & 1);
+  return o[0];
+}
+
+// Pass 2 on the register-K path, SnapKV / Ada-KV scores of prefix keys (no
+// per-head output).  The workgroup covers keys [chunk*kpw, +kpw) of one KV
+// head, wave v its 64-key blocks v, v+4, ...  For every window-row block the
+// lane holds the logits of its 16 consecutive keys (M-blocks 0-3); a fifth
+// M-block gives the pooling halo of the block's two ends (keys b0-4 .. b0-1
+// and b0+64 .. b0+67), and every lane group takes its 3 + 3 neighbours from
+// the adjacent groups by lane moves.  The max pooling runs on the logits (exp is
+// increasing), then the normalised weight exp2(z*c2 - m)*(1/l) is added per
+// key over all G*w rows of the KV head inside the lane; one butterfly over
+// the 16 lanes of a group per block finishes the sum, which is the mean over
+// rows and query heads once divided by G*w.
+template <int G, int NBW, int POOL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kr_emit_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float2* __restrict__ part,
+    const float* __restrict__ row_lse, float* __restrict__ score, int inst0, int hq, int hkv, int n, int w, int p,
+    int nsub, int kpw, float c2) {
+  constexpr int NBT = G * NBW, RHO = (POOL - 1) / 2;
+  constexpr int NMB = RHO > 0 ? 5 : 4;
+  constexpr int NX = 16 + 2 * RHO;
+  extern __shared__ __align__(16) char lds[];
+  const int chunk = blockIdx.x, g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane >> 4, c = lane & 15;
+  kr_stage_q<G, NBW>(lds, q, inst, hq, g, w);
+  const int Gw = G * w;
+
+  // Row statistics of rows (nb, c), wave v taking blocks nb = v, v+4, ...:
+  // the pass-1 partials merged, lane group gq folding partials gq, gq+4, ...
+  // in order, then the four groups combined (the same order in every
+  // workgroup of the head).  With row_lse given, its value times log2 e split
+  // in float64 into hi (the reference) + lo (the factor exp2(-lo)).  Padding
+  // rows (r >= w, zero queries) get weight 0.  Kept in LDS after the queries:
+  // (reference, 1/sum) per row.
+  float2* rstat = reinterpret_cast<float2*>(lds + NBT * 4096);
+  for (int nb = wv; nb < NBT; nb += KR_WAVES) {
+    const int h = nb / NBW, r = (nb % NBW) * 16 + c;
+    const bool ok = r < w;
+    float mc = 0.f, il_row = 0.f;
+    if (row_lse != nullptr) {
+      if (ok) {
+        const double x = (double)row_lse[((size_t)inst * hq + (size_t)g * G + h) * w + r] * 1.4426950408889634;
+        const float hi = (float)x;
+        mc = hi;
+        il_row = fast_exp2(-(float)(x - (double)hi));
+      }
+    } else {
+      float m = -INFINITY, l = 0.f;
+      if (ok) {
+        const float2* pr = part + ((size_t)il * hkv + g) * nsub * (size_t)Gw + h * w + r;
+        for (int ch0 = gq; ch0 < nsub; ch0 += 32) {
+          float2 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int ch = ch0 + 4 * u;
+            v[u] = ch < nsub ? pr[(size_t)ch * Gw] : make_float2(-INFINITY, 0.f);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) merge_ml(m, l, v[u].x, v[u].y);
+        }
+      }
+#pragma unroll
+      for (int mask = 16; mask <= 32; mask <<= 1) {
+        const float om = shfl_xor(m, mask), ol = shfl_xor(l, mask);
+        merge_ml(m, l, om, ol);
+      }
+      mc = ok ? m : 0.f;
+      il_row = ok ? 1.0f / l : 0.f;
+    }
+    if (gq == 0) rstat[nb * 16 + c] = make_float2(mc, il_row);
+  }
+  __syncthreads();
+
+  const uint16_t* kh = k + ((size_t)inst * hkv + g) * (size_t)n * 128;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kh), 0, n * KR_QROWB, 0x00020000);
+  int koff[NMB];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) koff[mb] = kr_key(mb, c) * KR_QROWB + 16 * gq;
+  // halo block: M-rows 12-15 (lane group 3 of the result) hold keys b0-4 ..
+  // b0-1, the others b0+64 .. b0+67 (used by lane group 0)
+  if (NMB == 5) koff[NMB - 1] = (((c >> 2) == 3) ? -4 + (c & 3) : 64 + (c & 3)) * KR_QROWB + 16 * gq;
+  int qoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qoff[ks] = kr_qoff(ks, c, gq);
+  const float inv_gw = 1.0f / (float)Gw;
+  const int c0 = chunk * kpw, c1 = min(c0 + kpw, p);
+  float* out = score + ((size_t)inst * hkv + g) * (size_t)p;
+
+  auto block = [&](const bf16x8 (&kf)[NMB][4], int b0) {
+    const int kl = b0 + 16 * gq;   // first key of this lane's 16
+    float ks[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ks[i] = 0.f;
+    auto fold = [&](auto interior_tag) {
+      constexpr bool INTERIOR = decltype(interior_tag)::value;
+#pragma unroll
+      for (int nb = 0; nb < NBT; ++nb) {
+        // one window-row block at a time: without the fence the scheduler
+        // hoists every block's logits and runs out of registers
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 qo[4];
+#pragma unroll
+        for (int ks2 = 0; ks2 < 4; ++ks2) qo[ks2] = *reinterpret_cast<const bf16x8*>(lds + qoff[ks2] + 4096 * nb);
+        const float2 st = rstat[nb * 16 + c];
+        f32x4 z[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) z[mb] = kr_logits<NMB>(kf, mb, qo);
+        // x[t] <-> key kl - RHO + t; keys outside the prefix -> -inf
+        float x[NX];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[RHO + 4 * mb + j] = z[mb][j];
+#pragma unroll
+        for (int j = 0; j < RHO; ++j) {
+          // lane group gq reads its left halo from group gq - 1 and its right
+          // halo from group gq + 1 (mod 4); groups 3 and 0 offer the halo
+          // block's keys in place of their own edge keys.  (Selecting after
+          // the lane moves instead made the compiler spill.)
+          const float yl = (gq == 3) ? z[NMB - 1][4 - RHO + j] : z[(16 - RHO + j) >> 2][(16 - RHO + j) & 3];
+          const float yr = (gq == 0) ? z[NMB - 1][j] : z[0][j];
+          x[j] = shfl_lane(yl, (lane - 16) & 63);
+          x[16 + RHO + j] = shfl_lane(yr, (lane + 16) & 63);
+        }
+        if (!INTERIOR) {
+#pragma unroll
+          for (int t = 0; t < NX; ++t) {
+            const int key = kl - RHO + t;
+            if (key < 0 || key >= p) x[t] = -INFINITY;
+          }
+        }
+        const float mc = st.x, il_row = st.y;
+        if (RHO == 3) {
+          float a3[NX - 2];
+#pragma unroll
+          for (int t = 0; t < NX - 2; ++t) a3[t] = fmax3(x[t], x[t + 1], x[t + 2]);
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk)
+            ks[kk] = fmaf(fast_exp2(fmaf(fmax3(a3[kk], a3[kk + 2], a3[kk + 4]), c2, -mc)), il_row, ks[kk]);
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk) {
+            float pooled = x[kk + RHO];
+            if (RHO >= 1) pooled = fmax3(pooled, x[kk + RHO - 1], x[kk + RHO + 1]);
+            if (RHO >= 2) pooled = fmax3(pooled, x[kk + RHO - 2], x[kk + RHO + 2]);
+            ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
+          }
+        }
+      }
+    };
+    if (b0 >= RHO && b0 + KB + RHO <= p) fold(std::true_type{});
+    else fold(std::false_type{});
+    const float tot = reduce16(ks, c);
+    if (kl + c < p) out[kl + c] = tot * inv_gw;
+  };
+  // Two register sets: the next block's loads are in flight while a block is
+  // folded; unconditional (past the wave's last block they re-read its
+  // current block, an L2 hit) so the waits stay exact.
+  int b0 = c0 + wv * KB;
+  if (b0 < c1) {
+    bf16x8 ka[NMB][4], kb[NMB][4];
+    kr_load<NMB>(ka, rs, koff, b0);
+    while (true) {
+      int b1 = b0 + KR_WAVES * KB;
+      bool more = b1 < c1;
+      kr_load<NMB>(kb, rs, koff, more ? b1 : b0);
+      block(ka, b0);
+      if (!more) break;
+      b0 = b1;
+      b1 = b0 + KR_WAVES * KB;
+      more = b1 < c1;
+      kr_load<NMB>(ka, rs, koff, more ? b1 : b0);
+      block(kb, b0);
+      if (!more) break;
+      b0 = b1;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- pass 2
 // EMIT_SQ: the SNAP path without pooling on squared weights, written per head
 // unscaled (sum over rows of A^2).
@@ -680,6 +1059,81 @@ __global__ __launch_bounds__(256) void vbar_kernel(const T* __restrict__ v, floa
 constexpr int VBAR_ROWS = 2048;   // rows per value-norm workgroup
 int vbar_blocks(const Geo& g) { return (g.n + VBAR_ROWS - 1) / VBAR_ROWS; }
 
+constexpr int KR_MIN_KPW = 512;   // keys per register-K statistics workgroup, at least
+constexpr int KR_MIN_BLOCKS = 8;  // 64-key blocks per resident workgroup below which the LDS-tiled kernels run
+
+// The register-K kernels of a geometry, or nullptr where the LDS-tiled
+// kernels serve it (fp32, d != 128, w > 32, group sizes without an instance;
+// for pass 2 also LAVa, LaProx and CriticalKV, which need per-head or summed
+// rows).
+using KrStatsFn = void (*)(const uint16_t*, const uint16_t*, float2*, int, int, int, int, int, int, int, int, int,
+                           float);
+using KrEmitFn = void (*)(const uint16_t*, const uint16_t*, const float2*, const float*, float*, int, int, int, int,
+                          int, int, int, int, float);
+bool kr_geometry(const Geo& g) {
+  if (g.dtype != ADAKV_BF16 || g.d != 128 || g.w > 32) return false;
+  if ((int64_t)g.n * KR_QROWB >= ((int64_t)1 << 31)) return false;   // buffer range in 32 bits
+  return g.G == 1 || g.G == 2 || g.G == 4 || g.G == 5 || (g.G == 8 && g.w <= 16);
+}
+template <int G>
+KrStatsFn kr_stats_for(int w, bool causal) {
+  if (w <= 16) return causal ? kr_stats_kernel<G, 1, true> : kr_stats_kernel<G, 1, false>;
+  if constexpr (G <= 5) return causal ? kr_stats_kernel<G, 2, true> : kr_stats_kernel<G, 2, false>;
+  return nullptr;
+}
+KrStatsFn kr_stats_pick(const Geo& g, bool causal) {
+  if (!kr_geometry(g)) return nullptr;
+  switch (g.G) {
+    case 1: return kr_stats_for<1>(g.w, causal);
+    case 2: return kr_stats_for<2>(g.w, causal);
+    case 4: return kr_stats_for<4>(g.w, causal);
+    case 5: return kr_stats_for<5>(g.w, causal);
+    case 8: return kr_stats_for<8>(g.w, causal);
+    default: return nullptr;
+  }
+}
+template <int G, int NBW>
+KrEmitFn kr_emit_for_pool(int pool) {
+  switch (pool) {
+    case 1: return kr_emit_kernel<G, NBW, 1>;
+    case 3: return kr_emit_kernel<G, NBW, 3>;
+    case 5: return kr_emit_kernel<G, NBW, 5>;
+    case 7: return kr_emit_kernel<G, NBW, 7>;
+    default: return nullptr;
+  }
+}
+template <int G>
+KrEmitFn kr_emit_for(int w, int pool) {
+  if (w <= 16) return kr_emit_for_pool<G, 1>(pool);
+  if constexpr (G <= 5) return kr_emit_for_pool<G, 2>(pool);
+  return nullptr;
+}
+KrEmitFn kr_emit_pick(const Geo& g) {
+  if (!kr_geometry(g) || g.scorer != ADAKV_SCORE_SNAPKV) return nullptr;
+  switch (g.G) {
+    case 1: return kr_emit_for<1>(g.w, g.pool);
+    case 2: return kr_emit_for<2>(g.w, g.pool);
+    case 4: return kr_emit_for<4>(g.w, g.pool);
+    case 5: return kr_emit_for<5>(g.w, g.pool);
+    case 8: return kr_emit_for<8>(g.w, g.pool);
+    default: return nullptr;
+  }
+}
+// Resident workgroups of a register-K kernel on the device (one round of them
+// covers a launch).
+long kr_resident_wgs(const void* fn, size_t lds, int cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, KR_WAVES * WAVE, lds) != hipSuccess || per_cu < 1)
+    per_cu = 2;
+  return (long)per_cu * cus;
+}
+// Keys per workgroup for one round of `resident` workgroups over `blocks`
+// 64-key blocks, a multiple of 4 blocks (one per wave) and at least min_keys.
+int kr_keys_per_wg(long blocks, long resident, int min_keys) {
+  const long per_wg = std::max<long>((blocks + resident - 1) / resident, min_keys / KB);
+  return (int)(((per_wg + KR_WAVES - 1) / KR_WAVES) * KR_WAVES * KB);
+}
+
 struct ScorePlan {
   int ib;        // instances per batch
   int nchunk;    // stats chunks per head
@@ -696,7 +1150,9 @@ ScorePlan plan_score(const Geo& g) {
   P.ib = (int)ib;
   const bool laprox = g.scorer == ADAKV_SCORE_LAPROX;
   P.kend = (g.scorer == ADAKV_SCORE_LAVA || laprox) ? g.n : g.p;
-  P.nchunk = (P.kend + TILE - 1) / TILE;   // the most chunks a launch can use (one tile each)
+  // the most row partials a launch can write: one tile per chunk, or (register-K
+  // path) four waves per chunk of at least KR_MIN_KPW keys
+  P.nchunk = std::max((P.kend + TILE - 1) / TILE, KR_WAVES * ((P.kend + KR_MIN_KPW - 1) / KR_MIN_KPW));
   const size_t Gw = (size_t)g.G * g.w;
   size_t off = 0;
   P.off_part = off;  off = align_up(off + (size_t)P.ib * g.hkv * P.nchunk * Gw * sizeof(float2), 256);
@@ -747,15 +1203,46 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
     cus = 256;
   const long target = 2L * (cus > 0 ? cus : 256);
   const int ktiles = (P.kend + TILE - 1) / TILE;
+  KrStatsFn krs = nullptr;
+  KrEmitFn kre = nullptr;
+  size_t kr_lds = 0, kr_lds_e = 0;
+  long krs_res = 0, kre_res = 0;
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    if (kr_geometry(g) && !laprox) {
+      // only where every resident workgroup gets several blocks of each pass
+      const long blocks = (long)((P.kend + KB - 1) / KB) * g.hkv * P.ib;
+      kr_lds = (size_t)g.G * ((g.w + 15) / 16) * 16 * KR_QROWB;   // the window queries
+      kr_lds_e = kr_lds + (size_t)g.G * ((g.w + 15) / 16) * 16 * sizeof(float2);   // + row statistics
+      krs = kr_stats_pick(g, lava);
+      if (krs != nullptr) {
+        krs_res = kr_resident_wgs(reinterpret_cast<const void*>(krs), kr_lds, cus > 0 ? cus : 256);
+        if (blocks < KR_MIN_BLOCKS * krs_res) krs = nullptr;
+      }
+      kre = (krs != nullptr || row_lse != nullptr) ? kr_emit_pick(g) : nullptr;
+      if (kre != nullptr) {
+        kre_res = kr_resident_wgs(reinterpret_cast<const void*>(kre), kr_lds_e, cus > 0 ? cus : 256);
+        if (blocks < KR_MIN_BLOCKS * kre_res) kre = nullptr;
+      }
+    }
+  }
   for (int i0 = 0; i0 < g.I; i0 += P.ib) {
     const int ni = std::min(P.ib, g.I - i0);
     const long stiles = (long)ktiles * g.hkv * ni;
     const int spw = (int)std::min<long>(ktiles, std::max<long>(1, stiles / target));
     const int kpw = spw * TILE;
-    const int nchunk = (P.kend + kpw - 1) / kpw;
+    int nchunk = (P.kend + kpw - 1) / kpw;
     dim3 g1(nchunk, g.hkv, ni);
     if (row_lse != nullptr) {
       // the caller's row statistics replace pass 1
+    } else if (krs != nullptr) {
+      // one round of resident workgroups, each over an equal key range of one head
+      const int kpw_kr = kr_keys_per_wg((long)((P.kend + KB - 1) / KB) * g.hkv * ni, krs_res, KR_MIN_KPW);
+      const int chunks = (P.kend + kpw_kr - 1) / kpw_kr;
+      nchunk = chunks * KR_WAVES;
+      krs<<<dim3(chunks, g.hkv, ni), KR_WAVES * WAVE, kr_lds, st>>>(reinterpret_cast<const uint16_t*>(qt),
+                                                                   reinterpret_cast<const uint16_t*>(kt), part, i0,
+                                                                   g.hq, g.hkv, g.n, g.w, g.p, P.kend, nchunk,
+                                                                   kpw_kr, c2);
     } else if (lava)
       score_stats_kernel<T, D, NB, true><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
                                                                          g.w, g.p, P.kend, nchunk, kpw, c2);
@@ -775,7 +1262,12 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
       score_emit_kernel<T, D, NB, POOLV, EMIT_SNAP><<<g2, threads, lds_emit, st>>>(                          \
           qt, kt, part, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
   } while (0)
-    if (laprox) {
+    if (kre != nullptr && heads == nullptr) {
+      const int kpw_e = kr_keys_per_wg((long)((g.p + KB - 1) / KB) * g.hkv * ni, kre_res, KR_WAVES * KB);
+      kre<<<dim3((g.p + kpw_e - 1) / kpw_e, g.hkv, ni), KR_WAVES * WAVE, kr_lds_e, st>>>(
+          reinterpret_cast<const uint16_t*>(qt), reinterpret_cast<const uint16_t*>(kt), part, row_lse, score, i0,
+          g.hq, g.hkv, g.n, g.w, g.p, nchunk, kpw_e, c2);
+    } else if (laprox) {
       if constexpr (sizeof(T) == 2 && D == 128)   // the only LaProx geometry the ABI accepts
         score_emit_kernel<T, D, NB, 1, EMIT_SQ><<<g2, threads, lds_emit, st>>>(
             qt, kt, part, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);
