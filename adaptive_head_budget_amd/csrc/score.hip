@@ -527,7 +527,7 @@ __device__ __forceinline__ float reduce16(const float (&x)[16], int c) {
 // the 16 lanes of a group per block finishes the sum, which is the mean over
 // rows and query heads once divided by G*w.
 template <int G, int NBW, int POOL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void kr_emit_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void kr_emit_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float2* __restrict__ part,
     const float* __restrict__ row_lse, float* __restrict__ score, int inst0, int hq, int hkv, int n, int w, int p,
     int nsub, int kpw, float c2) {
@@ -608,20 +608,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float ks[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) ks[i] = 0.f;
+    auto logits = [&](int nb, f32x4 (&z)[NMB]) {
+      bf16x8 qo[4];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 4; ++ks2) qo[ks2] = *reinterpret_cast<const bf16x8*>(lds + qoff[ks2] + 4096 * nb);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) z[mb] = kr_logits<NMB>(kf, mb, qo);
+    };
     auto fold = [&](auto interior_tag) {
       constexpr bool INTERIOR = decltype(interior_tag)::value;
+      // software pipeline over the window-row blocks: the MFMAs of block
+      // nb + 1 are issued between the vector instructions of block nb (the
+      // matrix unit runs while vector instructions issue)
+      f32x4 zc[NMB];
+      logits(0, zc);
 #pragma unroll
       for (int nb = 0; nb < NBT; ++nb) {
-        // one window-row block at a time: without the fence the scheduler
-        // hoists every block's logits and runs out of registers
         __builtin_amdgcn_sched_barrier(0);
-        bf16x8 qo[4];
-#pragma unroll
-        for (int ks2 = 0; ks2 < 4; ++ks2) qo[ks2] = *reinterpret_cast<const bf16x8*>(lds + qoff[ks2] + 4096 * nb);
+        f32x4 zn[NMB];
+        if (nb + 1 < NBT) logits(nb + 1, zn);
         const float2 st = rstat[nb * 16 + c];
-        f32x4 z[NMB];
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) z[mb] = kr_logits<NMB>(kf, mb, qo);
+        const f32x4 (&z)[NMB] = zc;
         // x[t] <-> key kl - RHO + t; keys outside the prefix -> -inf
         float x[NX];
 #pragma unroll
@@ -663,6 +670,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             ks[kk] = fmaf(fast_exp2(fmaf(pooled, c2, -mc)), il_row, ks[kk]);
           }
         }
+        if (nb + 1 < NBT) {
+#pragma unroll
+          for (int i = 0; i < NMB * 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six vector instructions
+          }
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) zc[mb] = zn[mb];
+        }
       }
     };
     if (b0 >= RHO && b0 + KB + RHO <= p) fold(std::true_type{});
@@ -670,27 +686,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float tot = reduce16(ks, c);
     if (kl + c < p) out[kl + c] = tot * inv_gw;
   };
-  // Two register sets: the next block's loads are in flight while a block is
-  // folded; unconditional (past the wave's last block they re-read its
-  // current block, an L2 hit) so the waits stay exact.
-  int b0 = c0 + wv * KB;
-  if (b0 < c1) {
-    bf16x8 ka[NMB][4], kb[NMB][4];
-    kr_load<NMB>(ka, rs, koff, b0);
-    while (true) {
-      int b1 = b0 + KR_WAVES * KB;
-      bool more = b1 < c1;
-      kr_load<NMB>(kb, rs, koff, more ? b1 : b0);
-      block(ka, b0);
-      if (!more) break;
-      b0 = b1;
-      b1 = b0 + KR_WAVES * KB;
-      more = b1 < c1;
-      kr_load<NMB>(ka, rs, koff, more ? b1 : b0);
-      block(kb, b0);
-      if (!more) break;
-      b0 = b1;
-    }
+  for (int b0 = c0 + wv * KB; b0 < c1; b0 += KR_WAVES * KB) {
+    bf16x8 kf[NMB][4];
+    kr_load<NMB>(kf, rs, koff, b0);
+    block(kf, b0);
   }
 }
 
