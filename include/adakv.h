@@ -328,7 +328,14 @@ adakv_status adakv_lava_online_compact(const adakv_shape* shape, const void* k_n
  *   q          [I, hq, d]    dtype
  *   k_new, v_new [I, hkv, d] dtype, both or neither (NULL = no append)
  *   k_flat, v_flat, seg_start, seg_len       from adakv_compact
- *   reserve    the reserve given to adakv_compact
+ *   reserve    the reserve given to adakv_compact.  The library keeps no
+ *              state, so it cannot check this against the call that built the
+ *              cache: with a larger value an append that passes a segment's
+ *              reserved rows (its end is seg_start[s + 1]) is dropped on the
+ *              device: the row is neither stored nor attended, nothing past
+ *              the segment is read or written, and the call still returns
+ *              ADAKV_OK (out is then the attention over the rows already in
+ *              the segment, as if k_new / v_new were NULL).
  *   step       rows appended since adakv_compact (0 for the first decode);
  *              an append with step >= reserve returns ADAKV_ECAPACITY, and
  *              step > reserve returns ADAKV_EINVAL

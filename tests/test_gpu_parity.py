@@ -842,3 +842,43 @@ def test_score_precondition_flag(gpu_lib, kind):
                 in_bounds()
         t.copy_(good)
     log(f"  {kind}: flag clear on valid scores, set on -1, NaN, +-inf; selection in bounds")
+
+
+def test_decode_reserve_larger_than_compacted(gpu_lib):
+    """The documented behaviour when decode is given a larger reserve than
+    compaction used: an append that does not fit its segment is dropped (no
+    row stored, none read past the segment), the call succeeds, and the output
+    equals the attention over the rows already there (the same call without
+    an append)."""
+    from adaptive_head_budget_amd import lib
+    cfg = scaled(configs.LLAMA8B_LAYER, name="reserve_mismatch", decode_steps=2, reserve=1)
+    n = 2000
+    insts, st = _stack(cfg, 1, n)
+    q, k, v = (pipeline.to_device(st[x], "bf16") for x in ("q_win", "k", "v"))
+    ev = pipeline.Eviction(cfg, n=n, budget=cfg.hkv * cfg.w + (cfg.hkv * (n - cfg.w)) // 5, reserve=1)
+    ev.evict(q, k, v)
+    qd = [pipeline.to_device(np.ascontiguousarray(st["q_dec"][:, t]), "bf16") for t in range(2)]
+    kn = [pipeline.to_device(np.ascontiguousarray(st["k_new"][:, t]), "bf16") for t in range(2)]
+    vn = [pipeline.to_device(np.ascontiguousarray(st["v_new"][:, t]), "bf16") for t in range(2)]
+    # step 0 fills the one reserved row of every segment
+    lib.adakv_decode_attn(ev.shape, ev.alloc, qd[0], kn[0], vn[0], ev.k_flat, ev.v_flat, ev.seg_start, ev.seg_len,
+                          1, 0, ev.out, ev.ws)
+    torch.cuda.synchronize()
+    k_before, v_before = ev.k_flat.clone(), ev.v_flat.clone()
+    # step 1 under a reserve of 3: passes the host check, does not fit on the device
+    ws3 = torch.empty(lib.adakv_workspace_bytes(ev.shape, ev.alloc, 3), dtype=torch.uint8, device="cuda")
+    out_app = torch.empty_like(ev.out)
+    lib.adakv_decode_attn(ev.shape, ev.alloc, qd[1], kn[1], vn[1], ev.k_flat, ev.v_flat, ev.seg_start, ev.seg_len,
+                          3, 1, out_app, ws3)
+    torch.cuda.synchronize()
+    assert torch.equal(ev.k_flat, k_before) and torch.equal(ev.v_flat, v_before), "a dropped append wrote rows"
+    out_none = torch.empty_like(ev.out)
+    lib.adakv_decode_attn(ev.shape, ev.alloc, qd[1], None, None, ev.k_flat, ev.v_flat, ev.seg_start, ev.seg_len,
+                          1, 1, out_none, ws3)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_app).all()
+    # the same rows attended (the two calls may split the rows differently, so
+    # the sums can differ in rounding only)
+    diff = (out_app - out_none).abs().max().item()
+    assert diff <= 1e-5, f"a dropped append changed the output (max-abs {diff:.2e})"
+    log("  reserve larger than compacted: the append is dropped, cache untouched, output = no-append output")
