@@ -1,14 +1,21 @@
 // Observation-window scoring on gfx950.
 //
-// Pass 1 (score_stats_kernel): per window row, the softmax normaliser over the
-// row's key domain, as (row max, sum of exp) partials over key chunks.
-// Pass 2 (score_emit_kernel): the pooled, normalised weights reduced to one
-// score per key.  Both passes form Q_win K^T with 16x16 MFMA tiles: keys are the
-// M side (A operand, staged through LDS), window rows the N side (B operand,
-// held in registers).  The A rows are permuted so that every lane ends up with
-// 32 consecutive keys of one window row, which makes the max pooling a
-// register-local sliding maximum.  The row sums over a lane group use DPP lane
-// moves on the vector unit rather than LDS permutes.
+// Pass 1: per window row, the softmax normaliser over the row's key domain, as
+// (reference, sum of exp) partials over key chunks.  Pass 2: the pooled,
+// normalised weights reduced to one score per key.  Both passes form Q_win K^T
+// with 16x16x32 MFMA tiles, keys on the M side and window rows on the N side,
+// the A rows permuted so that every lane ends up with consecutive keys of one
+// window row (the max pooling is a register-local sliding maximum) and row sums
+// over a lane group done with DPP lane moves on the vector unit.  Two layouts:
+//  * register-K (kr_stats_kernel, kr_emit_kernel; bf16, d = 128, w <= 32):
+//    the window queries of the KV head's G query heads stay in LDS, and every
+//    wave streams its own 64-key blocks of K straight into its A-operand
+//    registers, so no K tile is staged through LDS and no barrier follows the
+//    prologue; a wave covers all G*w rows of its keys, so its row sums need one
+//    lane butterfly per block;
+//  * LDS-tiled (score_stats_kernel, score_emit_kernel; every other geometry,
+//    LAVa's and CriticalKV's emit passes, small calls): 128-key K tiles staged
+//    through LDS, each wave one query head with its rows' operands in registers.
 //
 // Definitions followed:
 //  * Ada-KV notes, Algorithm 2 ("Ada-KV Integration") steps 2-4: softmax of the
