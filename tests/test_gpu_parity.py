@@ -237,6 +237,40 @@ def test_geometries(gpu_lib, hq, hkv, w, pool, d, dtype):
     run_case(cfg, 2, n, (30 * hkv * n) // 100, 1, 1, cfg.name)
 
 
+# The register-K scoring kernels (bf16, d = 128, w <= 32) engage only when a
+# call gives every resident workgroup several 64-key blocks; many short
+# instances in one call do, so these cases reach their edges: group sizes 1,
+# 2, 5, 8, one or two 16-row window blocks (padded rows), every pool width,
+# ragged last blocks, causal statistics, the supplied-statistics mode.
+KR_CASES = [
+    # scorer, hq, hkv, w, pool, n
+    ("snapkv", 32, 8, 32, 7, 1000),
+    ("snapkv", 8, 8, 16, 3, 777),
+    ("snapkv", 16, 8, 20, 5, 1500),
+    ("snapkv", 40, 8, 32, 1, 900),
+    ("snapkv", 64, 8, 12, 7, 1100),
+    ("lava", 32, 8, 32, 7, 1000),
+]
+
+
+@pytest.mark.parametrize("scorer,hq,hkv,w,pool,n", KR_CASES)
+def test_register_k_path(gpu_lib, scorer, hq, hkv, w, pool, n):
+    base = configs.MISTRAL7B_LAVA if scorer == "lava" else configs.LLAMA8B_LAYER
+    cfg = scaled(base, hq=hq, hkv=hkv, w=w, pool=pool, name=f"kr_{scorer}_{hq}_{hkv}_{w}_{pool}", reserve=1,
+                 decode_steps=1)
+    I = 256
+    if scorer == "lava":   # the layers share at most one layer's prefix entries (B' <= hkv * p)
+        run_case(cfg, I, n, I * hkv * w + (hkv * (n - w)) // 2, 1, 1, cfg.name)
+    else:
+        run_case(cfg, I, n, hkv * w + (hkv * (n - w)) // 5, 1, 1, cfg.name)
+
+
+def test_register_k_single_pass(gpu_lib):
+    cfg = scaled(configs.LLAMA8B_LAYER, name="kr_single_pass", reserve=1, decode_steps=1)
+    n = 1000
+    run_case(cfg, 256, n, cfg.hkv * cfg.w + (cfg.hkv * (n - cfg.w)) // 5, 1, 1, cfg.name, single_pass=True)
+
+
 def test_budget_extremes(gpu_lib):
     base = scaled(configs.LLAMA8B_LAYER, name="extremes", decode_steps=1, reserve=1)
     n = 700
