@@ -66,6 +66,50 @@ def window_lse(q_win: np.ndarray, k: np.ndarray, causal: bool, full: bool = Fals
     return out
 
 
+def lse_from_causal(lse_causal: np.ndarray, q_win: np.ndarray, k: np.ndarray, scorer: str):
+    """A scorer's row statistic from the causal one a prefill leaves behind.
+
+    The prefill's causal attention (LAVa notes, "时间复杂度与内存使用分析": the
+    O(H N^2 d_h) term, the window-score pass a separate O(H N w d_h) one) leaves
+    for window row r, at position p + r, the log-sum-exp of its logits over
+    keys 0 .. p + r: the LAVa domain as it is.  The Ada-KV / CriticalKV domain is the prefix t < p
+    (Ada-KV notes, Algorithm 2 step 2), so the window keys p .. p + r come out:
+        lse = lse_c + ln(1 - sum_{t=p}^{p+r} exp(z_t - lse_c));
+    the LaProx domain is all n keys (LaProx page, Algorithm 1), so the later
+    window keys p + r + 1 .. n - 1 go in:
+        lse = lse_c + ln(1 + sum_{t>p+r} exp(z_t - lse_c)),
+    with z_t = q_win[i, r] . k[g, t] / sqrt(d).  Returns (lse [Hq, w], keep
+    [Hq, w]): keep is the prefix share 1 - sum(...) for the subtraction (1 for
+    the other scorers): the relative error of the causal input grows by 1/keep
+    in the result.
+    """
+    hq, w, d = q_win.shape
+    hkv, n, _ = k.shape
+    G = hq // hkv
+    p = n - w
+    lse = np.array(lse_causal, dtype=np.float64, copy=True)
+    keep = np.ones((hq, w), dtype=np.float64)
+    if scorer == "lava":
+        return lse, keep
+    for i in range(hq):
+        g = i // G
+        for r in range(w):
+            if scorer == "laprox":
+                keys = range(p + r + 1, n)
+            else:
+                keys = range(p, p + r + 1)
+            s = 0.0
+            for t in keys:
+                z = float(q_win[i, r] @ k[g, t]) / math.sqrt(d)
+                s += math.exp(z - lse_causal[i, r])
+            if scorer == "laprox":
+                lse[i, r] = lse_causal[i, r] + math.log1p(s)
+            else:
+                keep[i, r] = 1.0 - s
+                lse[i, r] = lse_causal[i, r] + math.log(keep[i, r])
+    return lse, keep
+
+
 def snapkv_head_scores(q_win: np.ndarray, k: np.ndarray, pool: int, lse: np.ndarray | None = None) -> np.ndarray:
     """Per-query-head window score A-bar_i over the prefix keys, [Hq, p].
 

@@ -243,6 +243,98 @@ def test_scores_from_supplied_normaliser():
     assert not np.allclose(scoring.snapkv_scores(q, k, 3, lc), a, rtol=1e-6)
 
 
+def check_causal_correction(fn) -> bool:
+    """From the exact causal statistic the correction gives each scorer's own
+    domain statistic, as window_lse defines it (pinned to SciPy above): the
+    prefix for Ada-KV and CriticalKV, all n keys for LaProx, the causal one
+    unchanged for LAVa; the prefix share is exp(lse_prefix - lse_causal)."""
+    r = rng(33)
+    hq, hkv, w, d, n = 6, 3, 5, 8, 30
+    q = r.standard_normal((hq, w, d)) * 2.0
+    k = r.standard_normal((hkv, n, d))
+    lc = scoring.window_lse(q, k, causal=True)
+    ok = True
+    for scorer, want in (("snapkv", scoring.window_lse(q, k, causal=False)),
+                         ("criticalkv", scoring.window_lse(q, k, causal=False)),
+                         ("laprox", scoring.window_lse(q, k, causal=False, full=True)),
+                         ("lava", lc)):
+        got, keep = fn(lc, q, k, scorer)
+        ok &= bool(np.allclose(got, want, rtol=0, atol=1e-12))
+        if scorer in ("snapkv", "criticalkv"):
+            ok &= bool(np.allclose(keep, np.exp(want - lc), rtol=1e-12))
+    return ok
+
+
+def _corr_window_off_by_one(lse_c, q, k, scorer):
+    """Planted mistake: the window range stops one key early (p .. p + r - 1)."""
+    hq, w, d = q.shape
+    hkv, n, _ = k.shape
+    p, G = n - w, hq // hkv
+    lse = np.array(lse_c, dtype=np.float64, copy=True)
+    if scorer in ("snapkv", "criticalkv"):
+        for i in range(hq):
+            for row in range(w):
+                s = sum(math.exp(float(q[i, row] @ k[i // G, t]) / math.sqrt(d) - lse_c[i, row])
+                        for t in range(p, p + row))
+                lse[i, row] = lse_c[i, row] + math.log(1.0 - s)
+        return lse, np.ones((hq, w))
+    return scoring.lse_from_causal(lse_c, q, k, scorer)
+
+
+def _corr_sign(lse_c, q, k, scorer):
+    """Planted mistake: the window mass added instead of removed."""
+    hq, w, d = q.shape
+    hkv, n, _ = k.shape
+    p, G = n - w, hq // hkv
+    lse = np.array(lse_c, dtype=np.float64, copy=True)
+    if scorer in ("snapkv", "criticalkv"):
+        for i in range(hq):
+            for row in range(w):
+                s = sum(math.exp(float(q[i, row] @ k[i // G, t]) / math.sqrt(d) - lse_c[i, row])
+                        for t in range(p, p + row + 1))
+                lse[i, row] = lse_c[i, row] + math.log1p(s)
+        return lse, np.ones((hq, w))
+    return scoring.lse_from_causal(lse_c, q, k, scorer)
+
+
+def _corr_laprox_includes_own(lse_c, q, k, scorer):
+    """Planted mistake: LaProx adds the row's own key p + r a second time."""
+    hq, w, d = q.shape
+    hkv, n, _ = k.shape
+    p, G = n - w, hq // hkv
+    if scorer != "laprox":
+        return scoring.lse_from_causal(lse_c, q, k, scorer)
+    lse = np.array(lse_c, dtype=np.float64, copy=True)
+    for i in range(hq):
+        for row in range(w):
+            s = sum(math.exp(float(q[i, row] @ k[i // G, t]) / math.sqrt(d) - lse_c[i, row])
+                    for t in range(p + row, n))
+            lse[i, row] = lse_c[i, row] + math.log1p(s)
+    return lse, np.ones((hq, w))
+
+
+def test_causal_correction_gives_each_domain():
+    assert check_causal_correction(scoring.lse_from_causal)
+
+
+def test_causal_correction_pins_catch_planted_mistakes():
+    assert not check_causal_correction(_corr_window_off_by_one)
+    assert not check_causal_correction(_corr_sign)
+    assert not check_causal_correction(_corr_laprox_includes_own)
+
+
+def test_causal_correction_scores():
+    """Scores from the corrected causal statistic are the two-pass scores."""
+    r = rng(34)
+    hq, hkv, w, d, n = 4, 2, 4, 16, 40
+    q = r.standard_normal((hq, w, d)) * 2.0
+    k = r.standard_normal((hkv, n, d))
+    lc = scoring.window_lse(q, k, causal=True)
+    lse, keep = scoring.lse_from_causal(lc, q, k, "snapkv")
+    np.testing.assert_allclose(scoring.snapkv_scores(q, k, 3, lse), scoring.snapkv_scores(q, k, 3), rtol=1e-11)
+    assert (keep > 0).all() and (keep < 1).all()
+
+
 # ---------------------------------------------------------------- LaProx
 def check_laprox_is_frobenius_norm(fn) -> bool:
     """G = 1: p_i[t] is the Frobenius norm of the explicit w x D matrix
