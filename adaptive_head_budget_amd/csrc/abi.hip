@@ -154,6 +154,18 @@ adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const 
   return score_call(shape, q_win, k, v, w_o, row_lse, score, score2, ws, ws_bytes, stream);
 }
 
+adakv_status adakv_lse_from_causal(const adakv_shape* shape, const void* q_win, const void* k,
+                                   const float* lse_causal, float* lse_out, int32_t* row_flag, void* stream) {
+  Geo g{};
+  adakv_status st = check_shape(shape, g);
+  if (st != ADAKV_OK) return st;
+  if (!aligned16(q_win) || !aligned16(k) || !aligned16(lse_causal) || !aligned16(lse_out)) return ADAKV_EINVAL;
+  if (row_flag != nullptr && !aligned16(row_flag)) return ADAKV_EINVAL;
+  if (g.w > 64 || g.G > 8) return ADAKV_EUNSUPPORTED;
+  return hip_status(launch_lse_from_causal(g, q_win, k, lse_causal, lse_out, row_flag,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, const float* score,
                             const float* score2, int32_t* budgets, int32_t* sel, int64_t* sel_off, void* ws,
                             size_t ws_bytes, void* stream) {

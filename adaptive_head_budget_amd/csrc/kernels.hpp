@@ -36,6 +36,9 @@ inline int factor_slices(const Geo& g) {
 }
 size_t factor_ws_bytes(const Geo& g);
 hipError_t launch_factor(const Geo& g, const void* w_o, char* ws, hipStream_t st);
+// Window-row log-sum-exp of the scorer's key domain from the causal one (causal.hip).
+hipError_t launch_lse_from_causal(const Geo& g, const void* q_win, const void* k, const float* lse_c,
+                                  float* lse_out, int32_t* row_flag, hipStream_t st);
 
 // ---- allocation (select.hip)
 size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a);

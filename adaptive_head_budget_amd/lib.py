@@ -21,8 +21,8 @@ ADAKV_SCORE_SNAPKV, ADAKV_SCORE_LAVA, ADAKV_SCORE_CRITICALKV, ADAKV_SCORE_LAPROX
 (ADAKV_ALLOC_ADA, ADAKV_ALLOC_LAVA_LAYERS, ADAKV_ALLOC_ADA_CRITICALKV, ADAKV_ALLOC_GLOBAL, ADAKV_ALLOC_ADA_FLOOR,
  ADAKV_ALLOC_STREAMING) = range(6)
 
-EXPORTS = ("adakv_workspace_bytes", "adakv_score", "adakv_score_lse", "adakv_allocate", "adakv_compact",
-           "adakv_decode_attn", "adakv_decode_attn_noalloc", "adakv_strerror", "adakv_version",
+EXPORTS = ("adakv_workspace_bytes", "adakv_score", "adakv_score_lse", "adakv_lse_from_causal", "adakv_allocate",
+           "adakv_compact", "adakv_decode_attn", "adakv_decode_attn_noalloc", "adakv_strerror", "adakv_version",
            "adakv_lava_online_allocate", "adakv_lava_online_compact")
 
 
@@ -65,6 +65,8 @@ def load(path: Optional[str] = None):
     lib.adakv_score.restype = ctypes.c_int
     lib.adakv_score_lse.argtypes = [S, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.adakv_score_lse.restype = ctypes.c_int
+    lib.adakv_lse_from_causal.argtypes = [S, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.adakv_lse_from_causal.restype = ctypes.c_int
     lib.adakv_allocate.argtypes = [S, A, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.adakv_allocate.restype = ctypes.c_int
     lib.adakv_compact.argtypes = [S, A, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
@@ -137,6 +139,12 @@ def adakv_score_lse(shape, q_win, k, v, w_o, row_lse, score, score2, ws, stream=
     st = load().adakv_score_lse(ctypes.byref(shape), _p(q_win), _p(k), _p(v), _p(w_o), _p(row_lse), _p(score),
                                 _p(score2), _p(ws), _nbytes(ws), _stream(stream))
     _check(st, "adakv_score_lse")
+
+
+def adakv_lse_from_causal(shape, q_win, k, lse_causal, lse_out, row_flag=None, stream=None):
+    st = load().adakv_lse_from_causal(ctypes.byref(shape), _p(q_win), _p(k), _p(lse_causal), _p(lse_out),
+                                      _p(row_flag), _stream(stream))
+    _check(st, "adakv_lse_from_causal")
 
 
 def adakv_allocate(shape, alloc, score, score2, budgets, sel, sel_off, ws, stream=None):

@@ -122,6 +122,19 @@ class Eviction:
         else:
             lib.adakv_score_lse(self.shape, q_win, k, v, w_o, row_lse, self.score, self.score2, self.ws, stream)
 
+    def lse_from_causal(self, q_win, k, lse_causal, out=None, row_flag=None, stream=None):
+        """The scorer's window-row log-sum-exp [I, hq, w] (float32) from the
+        causal one a prefill leaves (keys 0 .. p + r for window row r), for
+        run_score's row_lse.  out may be lse_causal (in place); row_flag, an
+        int32 [I, hq, w] tensor or None, receives 0 (well conditioned), 1
+        (the prefix keeps less than 2^-7 of the causal mass) or 2 (not
+        finite) per row."""
+        import torch
+        if out is None:
+            out = torch.empty_like(lse_causal)
+        lib.adakv_lse_from_causal(self.shape, q_win, k, lse_causal, out, row_flag, stream)
+        return out
+
     def scores_invalid(self) -> bool:
         """Whether the last allocation read a negative, NaN or infinite score
         (the int32 the library keeps at the start of the workspace).  Waits

@@ -101,18 +101,20 @@ def score_bytes(cfg) -> int:
     return b
 
 
-def device_row_lse(cfg, data):
+def device_row_lse(cfg, data, causal=None):
     """Input preparation for the single-pass scorer (not timed): the natural-log
     log-sum-exp of every window row's logits / sqrt(d) over the row's domain
     (prefix keys; LAVa: keys 0 .. p + r; LaProx: all keys), the statistic an
-    attention pass over the window rows leaves behind.  Plain torch float32 on
-    the device, one instance at a time."""
+    attention pass over the window rows leaves behind; causal=True: over keys
+    0 .. p + r whatever the scorer (what a causal prefill leaves).  Plain torch
+    float32 on the device, one instance at a time."""
     import math
     import torch
     I, hq, hkv, w, n, d, p = cfg.instances, cfg.hq, cfg.hkv, cfg.w, cfg.n, cfg.d, cfg.p
     G = hq // hkv
     out = torch.empty((I, hq, w), dtype=torch.float32, device=data["q_win"].device)
-    causal = cfg.scorer == "lava"
+    if causal is None:
+        causal = cfg.scorer == "lava"
     keys = n if (causal or cfg.scorer == "laprox") else p
     if causal:
         pos = torch.arange(n, device=out.device)[None, :]
@@ -255,6 +257,10 @@ def main():
     ap.add_argument("--row-lse", action="store_true",
                     help="score with adakv_score_lse: the window rows' log-sum-exp is supplied (prepared before "
                          "timing), so the keys are read once")
+    ap.add_argument("--row-lse-causal", action="store_true",
+                    help="score from the causal log-sum-exp a prefill leaves (keys 0 .. p + r, prepared before "
+                         "timing): adakv_lse_from_causal turns it into the scorer's own inside the timed "
+                         "scoring phase, then adakv_score_lse reads the keys once")
     ap.add_argument("--lava-online", action="store_true",
                     help="LAVa workloads: evict during a layer-by-layer prefill (each layer scored, all layers so "
                          "far re-allocated and their flat cache rebuilt after every layer)")
@@ -291,10 +297,18 @@ def main():
     w_o = data.get("w_o")
     steps_dec = cfg.decode_steps
     rows_base = ev.n_sel + cfg.instances * cfg.hkv * cfg.w
-    row_lse = None
+    row_lse = lse_causal = None
+    if args.row_lse and args.row_lse_causal:
+        print("--row-lse and --row-lse-causal exclude each other", file=sys.stderr)
+        sys.exit(2)
     if args.row_lse:
         print(f"[bench] {cfg.name}: preparing window-row log-sum-exp", file=sys.stderr, flush=True)
         row_lse = device_row_lse(cfg, data)
+        torch.cuda.synchronize()
+    if args.row_lse_causal:
+        print(f"[bench] {cfg.name}: preparing the causal window-row log-sum-exp", file=sys.stderr, flush=True)
+        lse_causal = device_row_lse(cfg, data, causal=True)
+        row_lse = torch.empty_like(lse_causal)
         torch.cuda.synchronize()
 
     # A step whose K and V fit in 1 GiB would find them in the 256 MB infinity
@@ -312,6 +326,8 @@ def main():
         if flush is not None:
             flush.zero_()
         e[0].record(stream)
+        if lse_causal is not None:
+            ev.lse_from_causal(data["q_win"], data["k"], lse_causal, out=row_lse, stream=stream)
         ev.run_score(data["q_win"], data["k"], v_arg, w_o, row_lse=row_lse)
         e[1].record(stream)
         ev.run_allocate()
@@ -375,7 +391,9 @@ def main():
                    "hq": cfg.hq, "hkv": cfg.hkv, "d": cfg.d, "n": cfg.n, "w": cfg.w, "pool": cfg.pool,
                    "budget": cfg.budget, "alpha": list(cfg.alpha), "decode_steps": steps_dec,
                    "scorer": cfg.scorer,
-                   "scoring": "single pass, window-row log-sum-exp supplied" if args.row_lse else "two passes",
+                   "scoring": ("single pass, window-row log-sum-exp supplied" if args.row_lse else
+                               "single pass from the prefill's causal log-sum-exp, corrected on the device"
+                               if args.row_lse_causal else "two passes"),
                    "infinity_cache": "flushed before each eviction" if flush is not None else "not flushed"},
         "phases_ms": {"score": sc, "allocate": al, "compact": co, "evict": evict_ms, "decode_total": dec_ms_step},
         "evict_hbm_gbps": evict_bytes(cfg) / (evict_ms * 1e-3) / 1e9,

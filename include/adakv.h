@@ -5,6 +5,7 @@
  * The path, per layer instance (one layer of one sequence):
  *   adakv_score        observation-window scores of every prefix token
  *   adakv_score_lse    the same with the window softmax normaliser supplied
+ *   adakv_lse_from_causal  that normaliser from the one a causal prefill leaves
  *   adakv_allocate     layer-wide top-B -> per-head budgets -> per-head selection
  *   adakv_compact      selected rows + window rows -> one flat variable-length cache
  *   adakv_decode_attn  decode attention over the flat cache (optional append)
@@ -186,6 +187,39 @@ adakv_status adakv_score(const adakv_shape* shape, const void* q_win, const void
 adakv_status adakv_score_lse(const adakv_shape* shape, const void* q_win, const void* k, const void* v,
                              const void* w_o, const float* row_lse, float* score, float* score2, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* The window softmax normaliser of adakv_score_lse from a causal prefill's.
+ *
+ * An attention pass over the prompt with the causal mask leaves, for window
+ * row r (position p + r) of query head j, L = the natural-log log-sum-exp of
+ * z_t = q_win[i,j,r].k[i,g,t]/sqrt(d) over keys t = 0 .. p + r (g = j / G).
+ * That is the LAVA domain ([LAVa-notes] Definition 1).  The other scorers'
+ * domains differ from it by window keys only, so the call reads the w window
+ * rows of K and rewrites L in float64:
+ *   SNAPKV, CRITICALKV  prefix t < p ([AdaKV-notes] Algorithm 2, step 2):
+ *                       out = L + ln(1 - sum_{t=p}^{p+r} exp(z_t - L))
+ *   LAPROX              all n keys ([LaProx] Section 4.1, Algorithm 1):
+ *                       out = L + ln(1 + sum_{t=p+r+1}^{n-1} exp(z_t - L))
+ *   LAVA                out = L
+ * out is what adakv_score_lse takes as row_lse.
+ *
+ *   q_win      [I, hq, w, d]  dtype
+ *   k          [I, hkv, n, d] dtype    only rows p .. n-1 of each head are read
+ *   lse_causal [I, hq, w] float32      L, finite
+ *   lse_out    [I, hq, w] float32 out  may be lse_causal itself (in place)
+ *   row_flag   [I, hq, w] int32 out, or NULL:
+ *                0  the row is well conditioned;
+ *                1  prefix domain, and the prefix holds less than 2^-7 of the
+ *                   causal mass (1 - sum < 2^-7).  The subtraction multiplies
+ *                   the absolute error of L by 1 / (1 - sum), so more than 7
+ *                   bits of L's precision are lost; where rounding in L leaves
+ *                   no positive share at all, out = L - 60 ln 2.  Score such
+ *                   rows with adakv_score (two passes) instead;
+ *                2  L, or the result, is not finite (out = L).
+ * Supported shapes: those of adakv_score (pool, hidden and eps are not read).
+ * No workspace; nothing is allocated. */
+adakv_status adakv_lse_from_causal(const adakv_shape* shape, const void* q_win, const void* k,
+                                   const float* lse_causal, float* lse_out, int32_t* row_flag, void* stream);
 
 /* Budget allocation and selection.  Scores must be finite and >= 0 (-0.0 is
  * treated as +0.0).  Ranking: a larger score first; equal scores by the smaller

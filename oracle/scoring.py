@@ -94,19 +94,15 @@ def lse_from_causal(lse_causal: np.ndarray, q_win: np.ndarray, k: np.ndarray, sc
     for i in range(hq):
         g = i // G
         for r in range(w):
-            if scorer == "laprox":
-                keys = range(p + r + 1, n)
-            else:
-                keys = range(p, p + r + 1)
-            s = 0.0
-            for t in keys:
-                z = float(q_win[i, r] @ k[g, t]) / math.sqrt(d)
-                s += math.exp(z - lse_causal[i, r])
+            keys = slice(p + r + 1, n) if scorer == "laprox" else slice(p, p + r + 1)
+            z = (k[g, keys] @ q_win[i, r]) / math.sqrt(d)
+            s = float(np.exp(z - lse_causal[i, r]).sum())
             if scorer == "laprox":
                 lse[i, r] = lse_causal[i, r] + math.log1p(s)
             else:
                 keep[i, r] = 1.0 - s
-                lse[i, r] = lse_causal[i, r] + math.log(keep[i, r])
+                # no prefix mass left (rounding in a supplied lse_causal): -inf
+                lse[i, r] = lse_causal[i, r] + math.log(keep[i, r]) if keep[i, r] > 0 else -math.inf
     return lse, keep
 
 

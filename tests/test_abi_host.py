@@ -106,6 +106,24 @@ def test_score_lse_validates_like_score(L):
     assert score_lse_status(L, _shape(w=65)) == lib.ADAKV_EUNSUPPORTED
 
 
+def causal_status(L, shape, q=FAKE, k=FAKE, lse=FAKE, out=FAKE, flag=None):
+    return L.adakv_lse_from_causal(ctypes.byref(shape), q, k, lse, out, flag, None)
+
+
+def test_lse_from_causal_rejects(L):
+    s = _shape()
+    assert causal_status(L, s, lse=None) == lib.ADAKV_EINVAL
+    assert causal_status(L, s, out=None) == lib.ADAKV_EINVAL
+    assert causal_status(L, s, q=None) == lib.ADAKV_EINVAL
+    assert causal_status(L, s, k=FAKE + 8) == lib.ADAKV_EINVAL
+    assert causal_status(L, s, flag=FAKE + 4) == lib.ADAKV_EINVAL       # the flags are optional, but aligned
+    assert causal_status(L, _shape(hq=33)) == lib.ADAKV_EINVAL
+    assert causal_status(L, _shape(n=32)) == lib.ADAKV_EINVAL
+    assert causal_status(L, _shape(w=65)) == lib.ADAKV_EUNSUPPORTED
+    assert causal_status(L, _shape(hq=80, hkv=8)) == lib.ADAKV_EUNSUPPORTED
+    assert causal_status(L, _shape(d=96)) == lib.ADAKV_EUNSUPPORTED
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(hq=33), lib.ADAKV_EINVAL),            # hq not a multiple of hkv
     (dict(n=32), lib.ADAKV_EINVAL),             # no prefix: n <= w

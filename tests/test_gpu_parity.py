@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from adaptive_head_budget_amd import configs, pipeline, synth
+from adaptive_head_budget_amd import configs, lib, pipeline, synth
 from adaptive_head_budget_amd.configs import scaled
 from oracle import allocation, cache, scoring
 from parity_util import (assert_decode_close, assert_scores_close, check_flat, check_lava_layer_budgets,
@@ -30,12 +30,16 @@ def _w(x, dtype):
     return synth.widen(x, dtype)
 
 
-def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, single_pass=False, inst_budget=None):
+def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, single_pass=False, inst_budget=None,
+             causal_lse=False):
     """Run score -> allocate -> compact -> decode on numpy-drawn inputs and
     check every stage.  Returns the Eviction object.  single_pass: score
     through adakv_score_lse with the oracle's window-row log-sum-exp (rounded
-    to float32, the same input for both sides).  inst_budget: per-instance
-    budgets (preset layer budgets) instead of `budget`."""
+    to float32, the same input for both sides).  causal_lse: the same, but the
+    input is the causal statistic a prefill leaves (keys 0 .. p + r, rounded
+    to float32), turned into the scorer's own by adakv_lse_from_causal on the
+    device and by the oracle's lse_from_causal on the host.  inst_budget:
+    per-instance budgets (preset layer budgets) instead of `budget`."""
     log(f"case {label}: {cfg.name} I={I} n={n} budget={budget} reserve={reserve} steps={steps}")
     if steps != cfg.decode_steps:
         cfg = scaled(cfg, decode_steps=steps)       # draws of q, k, v do not depend on this
@@ -55,20 +59,27 @@ def run_case(cfg, I, n, budget, reserve, steps, label, check_scores_of=None, sin
     w = cfg.w
     k64 = [_w(x["k"], dt) for x in insts]
     v64 = [_w(x["v"], dt) for x in insts]
-    lse32 = None
-    if single_pass:
+    lse32 = lse_ref = lse_dev = None
+    if causal_lse:
+        lc32 = np.stack([scoring.window_lse(_w(insts[i]["q_win"], dt), k64[i], causal=True)
+                         for i in range(I)]).astype(np.float32)
+        lse_dev = ev.lse_from_causal(q, k, torch.from_numpy(lc32).cuda())
+        lse_ref = np.stack([scoring.lse_from_causal(lc32[i].astype(np.float64), _w(insts[i]["q_win"], dt), k64[i],
+                                                    cfg.scorer)[0] for i in range(I)])
+    elif single_pass:
         lse32 = np.stack([scoring.window_lse(_w(insts[i]["q_win"], dt), k64[i], causal=cfg.scorer == "lava",
                                              full=cfg.scorer == "laprox")
                           for i in range(I)]).astype(np.float32)
-    ev.run_score(q, k, v if cfg.scorer != "snapkv" else None, w_o,
-                 row_lse=None if lse32 is None else torch.from_numpy(lse32).cuda())
+        lse_dev = torch.from_numpy(lse32).cuda()
+        lse_ref = lse32.astype(np.float64)
+    ev.run_score(q, k, v if cfg.scorer != "snapkv" else None, w_o, row_lse=lse_dev)
     torch.cuda.synchronize()
     score = ev.score.cpu().numpy()
     score2 = ev.score2.cpu().numpy() if ev.score2 is not None else None
     for i in (range(I) if check_scores_of is None else check_scores_of):
         ref, ref2 = oracle_scores(cfg.scorer, _w(insts[i]["q_win"], dt), k64[i], v64[i],
                                   _w(wo_of(i), dt) if w_o is not None else None, cfg.pool, cfg.eps,
-                                  None if lse32 is None else lse32[i].astype(np.float64))
+                                  None if lse_ref is None else lse_ref[i])
         worst = assert_scores_close(score[i], ref, f"{label} score inst {i}")
         if ref2 is not None:
             assert_scores_close(score2[i], ref2, f"{label} composite inst {i}")
@@ -269,6 +280,120 @@ def test_register_k_single_pass(gpu_lib):
     cfg = scaled(configs.LLAMA8B_LAYER, name="kr_single_pass", reserve=1, decode_steps=1)
     n = 1000
     run_case(cfg, 256, n, cfg.hkv * cfg.w + (cfg.hkv * (n - cfg.w)) // 5, 1, 1, cfg.name, single_pass=True)
+
+
+# scorer, dtype, hq, hkv, d, w, n: GQA groups 1..8, window lengths with a
+# ragged last chunk of eight keys, up to 512 rows (and 64 KiB of window keys)
+# per workgroup
+CAUSAL_CASES = [
+    ("snapkv", "bf16", 32, 8, 128, 32, 300),
+    ("criticalkv", "bf16", 40, 8, 128, 32, 257),
+    ("laprox", "bf16", 32, 8, 128, 32, 300),
+    ("lava", "bf16", 32, 8, 128, 32, 300),
+    ("snapkv", "bf16", 64, 8, 128, 64, 200),
+    ("laprox", "bf16", 64, 8, 64, 64, 200),
+    ("snapkv", "bf16", 8, 8, 64, 13, 150),
+    ("snapkv", "f32", 4, 4, 16, 4, 64),
+    ("laprox", "f32", 12, 4, 64, 21, 90),
+    ("snapkv", "bf16", 10, 2, 128, 1, 40),
+]
+
+
+def _causal_inputs(scorer, dtype, hq, hkv, d, w, n, I, window_gain=0.0):
+    """Instances of a scaled Llama layer, the window keys optionally pulled
+    towards each head group's first query head (gain a: row j's own key gets
+    a * (j+1)/w * 4 sqrt(d) along that query), so the window holds most of
+    the causal mass of the later rows."""
+    base = configs.TINY_MHA if dtype == "f32" else configs.LLAMA8B_LAYER
+    cfg = scaled(base, name=f"causal_{scorer}_{hq}_{hkv}_{d}_{w}", hq=hq, hkv=hkv, d=d, w=w, scorer=scorer,
+                 tau=("loguniform", 0.1, 3.0), hidden=256 if scorer in ("criticalkv", "laprox") else 0)
+    insts, st = _stack(cfg, I, n)
+    q64 = _w(st["q_win"], dtype)
+    k64 = _w(st["k"], dtype)
+    if window_gain:
+        G, p = hq // hkv, n - w
+        for i in range(I):
+            for g in range(hkv):
+                for j in range(w):
+                    qj = q64[i, g * G, j]
+                    k64[i, g, p + j] = (window_gain * (j + 1) / w * 4 * np.sqrt(d)) * qj / np.linalg.norm(qj)
+        k_st = synth._store(k64.astype(np.float32), dtype)
+        k64 = _w(k_st, dtype)
+        st["k"] = k_st
+    return cfg, st, q64, k64
+
+
+def _check_causal(cfg, st, q64, k64, label, in_place=False):
+    dt, I = cfg.dtype, q64.shape[0]
+    lc32 = np.stack([scoring.window_lse(q64[i], k64[i], causal=True) for i in range(I)]).astype(np.float32)
+    ref, keep = zip(*[scoring.lse_from_causal(lc32[i].astype(np.float64), q64[i], k64[i], cfg.scorer)
+                      for i in range(I)])
+    ref, keep = np.stack(ref), np.stack(keep)
+    lc = torch.from_numpy(lc32).cuda()
+    flag = torch.full(lc.shape, -1, dtype=torch.int32, device="cuda")
+    out = lc if in_place else torch.full_like(lc, float("nan"))
+    lib.adakv_lse_from_causal(pipeline.make_shape(cfg, I, k64.shape[2]), pipeline.to_device(st["q_win"], dt),
+                              pipeline.to_device(st["k"], dt), lc, out, flag)
+    torch.cuda.synchronize()
+    got, fl = out.cpu().numpy().astype(np.float64), flag.cpu().numpy()
+    want_flag = np.where(keep < 2.0 ** -7, 1, 0)
+    # the flag is a float64 comparison on both sides: no row may sit at the threshold
+    assert np.all(np.abs(keep - 2.0 ** -7) > 1e-12), f"{label}: a row sits at the flag threshold"
+    assert np.array_equal(fl, want_flag), f"{label}: flags differ at {np.argwhere(fl != want_flag)[:5]}"
+    assert np.isfinite(got).all(), f"{label}: non-finite statistic"
+    tight = keep >= 2.0 ** -20
+    ulp = np.spacing(np.abs(ref[tight]).astype(np.float32)).astype(np.float64)
+    err = np.abs(got[tight] - ref[tight])
+    assert np.all(err <= ulp), f"{label}: worst {np.max(err / ulp):.2f} float32 ulp"
+    lost = keep <= 2.0 ** -60
+    assert np.array_equal(got[lost], (lc32.astype(np.float64) + np.log(2.0 ** -60)).astype(np.float32)[lost])
+    log(f"  {label}: {tight.sum()} rows within 1 float32 ulp, {int(want_flag.sum())} flagged, "
+        f"{int(lost.sum())} with no prefix share left")
+    return int(want_flag.sum()), int(lost.sum())
+
+
+@pytest.mark.parametrize("scorer,dtype,hq,hkv,d,w,n", CAUSAL_CASES)
+def test_lse_from_causal(gpu_lib, scorer, dtype, hq, hkv, d, w, n):
+    """Every corrected window-row statistic against the oracle's, to one
+    float32 ulp (both sides correct in float64 and the device rounds once),
+    and every row's precision flag."""
+    cfg, st, q64, k64 = _causal_inputs(scorer, dtype, hq, hkv, d, w, n, 3)
+    log(f"case lse_from_causal {cfg.name} n={n}")
+    _check_causal(cfg, st, q64, k64, cfg.name)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_lse_from_causal_window_dominated(gpu_lib, in_place):
+    """Window keys that carry most of the later rows' causal mass: rows below
+    the 2^-7 prefix share are flagged, rows where the float32 input leaves no
+    share get L - 60 ln 2, the rest match; also written over the input."""
+    cfg, st, q64, k64 = _causal_inputs("snapkv", "bf16", 32, 8, 128, 32, 300, 2, window_gain=0.4)
+    log(f"case lse_from_causal window-dominated in_place={in_place}")
+    flagged, lost = _check_causal(cfg, st, q64, k64, "window-dominated", in_place=in_place)
+    assert flagged > 0 and lost > 0
+
+
+@pytest.mark.parametrize("scorer", ["snapkv", "criticalkv", "laprox", "lava"])
+def test_causal_single_pass(gpu_lib, scorer):
+    """The whole path scored from a prefill's causal statistic: corrected on
+    the device, then adakv_score_lse; scores against the oracle's scores from
+    the oracle's correction of the same float32 input."""
+    if scorer == "snapkv":     # enough instances for the register-K emit pass
+        cfg = scaled(configs.LLAMA8B_LAYER, name="causal_e2e_snapkv", reserve=1, decode_steps=1)
+        n = 1000
+        run_case(cfg, 256, n, cfg.hkv * cfg.w + (cfg.hkv * (n - cfg.w)) // 5, 1, 1, cfg.name, causal_lse=True)
+    elif scorer == "criticalkv":
+        cfg = scaled(configs.QWEN32B_CK, name="causal_e2e_ck", hidden=256)
+        n = 700
+        run_case(cfg, 1, n, cfg.hkv * cfg.w + (cfg.hkv * (n - cfg.w)) // 4, 0, 0, cfg.name, causal_lse=True)
+    elif scorer == "laprox":
+        cfg = scaled(configs.MISTRAL7B_LAPROX, layers=2, hidden=256, name="causal_e2e_laprox")
+        n = 600
+        run_case(cfg, 2, n, 2 * cfg.w * cfg.hkv + cfg.hkv * (n - cfg.w) // 3, 0, 0, cfg.name, causal_lse=True)
+    else:
+        cfg = scaled(configs.MISTRAL7B_LAVA, layers=3, name="causal_e2e_lava")
+        n = 500
+        run_case(cfg, 3, n, 3 * cfg.w * cfg.hkv + cfg.hkv * (n - cfg.w) // 2, 0, 0, cfg.name, causal_lse=True)
 
 
 def test_budget_extremes(gpu_lib):
