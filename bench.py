@@ -250,8 +250,8 @@ def bench_lava_online(args, cfg, data):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama3.1-8b_32L_b4_n32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--row-lse", action="store_true",
@@ -403,6 +403,7 @@ def main():
                                if args.row_lse_causal else "two passes"),
                    "infinity_cache": "flushed before each eviction" if flush is not None else "not flushed"},
         "phases_ms": {"score": sc, "allocate": al, "compact": co, "evict": evict_ms, "decode_total": dec_ms_step},
+        "evicted_kv_entries_per_s": value * cfg.hkv,
         "evict_hbm_gbps": evict_bytes(cfg) / (evict_ms * 1e-3) / 1e9,
         "score_hbm_gbps": score_bytes(cfg) / (sc * 1e-3) / 1e9,
         "compact_hbm_gbps": compact_bytes(cfg) / (co * 1e-3) / 1e9,
