@@ -475,3 +475,13 @@ def test_lava_online_first_step_keeps_at_most_the_layer():
     st = allocation.lava_online_steps(u, L * w * hkv + 12, w)
     assert list(st[-1]["layer_budgets"]) == [4, 4, 4]
     assert list(st[1]["layer_budgets"]) == [7, 7]             # (12 + 3*2 - 2*2) / 2 = 7 each
+
+
+def test_largest_remainder_ties_go_to_lower_index():
+    """Equal fractional parts: the extra units go to the lower indices first
+    (the tie order of the LAVa layer split); larger parts before smaller."""
+    np.testing.assert_array_equal(allocation.largest_remainder(np.array([1.5, 2.5, 0.5]), 5), [2, 3, 0])
+    np.testing.assert_array_equal(allocation.largest_remainder(np.array([0.5, 0.5, 0.5, 0.5]), 2), [1, 1, 0, 0])
+    np.testing.assert_array_equal(allocation.largest_remainder(np.array([0.2, 0.7, 0.7, 1.4]), 3), [0, 1, 1, 1])
+    # exact integers take no extra unit
+    np.testing.assert_array_equal(allocation.largest_remainder(np.array([2.0, 1.0, 0.0]), 3), [2, 1, 0])

@@ -2,6 +2,7 @@
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import allocation, bounds, cache, scoring
@@ -104,3 +105,46 @@ def test_bounds_hold_on_produced_and_random_masks():
     full = np.ones((hkv, n), dtype=bool)
     loss, eps = bounds.adakv_theorem31(q, k, v, w_o, full)
     assert loss < 1e-12 and abs(eps) < 1e-9
+
+
+def _two_entry_case(a, c):
+    """One head, d = 1, two cached entries with attention (a, 1 - a); the rows
+    of V W^O are +c e_1 and -c e_1; entry 0 kept.  The exact loss is
+    |c - (2a - 1) c| = 2 c (1 - a)."""
+    z1 = math.log((1 - a) / a)            # softmax([0, z1]) = (a, 1 - a)
+    q = np.array([[1.0]])
+    k = np.array([[[0.0], [z1]]])         # d = 1: logits are q.k exactly
+    v = np.array([[[1.0], [-1.0]]])
+    w_o = np.array([[c, 0.0, 0.0]])
+    keep = np.array([[True, False]])
+    return q, k, v, w_o, keep
+
+
+@pytest.mark.parametrize("a", [0.9, 0.6, 0.25])
+def test_bounds_are_attained(a):
+    """The three bounds are tight: on the two-entry case each equals the loss
+    2 c (1 - a) (Ada-KV notes, Theorem 3.1 with h = 1 and C = c; LAVa notes,
+    Theorem 1 with C_hat = c and V_bar = 1; CriticalKV notes, theta with
+    sum N A = a), so a looser constant or a dropped term cannot pass."""
+    c = 1.7
+    q, k, v, w_o, keep = _two_entry_case(a, c)
+    want = 2 * c * (1 - a)
+    loss, eps = bounds.adakv_theorem31(q, k, v, w_o, keep)
+    assert loss == pytest.approx(want, rel=1e-12) and eps == pytest.approx(want, rel=1e-12)
+    loss2, b2 = bounds.lava_theorem1(q, k, v, w_o, keep)
+    assert loss2 == pytest.approx(want, rel=1e-12) and b2 == pytest.approx(want, rel=1e-12)
+    (l3, th), = bounds.criticalkv_theta(q, k, v, w_o, keep)
+    assert l3 == pytest.approx(want, rel=1e-12) and th == pytest.approx(want, rel=1e-12)
+
+
+def test_bound_pins_catch_planted_constants():
+    """A bound with its constant doubled, or the kept mass counted twice, is
+    no longer attained (or no longer a bound) on the two-entry case."""
+    a, c = 0.6, 1.7
+    q, k, v, w_o, keep = _two_entry_case(a, c)
+    loss, eps = bounds.adakv_theorem31(q, k, v, w_o, keep)
+    hq = 1
+    looser = 2 * hq * (2 * c) - 2 * (2 * c) * a          # C doubled
+    dropped = 2 * hq * c - 4 * c * a                      # kept mass counted twice
+    assert looser != pytest.approx(loss, rel=1e-6)
+    assert not loss <= dropped * (1 + 1e-12)
