@@ -12,10 +12,14 @@
 //    wave streams its own 64-key blocks of K straight into its A-operand
 //    registers, so no K tile is staged through LDS and no barrier follows the
 //    prologue; a wave covers all G*w rows of its keys, so its row sums need one
-//    lane butterfly per block;
+//    lane butterfly per block.  LAVa's pass 2 on this layout (kr_lava_kernel)
+//    swaps the MFMA operands so a lane holds four rows of one key, writes the
+//    unpooled group maxima, and lava_pool_kernel pools them (LAVa pools the
+//    final vector, so no pooling halo is computed);
 //  * LDS-tiled (score_stats_kernel, score_emit_kernel; every other geometry,
-//    LAVa's and CriticalKV's emit passes, small calls): 128-key K tiles staged
-//    through LDS, each wave one query head with its rows' operands in registers.
+//    CriticalKV's emit pass, LAVa's for one instance, small calls): 128-key K
+//    tiles staged through LDS, each wave one query head with its rows'
+//    operands in registers.
 //
 // Definitions followed:
 //  * Ada-KV notes, Algorithm 2 ("Ada-KV Integration") steps 2-4: softmax of the
@@ -700,6 +704,217 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
 }
 
+// Logits of key block mb against a window-row block with the MFMA operands
+// swapped: lane (gq, c) gets rows 4*gq + j (j < 4) of the row block against
+// block key kr_key(mb, c).  The products and their order are kr_logits'.
+__device__ __forceinline__ f32x4 kr_logits_t(const bf16x8 (&kf)[4][4], int mb, const bf16x8 (&qo)[4]) {
+  f32x4 p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qo[0], kf[mb][0], zero4(), 0, 0, 0);
+  f32x4 p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qo[2], kf[mb][2], zero4(), 0, 0, 0);
+  p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qo[1], kf[mb][1], p0, 0, 0, 0);
+  p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qo[3], kf[mb][3], p1, 0, 0, 0);
+  f32x4 z;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) z[j] = p0[j] + p1[j];
+  return z;
+}
+
+// Pass 2 of LAVa on the register-K path.  LAVa pools the final vector, not
+// every row, so no pooling halo is computed here: the kernel writes the
+// unpooled group maximum max_i S_i[t] (S_i[t] the sum of head i's causal
+// weights of key t over its w rows) for keys t < ke = min(n, p + rho), and
+// lava_pool_kernel pools it and applies max_k ||V[k]||_1 / w.  The workgroup
+// covers keys [chunk*kpw, +kpw) of one KV head, wave v its 64-key blocks v,
+// v+4, ...  With the operands swapped, a lane holds four rows of one key per
+// row block, so a head's rows are summed inside the lane and then over the
+// four lane groups by two lane moves; one FMA, one exp and one FMA per logit.
+template <int G, int NBW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void kr_lava_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float2* __restrict__ part,
+    const float* __restrict__ row_lse, float* __restrict__ smax, int inst0, int hq, int hkv, int n, int w, int p,
+    int ke, int nsub, int kpw, float c2) {
+  constexpr int NBT = G * NBW;
+  extern __shared__ __align__(16) char lds[];
+  const int chunk = blockIdx.x, g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gq = lane >> 4, c = lane & 15;
+  kr_stage_q<G, NBW>(lds, q, inst, hq, g, w);
+  const int Gw = G * w;
+
+  // Row statistics (reference, 1/sum) of rows (nb, c) in LDS after the
+  // queries, merged exactly as in kr_emit_kernel.
+  float2* rstat = reinterpret_cast<float2*>(lds + NBT * 4096);
+  for (int nb = wv; nb < NBT; nb += KR_WAVES) {
+    const int h = nb / NBW, r = (nb % NBW) * 16 + c;
+    const bool ok = r < w;
+    float mc = 0.f, il_row = 0.f;
+    if (row_lse != nullptr) {
+      if (ok) {
+        const double x = (double)row_lse[((size_t)inst * hq + (size_t)g * G + h) * w + r] * 1.4426950408889634;
+        const float hi = (float)x;
+        mc = hi;
+        il_row = fast_exp2(-(float)(x - (double)hi));
+      }
+    } else {
+      float m = -INFINITY, l = 0.f;
+      if (ok) {
+        const float2* pr = part + ((size_t)il * hkv + g) * nsub * (size_t)Gw + h * w + r;
+        for (int ch0 = gq; ch0 < nsub; ch0 += 32) {
+          float2 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int ch = ch0 + 4 * u;
+            v[u] = ch < nsub ? pr[(size_t)ch * Gw] : make_float2(-INFINITY, 0.f);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) merge_ml(m, l, v[u].x, v[u].y);
+        }
+      }
+#pragma unroll
+      for (int mask = 16; mask <= 32; mask <<= 1) {
+        const float om = shfl_xor(m, mask), ol = shfl_xor(l, mask);
+        merge_ml(m, l, om, ol);
+      }
+      mc = ok ? m : 0.f;
+      il_row = ok ? 1.0f / l : 0.f;
+    }
+    if (gq == 0) rstat[nb * 16 + c] = make_float2(mc, il_row);
+  }
+  __syncthreads();
+
+  const uint16_t* kh = k + ((size_t)inst * hkv + g) * (size_t)n * 128;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kh), 0, n * KR_QROWB, 0x00020000);
+  int koff[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) koff[mb] = kr_key(mb, c) * KR_QROWB + 16 * gq;
+  int qoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qoff[ks] = kr_qoff(ks, c, gq);
+  const int c0 = chunk * kpw, c1 = min(c0 + kpw, ke);
+  float* out = smax + ((size_t)il * hkv + g) * (size_t)ke;
+
+  auto block = [&](const bf16x8 (&kf)[4][4], int b0) {
+    float acc[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[h][mb] = 0.f;
+    auto logits = [&](int nb, f32x4 (&z)[4]) {
+      bf16x8 qo[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qo[ks] = *reinterpret_cast<const bf16x8*>(lds + qoff[ks] + 4096 * nb);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) z[mb] = kr_logits_t(kf, mb, qo);
+    };
+    auto fold = [&](auto interior_tag) {
+      constexpr bool INTERIOR = decltype(interior_tag)::value;
+      // software pipeline over the window-row blocks: the MFMAs of block
+      // nb + 1 are issued between the vector instructions of block nb
+      f32x4 zc[4];
+      logits(0, zc);
+#pragma unroll
+      for (int nb = 0; nb < NBT; ++nb) {
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 zn[4];
+        if (nb + 1 < NBT) logits(nb + 1, zn);
+        const int h = nb / NBW;
+        // (reference, 1/sum) of the lane's rows 4*gq + j of block nb
+        const f32x4 s01 = *reinterpret_cast<const f32x4*>(rstat + nb * 16 + 4 * gq);
+        const f32x4 s23 = *reinterpret_cast<const f32x4*>(rstat + nb * 16 + 4 * gq + 2);
+        const float mc[4] = {s01[0], s01[2], s23[0], s23[2]};
+        const float ir[4] = {s01[1], s01[3], s23[1], s23[3]};
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int key = b0 + kr_key(mb, c);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float e = fast_exp2(fmaf(zc[mb][j], c2, -mc[j]));
+            if (INTERIOR) {
+              acc[h][mb] = fmaf(e, ir[j], acc[h][mb]);
+            } else {
+              const int r = (nb % NBW) * 16 + 4 * gq + j;
+              acc[h][mb] += (key <= p + r && key < n) ? e * ir[j] : 0.f;
+            }
+          }
+        }
+        if (nb + 1 < NBT) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four vector instructions
+          }
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) zc[mb] = zn[mb];
+        }
+      }
+    };
+    // keys below p are inside every row's causal domain (and below n)
+    if (b0 + KB <= p) fold(std::true_type{});
+    else fold(std::false_type{});
+    // each head's sum over its rows: the four lane groups hold rows 4*gq .. 4*gq+3
+    // of every block; then the maximum over the group's heads
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      float m = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float x = acc[h][mb];
+        x += shfl_xor(x, 16);
+        x += shfl_xor(x, 32);
+        m = h == 0 ? x : fmaxf(m, x);
+      }
+      const int key = b0 + kr_key(mb, c);
+      if (gq == 0 && key < ke) out[key] = m;
+    }
+  };
+  for (int b0 = c0 + wv * KB; b0 < c1; b0 += KR_WAVES * KB) {
+    bf16x8 kf[4][4];
+    kr_load<4>(kf, rs, koff, b0);
+    block(kf, b0);
+  }
+}
+
+// LAVa scores from kr_lava_kernel's group maxima: score[t] = max_k ||V[k]||_1 /
+// w times the maximum of smax over keys t - RHO .. t + RHO inside [0, ke), for
+// t < p (every group maximum is >= 0, so keys outside the range count as 0).
+// A workgroup pools LP_KEYS keys of one KV head from an LDS copy of them and
+// their halo; V's norm maximum comes from vbar_kernel's block maxima.
+constexpr int LP_KEYS = 2048;
+template <int RHO>
+__global__ __launch_bounds__(256) void lava_pool_kernel(const float* __restrict__ smax,
+                                                        const float* __restrict__ vpart, int nvblk,
+                                                        float* __restrict__ score, int inst0, int hkv, int p, int ke,
+                                                        int w) {
+  const int g = blockIdx.y, il = blockIdx.z, inst = inst0 + il;
+  __shared__ float tile[LP_KEYS + 2 * RHO];
+  __shared__ float vsc;
+  const int t0 = blockIdx.x * LP_KEYS;
+  const float* sm = smax + ((size_t)il * hkv + g) * (size_t)ke;
+  for (int i = threadIdx.x; i < LP_KEYS + 2 * RHO; i += 256) {
+    const int t = t0 - RHO + i;
+    tile[i] = (t >= 0 && t < ke) ? sm[t] : 0.f;
+  }
+  if (threadIdx.x < WAVE) {
+    float vb = 0.f;
+    for (int b = threadIdx.x; b < nvblk; b += WAVE) vb = fmaxf(vb, vpart[((size_t)inst * hkv + g) * nvblk + b]);
+#pragma unroll
+    for (int mask = 1; mask < 64; mask <<= 1) vb = fmaxf(vb, shfl_xor(vb, mask));
+    if (threadIdx.x == 0) vsc = vb / (float)w;
+  }
+  __syncthreads();
+  float* out = score + ((size_t)inst * hkv + g) * p;
+#pragma unroll
+  for (int u = 0; u < LP_KEYS / 256; ++u) {
+    const int i = u * 256 + threadIdx.x;
+    if (t0 + i < p) {
+      float m = tile[RHO + i];
+#pragma unroll
+      for (int o = 1; o <= RHO; ++o) m = fmax3(m, tile[RHO + i - o], tile[RHO + i + o]);
+      out[t0 + i] = vsc * m;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- pass 2
 // EMIT_SQ: the SNAP path without pooling on squared weights, written per head
 // unscaled (sum over rows of A^2).
@@ -1125,6 +1340,28 @@ KrEmitFn kr_emit_pick(const Geo& g) {
     default: return nullptr;
   }
 }
+using KrLavaFn = void (*)(const uint16_t*, const uint16_t*, const float2*, const float*, float*, int, int, int, int,
+                          int, int, int, int, int, float);
+template <int G>
+KrLavaFn kr_lava_for(int w) {
+  if (w <= 16) return kr_lava_kernel<G, 1>;
+  if constexpr (G <= 5) return kr_lava_kernel<G, 2>;
+  return nullptr;
+}
+KrLavaFn kr_lava_pick(const Geo& g) {
+  if (!kr_geometry(g) || g.scorer != ADAKV_SCORE_LAVA) return nullptr;
+  switch (g.G) {
+    case 1: return kr_lava_for<1>(g.w);
+    case 2: return kr_lava_for<2>(g.w);
+    case 4: return kr_lava_for<4>(g.w);
+    case 5: return kr_lava_for<5>(g.w);
+    case 8: return kr_lava_for<8>(g.w);
+    default: return nullptr;
+  }
+}
+// Keys whose LAVa group maximum the pooling of the prefix scores reads.
+int lava_keys(const Geo& g) { return std::min(g.n, g.p + (g.pool - 1) / 2); }
+
 // Resident workgroups of a register-K kernel on the device (one round of them
 // covers a launch).
 long kr_resident_wgs(const void* fn, size_t lds, int cus) {
@@ -1144,7 +1381,7 @@ struct ScorePlan {
   int ib;        // instances per batch
   int nchunk;    // stats chunks per head
   int kend;      // end of the widest row domain
-  size_t off_part, off_heads, off_vbar, off_fac, total;
+  size_t off_part, off_heads, off_vbar, off_fac, off_smax, total;
 };
 
 ScorePlan plan_score(const Geo& g) {
@@ -1169,6 +1406,9 @@ ScorePlan plan_score(const Geo& g) {
   if (g.scorer == ADAKV_SCORE_LAVA) off = align_up(off + (size_t)g.I * g.hkv * vbar_blocks(g) * sizeof(float), 256);
   P.off_fac = off;
   off = align_up(off + factor_ws_bytes(g), 256);
+  P.off_smax = off;   // LAVa on the register-K path: unpooled group maxima of a batch
+  if (g.scorer == ADAKV_SCORE_LAVA && kr_geometry(g))
+    off = align_up(off + (size_t)P.ib * g.hkv * lava_keys(g) * sizeof(float), 256);
   P.total = off;
   return P;
 }
@@ -1211,8 +1451,10 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   const int ktiles = (P.kend + TILE - 1) / TILE;
   KrStatsFn krs = nullptr;
   KrEmitFn kre = nullptr;
+  KrLavaFn krl = nullptr;
   size_t kr_lds = 0, kr_lds_e = 0;
-  long krs_res = 0, kre_res = 0;
+  long krs_res = 0, kre_res = 0, krl_res = 0;
+  const int ke = lava_keys(g);
   if constexpr (sizeof(T) == 2 && D == 128) {
     if (kr_geometry(g) && !laprox) {
       // only where every resident workgroup gets several blocks of each pass
@@ -1228,6 +1470,13 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
       if (kre != nullptr) {
         kre_res = kr_resident_wgs(reinterpret_cast<const void*>(kre), kr_lds_e, cus > 0 ? cus : 256);
         if (blocks < KR_MIN_BLOCKS * kre_res) kre = nullptr;
+      }
+      // the pooling launch it adds costs a one-instance call (the online
+      // prefill's) what the faster emit saves
+      krl = (P.ib >= 2 && (krs != nullptr || row_lse != nullptr)) ? kr_lava_pick(g) : nullptr;
+      if (krl != nullptr) {
+        krl_res = kr_resident_wgs(reinterpret_cast<const void*>(krl), kr_lds_e, cus > 0 ? cus : 256);
+        if ((long)((ke + KB - 1) / KB) * g.hkv * P.ib < KR_MIN_BLOCKS * krl_res) krl = nullptr;
       }
     }
   }
@@ -1268,7 +1517,20 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
       score_emit_kernel<T, D, NB, POOLV, EMIT_SNAP><<<g2, threads, lds_emit, st>>>(                          \
           qt, kt, part, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
   } while (0)
-    if (kre != nullptr && heads == nullptr) {
+    if (krl != nullptr) {
+      float* smax = reinterpret_cast<float*>(ws + P.off_smax);
+      const int kpw_l = kr_keys_per_wg((long)((ke + KB - 1) / KB) * g.hkv * ni, krl_res, KR_WAVES * KB);
+      krl<<<dim3((ke + kpw_l - 1) / kpw_l, g.hkv, ni), KR_WAVES * WAVE, kr_lds_e, st>>>(
+          reinterpret_cast<const uint16_t*>(qt), reinterpret_cast<const uint16_t*>(kt), part, row_lse, smax, i0,
+          g.hq, g.hkv, g.n, g.w, g.p, ke, nchunk, kpw_l, c2);
+      const dim3 gp((g.p + LP_KEYS - 1) / LP_KEYS, g.hkv, ni);
+      switch (g.pool) {
+        case 1: lava_pool_kernel<0><<<gp, 256, 0, st>>>(smax, vpart, nvblk, score, i0, g.hkv, g.p, ke, g.w); break;
+        case 3: lava_pool_kernel<1><<<gp, 256, 0, st>>>(smax, vpart, nvblk, score, i0, g.hkv, g.p, ke, g.w); break;
+        case 5: lava_pool_kernel<2><<<gp, 256, 0, st>>>(smax, vpart, nvblk, score, i0, g.hkv, g.p, ke, g.w); break;
+        default: lava_pool_kernel<3><<<gp, 256, 0, st>>>(smax, vpart, nvblk, score, i0, g.hkv, g.p, ke, g.w); break;
+      }
+    } else if (kre != nullptr && heads == nullptr) {
       const int kpw_e = kr_keys_per_wg((long)((g.p + KB - 1) / KB) * g.hkv * ni, kre_res, KR_WAVES * KB);
       kre<<<dim3((g.p + kpw_e - 1) / kpw_e, g.hkv, ni), KR_WAVES * WAVE, kr_lds_e, st>>>(
           reinterpret_cast<const uint16_t*>(qt), reinterpret_cast<const uint16_t*>(kt), part, row_lse, score, i0,
