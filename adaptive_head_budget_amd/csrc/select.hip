@@ -1216,6 +1216,125 @@ __global__ __launch_bounds__(XB) void ada_small_kernel(const float* __restrict__
   (void)rbase;
 }
 
+// ---------------------------------------------------------------- one workgroup per row
+// Every head's own top-B_g (Ada-KV) for rows of at most RT_MAX scores, one
+// 1024-thread workgroup per row, from the state row_budget_kernel leaves
+// (pass 0 picked).  Each thread holds a contiguous run of up to RT_NPT keys of
+// the row in registers (NONE past the row's end: no prefix matches it):
+// passes 1 and 2 add the digits of the candidates into an LDS histogram, one
+// wave picks the digit, and the kept indices are written in index order from
+// the same registers (kept scores and ties counted per thread, scanned over
+// the workgroup, staged in LDS).  The same digits, picks and tie rule as the
+// chunked kernels, so the selection is identical; one launch and one read of
+// the scores instead of six launches and four reads.  Candidates of pass 1
+// share the threshold's top digit and the lanes of a wave hold keys RT_NPT
+// apart, so one LDS atomic per candidate meets little contention.
+constexpr int RT_NPT = 32;                // scores per thread
+constexpr int RT_MAX = XB * RT_NPT;
+constexpr int RT_STAGE = 8192;            // kept indices staged per window
+constexpr int RT_ROWS = 256;              // rows of a call the row kernel serves
+
+template <int PS>
+__device__ __forceinline__ RState row_pass(const uint32_t (&key)[RT_NPT], RState S, uint32_t* h, RState* st_sh) {
+  for (int b = threadIdx.x; b < NBIN; b += XB) h[b] = 0u;
+  __syncthreads();
+  const bool live = S.krem > 0 && S.prefix != NONE;   // uniform
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < RT_NPT; ++j)
+      if (in_prefix(key[j], S.prefix, PS)) atomicAdd(h + digit_of(key[j], PS), 1u);
+  }
+  __syncthreads();
+  if (threadIdx.x < WAVE) {
+    RState out = {NONE, 0};
+    if (live) {
+      uint32_t d, above;
+      wave_pick(h, pass_bins(PS), (uint32_t)S.krem, d, above);
+      out.prefix = S.prefix | (d << digit_shift(PS));
+      out.krem = S.krem - (int32_t)above;
+    }
+    if (threadIdx.x == 0) *st_sh = out;
+  }
+  __syncthreads();
+  return *st_sh;
+}
+
+__global__ __launch_bounds__(XB) void row_topk_kernel(const float* __restrict__ score, int p, int vec,
+                                                      const RState* __restrict__ rowst,
+                                                      const int64_t* __restrict__ rowbase,
+                                                      const int32_t* __restrict__ cap, int32_t* __restrict__ sel,
+                                                      int64_t sel_total) {
+  __shared__ uint32_t h[NBIN];
+  __shared__ uint32_t sh[XW + 4];
+  __shared__ RState st_sh;
+  __shared__ int32_t stage[RT_STAGE + WAVE];
+  const int r = blockIdx.x;
+  const int npt = ((p + XB - 1) / XB + 3) & ~3;   // <= RT_NPT, a multiple of 4
+  const int e0 = min(p, (int)threadIdx.x * npt);
+  const int n = min(npt, p - e0);
+  const float* row = score + (size_t)r * p;
+  uint32_t key[RT_NPT];
+#pragma unroll
+  for (int j = 0; j < RT_NPT; j += 4) {
+    if (vec) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (j < n) v = *reinterpret_cast<const f32x4*>(row + e0 + j);   // n is a multiple of 4 here
+#pragma unroll
+      for (int u = 0; u < 4; ++u) key[j + u] = (j < n) ? sel_key(v[u]) : NONE;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) key[j + u] = (j + u < n) ? sel_key(row[e0 + j + u]) : NONE;
+    }
+  }
+  RState S = rowst[r];
+  S = row_pass<1>(key, S, h, &st_sh);
+  S = row_pass<2>(key, S, h, &st_sh);
+  // emission in index order: S.prefix is the threshold T, S.krem the ties kept
+  const uint32_t quota = (S.prefix == NONE) ? 0u : (uint32_t)S.krem;
+  uint32_t n2 = 0, n1 = 0;
+#pragma unroll
+  for (int j = 0; j < RT_NPT; ++j) {
+    const int kc = klass(key[j], key[j] != NONE, false, S.prefix);
+    n2 += kc == 2 ? 1u : 0u;
+    n1 += kc == 1 ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t ex = xblock_excl_scan(n2 | (n1 << 16), sh, tot);   // p <= 2^15: no carry between halves
+  const uint32_t cnt = (tot & 0xFFFFu) + ((tot >> 16) < quota ? (tot >> 16) : quota);
+  const uint32_t tie0 = ex >> 16, loc0 = (ex & 0xFFFFu) + (tie0 < quota ? tie0 : quota);
+  const int64_t base = rowbase[r];
+  const uint32_t lim = (uint32_t)cap[r];
+  // The kept indices go through LDS in windows of RT_STAGE positions: every
+  // score is written (the kept ones of the window at their position, the
+  // others at a slot of the lane's own past the window), so no store is
+  // predicated, then the window is copied out with consecutive lanes on
+  // consecutive words.
+  const uint32_t trash = RT_STAGE + (threadIdx.x & (WAVE - 1));
+  for (uint32_t w0 = 0; w0 < cnt; w0 += RT_STAGE) {
+    // the keys marked changed: each key's class is recomputed where it is
+    // used instead of 2 * RT_NPT compare masks being kept in scalar registers
+#pragma unroll
+    for (int j = 0; j < RT_NPT; ++j) asm volatile("" : "+v"(key[j]));
+    uint32_t tie = tie0, loc = loc0;
+#pragma unroll
+    for (int j = 0; j < RT_NPT; ++j) {
+      const int kc = klass(key[j], key[j] != NONE, false, S.prefix);
+      const bool tk = kc == 2 || (kc == 1 && tie < quota);
+      tie += kc == 1 ? 1u : 0u;
+      const bool here = tk && loc >= w0 && loc - w0 < (uint32_t)RT_STAGE;
+      stage[here ? loc - w0 : trash] = e0 + j;
+      loc += tk ? 1u : 0u;
+    }
+    __syncthreads();
+    const uint32_t nw = min((uint32_t)RT_STAGE, cnt - w0);
+    for (uint32_t i = threadIdx.x; i < nw; i += XB) {
+      const uint32_t pos = w0 + i;
+      if (pos < lim && base + pos < sel_total) sel[base + pos] = stage[i];
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- workspace plan
 struct AllocPlan {
   int R, cpr, ntile, nchunk;
@@ -1401,6 +1520,14 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   row_budget_kernel<<<R, SB, 0, st>>>(hkv, mode, kP, a.alpha_num, a.alpha_den, a.ck_num, a.ck_den, g.I,
                                       preset ? klist : nullptr, preset ? kbase : nullptr, segst, cnt, rowhist, budgets,
                                       rowbase, rowk2, rowst, sel_off);
+  if (!lava && !ck && g.p <= RT_MAX && R <= RT_ROWS) {
+    // every head's own top-k and the emission, one workgroup per row: one
+    // launch instead of six while the rows fit about one round of workgroups
+    // (beyond that the chunked passes, bound by the scores' reads and spread
+    // over the chip, are faster: 117 against 129 us for 1024 rows of 32736)
+    row_topk_kernel<<<R, XB, 0, st>>>(score, g.p, vec1 ? 1 : 0, rowst, rowbase, budgets, sel, sel_total);
+    return hipGetLastError();
+  }
   // Every head's own top-k (LAVa keeps the layer threshold).
   if (!lava) {
     for (int ps = 1; ps < 3; ++ps) {
