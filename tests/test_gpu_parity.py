@@ -495,11 +495,12 @@ def test_streaming_baseline(gpu_lib, sinks):
     run_case(cfg, 4, 3000, 8 * 32 + 8 * 200 + 3, 2, 2, f"streaming sinks {sinks}")
 
 
-def test_ties_take_lower_index(gpu_lib):
+@pytest.mark.parametrize("n", [600, 3001])
+def test_ties_take_lower_index(gpu_lib, n):
     """Constant keys: every score of a head is identical, so the selection is
-    decided by the index tie-break alone."""
+    decided by the index tie-break alone (n = 600: the one-workgroup instance
+    path; n = 3001: the one-launch head top-k, rows of an odd length)."""
     cfg = scaled(configs.LLAMA8B_LAYER, name="ties", sinks=0, decode_steps=0)
-    n = 600
     inst = synth.make_instance(cfg, 0, n_override=n)
     kconst = np.broadcast_to(inst["k"][:, :1, :], inst["k"].shape).copy()
     q = pipeline.to_device(inst["q_win"][None], "bf16")
@@ -514,6 +515,18 @@ def test_ties_take_lower_index(gpu_lib):
     b, off, sel = ev.host_selection()
     r = allocation.ada_allocate(s.astype(np.float64), budget, cfg.w, cfg.alpha)
     check_selection(b[0], int(off[0]), sel[0], r["budgets"], r["sel"], "ties")
+
+
+@pytest.mark.parametrize("n,frac,I", [(9001, 1.0, 1), (9001, 0.5, 1), (3001, 0.2, 32), (3001, 0.2, 33)])
+def test_one_launch_head_topk(gpu_lib, n, frac, I):
+    """Every head's top-B_g in one launch per row (calls of at most 256 rows):
+    rows of 8969 scores (not a multiple of 4: scalar loads) with all of them
+    kept (more than one 8192-index staging window) or half, and 256 against 264
+    rows of one shape (either side of the one-launch path), every output
+    against the oracle."""
+    cfg = scaled(configs.LLAMA8B_LAYER, name=f"rowtopk_{n}_{I}", decode_steps=1, reserve=1)
+    p = n - cfg.w
+    run_case(cfg, I, n, cfg.w * cfg.hkv + int(frac * cfg.hkv * p), 1, 1, cfg.name)
 
 
 def test_deterministic_repeat(gpu_lib):
