@@ -704,7 +704,7 @@ __global__ __launch_bounds__(SB) void segment_budget_kernel(int seg_rows, int hk
     const uint32_t eq = in ? cnt[2 * (size_t)r + 1] : 0u;
     uint32_t eq_tot, f_tot;
     const uint32_t eq_before = eq_carry + block_excl_scan(eq, sh, eq_tot);
-    const uint32_t share = quota > eq_before ? min(quota - eq_before, eq) : 0u;
+    const uint32_t share = min(quota - min(quota, eq_before), eq);   // no subtraction under a condition
     const uint32_t f = (in ? (uint32_t)add : 0u) + gt + share;
     const uint32_t before = f_carry + block_excl_scan(f, sh, f_tot);
     if (in) {
@@ -828,8 +828,9 @@ __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ scor
 #pragma unroll
   for (int i = 0; i < SW; ++i) { B2 += before_sh[0][i]; B1 += before_sh[1][i]; }
   const uint32_t quota = (S.prefix == NONE) ? 0u : (uint32_t)S.krem;
-  const uint32_t qrem = quota > B1 ? quota - B1 : 0u;
-  const uint32_t pos0 = B2 + (quota < B1 ? quota : B1);
+  // ties kept by earlier chunks, and what is left (no subtraction under a condition)
+  const uint32_t qrem = quota - min(quota, B1);
+  const uint32_t pos0 = B2 + min(quota, B1);
   const int64_t base = TO_SEL ? rowbase[ch.r] : 0;
   const uint32_t lim = TO_SEL ? (uint32_t)cap[ch.r] : 0u;
 
@@ -1221,10 +1222,11 @@ __global__ __launch_bounds__(XB) void ada_small_kernel(const float* __restrict__
 // 1024-thread workgroup per row, from the state row_budget_kernel leaves
 // (pass 0 picked).  Each thread holds a contiguous run of up to RT_NPT keys of
 // the row in registers (NONE past the row's end: no prefix matches it):
-// passes 1 and 2 add the digits of the candidates into an LDS histogram, one
-// wave picks the digit, and the kept indices are written in index order from
-// the same registers (kept scores and ties counted per thread, scanned over
-// the workgroup, staged in LDS).  The same digits, picks and tie rule as the
+// passes 1 and 2 add the digits of the candidates into an LDS histogram, the
+// workgroup picks the digit (two bins per thread, one scan), and the kept
+// indices are written in index order from the same registers (kept scores
+// and ties as bit masks per thread, counts scanned over the workgroup, indices
+// staged in LDS).  The same digits, picks and tie rule as the
 // chunked kernels, so the selection is identical; one launch and one read of
 // the scores instead of six launches and four reads.  Candidates of pass 1
 // share the threshold's top digit and the lanes of a wave hold keys RT_NPT
@@ -1232,10 +1234,36 @@ __global__ __launch_bounds__(XB) void ada_small_kernel(const float* __restrict__
 constexpr int RT_NPT = 32;                // scores per thread
 constexpr int RT_MAX = XB * RT_NPT;
 constexpr int RT_STAGE = 8192;            // kept indices staged per window
-constexpr int RT_ROWS = 256;              // rows of a call the row kernel serves
+
+// Digit pick over nb bins (2048 or 512) by the whole 1024-thread workgroup:
+// thread t holds bins nb-1 - (t*bpt .. t*bpt+bpt-1), counted from the top; the
+// digit d with count(> d) < krem <= count(>= d), and count(> d).
+__device__ __forceinline__ void xblock_pick(const uint32_t* h, int nb, uint32_t krem, uint32_t* sh, uint32_t* res,
+                                            uint32_t& dig, uint32_t& above_out) {
+  const int bpt = nb >= XB ? nb / XB : 1;
+  const int t = threadIdx.x;
+  uint32_t c0 = 0, c1 = 0;
+  if (t * bpt < nb) {
+    c0 = h[nb - 1 - t * bpt];
+    if (bpt > 1) c1 = h[nb - 2 - t * bpt];
+  }
+  uint32_t total;
+  const uint32_t above = xblock_excl_scan(c0 + c1, sh, total);
+  if (above < krem && krem <= above + c0) {
+    res[0] = (uint32_t)(nb - 1 - t * bpt);
+    res[1] = above;
+  } else if (bpt > 1 && above + c0 < krem && krem <= above + c0 + c1) {
+    res[0] = (uint32_t)(nb - 2 - t * bpt);
+    res[1] = above + c0;
+  }
+  __syncthreads();
+  dig = res[0];
+  above_out = res[1];
+}
 
 template <int PS>
-__device__ __forceinline__ RState row_pass(const uint32_t (&key)[RT_NPT], RState S, uint32_t* h, RState* st_sh) {
+__device__ __forceinline__ RState row_pass(const uint32_t (&key)[RT_NPT], RState S, uint32_t* h, uint32_t* sh,
+                                           uint32_t* res) {
   for (int b = threadIdx.x; b < NBIN; b += XB) h[b] = 0u;
   __syncthreads();
   const bool live = S.krem > 0 && S.prefix != NONE;   // uniform
@@ -1245,18 +1273,15 @@ __device__ __forceinline__ RState row_pass(const uint32_t (&key)[RT_NPT], RState
       if (in_prefix(key[j], S.prefix, PS)) atomicAdd(h + digit_of(key[j], PS), 1u);
   }
   __syncthreads();
-  if (threadIdx.x < WAVE) {
-    RState out = {NONE, 0};
-    if (live) {
-      uint32_t d, above;
-      wave_pick(h, pass_bins(PS), (uint32_t)S.krem, d, above);
-      out.prefix = S.prefix | (d << digit_shift(PS));
-      out.krem = S.krem - (int32_t)above;
-    }
-    if (threadIdx.x == 0) *st_sh = out;
+  RState out = {NONE, 0};
+  if (live) {
+    uint32_t d, above;
+    xblock_pick(h, pass_bins(PS), (uint32_t)S.krem, sh, res, d, above);
+    out.prefix = S.prefix | (d << digit_shift(PS));
+    out.krem = S.krem - (int32_t)above;
   }
-  __syncthreads();
-  return *st_sh;
+  __syncthreads();   // res and h are reused
+  return out;
 }
 
 __global__ __launch_bounds__(XB) void row_topk_kernel(const float* __restrict__ score, int p, int vec,
@@ -1266,8 +1291,8 @@ __global__ __launch_bounds__(XB) void row_topk_kernel(const float* __restrict__ 
                                                       int64_t sel_total) {
   __shared__ uint32_t h[NBIN];
   __shared__ uint32_t sh[XW + 4];
-  __shared__ RState st_sh;
-  __shared__ int32_t stage[RT_STAGE + WAVE];
+  __shared__ uint32_t res[2];
+  __shared__ int32_t stage[RT_STAGE];
   const int r = blockIdx.x;
   const int npt = ((p + XB - 1) / XB + 3) & ~3;   // <= RT_NPT, a multiple of 4
   const int e0 = min(p, (int)threadIdx.x * npt);
@@ -1287,43 +1312,53 @@ __global__ __launch_bounds__(XB) void row_topk_kernel(const float* __restrict__ 
     }
   }
   RState S = rowst[r];
-  S = row_pass<1>(key, S, h, &st_sh);
-  S = row_pass<2>(key, S, h, &st_sh);
-  // emission in index order: S.prefix is the threshold T, S.krem the ties kept
+  S = row_pass<1>(key, S, h, sh, res);
+  S = row_pass<2>(key, S, h, sh, res);
+  // emission in index order: S.prefix is the threshold T, S.krem the ties
+  // kept.  The thread's kept scores (above T) and ties as bit masks over its
+  // RT_NPT positions; the ties it keeps are the first ones its share of the
+  // quota allows.
   const uint32_t quota = (S.prefix == NONE) ? 0u : (uint32_t)S.krem;
-  uint32_t n2 = 0, n1 = 0;
+  uint32_t m2 = 0u, m1 = 0u;
 #pragma unroll
   for (int j = 0; j < RT_NPT; ++j) {
+    // scheduling fences every 8 keys keep the compare masks from piling up
+    // in scalar registers
+    if ((j & 7) == 0) __builtin_amdgcn_sched_barrier(0);
     const int kc = klass(key[j], key[j] != NONE, false, S.prefix);
-    n2 += kc == 2 ? 1u : 0u;
-    n1 += kc == 1 ? 1u : 0u;
+    m2 |= (kc == 2 ? 1u : 0u) << j;
+    m1 |= (kc == 1 ? 1u : 0u) << j;
   }
+  const uint32_t n2 = __builtin_popcount(m2), n1 = __builtin_popcount(m1);
   uint32_t tot;
   const uint32_t ex = xblock_excl_scan(n2 | (n1 << 16), sh, tot);   // p <= 2^15: no carry between halves
   const uint32_t cnt = (tot & 0xFFFFu) + ((tot >> 16) < quota ? (tot >> 16) : quota);
-  const uint32_t tie0 = ex >> 16, loc0 = (ex & 0xFFFFu) + (tie0 < quota ? tie0 : quota);
+  // ties kept by earlier threads, then this thread's share of the rest (no
+  // subtraction under a condition: with `tie0 < quota ? min(n1, quota - tie0)
+  // : 0` the subtraction was hoisted out of its guard with a no-wrap flag and
+  // min(tie0, quota) below folded to tie0)
+  const uint32_t before = min(ex >> 16, quota);
+  const uint32_t take1 = min(n1, quota - before);
+  // the lowest take1 set bits of m1
+  uint32_t mt = 0u, rest = m1;
+  for (uint32_t i = 0; i < take1; ++i) {
+    const uint32_t low = rest & (0u - rest);
+    mt |= low;
+    rest ^= low;
+  }
+  const uint32_t mk = m2 | mt;                                       // kept positions
+  const uint32_t loc0 = (ex & 0xFFFFu) + before;
   const int64_t base = rowbase[r];
   const uint32_t lim = (uint32_t)cap[r];
-  // The kept indices go through LDS in windows of RT_STAGE positions: every
-  // score is written (the kept ones of the window at their position, the
-  // others at a slot of the lane's own past the window), so no store is
-  // predicated, then the window is copied out with consecutive lanes on
-  // consecutive words.
-  const uint32_t trash = RT_STAGE + (threadIdx.x & (WAVE - 1));
+  // kept indices staged in LDS by windows of RT_STAGE positions, copied out
+  // with consecutive lanes on consecutive words
   for (uint32_t w0 = 0; w0 < cnt; w0 += RT_STAGE) {
-    // the keys marked changed: each key's class is recomputed where it is
-    // used instead of 2 * RT_NPT compare masks being kept in scalar registers
-#pragma unroll
-    for (int j = 0; j < RT_NPT; ++j) asm volatile("" : "+v"(key[j]));
-    uint32_t tie = tie0, loc = loc0;
-#pragma unroll
-    for (int j = 0; j < RT_NPT; ++j) {
-      const int kc = klass(key[j], key[j] != NONE, false, S.prefix);
-      const bool tk = kc == 2 || (kc == 1 && tie < quota);
-      tie += kc == 1 ? 1u : 0u;
-      const bool here = tk && loc >= w0 && loc - w0 < (uint32_t)RT_STAGE;
-      stage[here ? loc - w0 : trash] = e0 + j;
-      loc += tk ? 1u : 0u;
+    uint32_t rem = mk, loc = loc0;
+    while (rem) {
+      const int j = __builtin_ctz(rem);
+      rem &= rem - 1u;
+      if (loc >= w0 && loc - w0 < (uint32_t)RT_STAGE) stage[loc - w0] = e0 + j;
+      ++loc;
     }
     __syncthreads();
     const uint32_t nw = min((uint32_t)RT_STAGE, cnt - w0);
@@ -1520,11 +1555,9 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   row_budget_kernel<<<R, SB, 0, st>>>(hkv, mode, kP, a.alpha_num, a.alpha_den, a.ck_num, a.ck_den, g.I,
                                       preset ? klist : nullptr, preset ? kbase : nullptr, segst, cnt, rowhist, budgets,
                                       rowbase, rowk2, rowst, sel_off);
-  if (!lava && !ck && g.p <= RT_MAX && R <= RT_ROWS) {
+  if (!lava && !ck && g.p <= RT_MAX) {
     // every head's own top-k and the emission, one workgroup per row: one
-    // launch instead of six while the rows fit about one round of workgroups
-    // (beyond that the chunked passes, bound by the scores' reads and spread
-    // over the chip, are faster: 117 against 129 us for 1024 rows of 32736)
+    // launch and one read of the scores instead of six and four
     row_topk_kernel<<<R, XB, 0, st>>>(score, g.p, vec1 ? 1 : 0, rowst, rowbase, budgets, sel, sel_total);
     return hipGetLastError();
   }
