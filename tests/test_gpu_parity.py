@@ -373,6 +373,35 @@ def test_lse_from_causal_window_dominated(gpu_lib, in_place):
     assert flagged > 0 and lost > 0
 
 
+@pytest.mark.parametrize("scorer", ["snapkv", "laprox", "lava"])
+def test_lse_from_causal_non_finite_rows(gpu_lib, scorer):
+    """Rows whose causal statistic is not finite are passed through with flag
+    2; every other row is corrected as usual (one float32 ulp of the oracle)."""
+    cfg, st, q64, k64 = _causal_inputs(scorer, "bf16", 32, 8, 128, 32, 300, 2)
+    I = q64.shape[0]
+    lc32 = np.stack([scoring.window_lse(q64[i], k64[i], causal=True) for i in range(I)]).astype(np.float32)
+    bad = np.zeros(lc32.shape, dtype=bool)
+    bad[0, 3, 5] = bad[1, 30, 0] = bad[1, 7, 31] = True
+    lc32[0, 3, 5], lc32[1, 30, 0], lc32[1, 7, 31] = np.inf, np.nan, -np.inf
+    lc = torch.from_numpy(lc32).cuda()
+    out = torch.full_like(lc, 7.0)
+    flag = torch.full(lc.shape, -1, dtype=torch.int32, device="cuda")
+    log(f"case lse_from_causal non-finite rows {scorer}")
+    lib.adakv_lse_from_causal(pipeline.make_shape(cfg, I, k64.shape[2]), pipeline.to_device(st["q_win"], "bf16"),
+                              pipeline.to_device(st["k"], "bf16"), lc, out, flag)
+    torch.cuda.synchronize()
+    got, fl = out.cpu().numpy(), flag.cpu().numpy()
+    assert np.all(fl[bad] == 2)
+    np.testing.assert_array_equal(got[bad], lc32[bad])     # passed through (NaN stays NaN)
+    ref, keep = zip(*[scoring.lse_from_causal(np.where(bad[i], 0.0, lc32[i]).astype(np.float64), q64[i], k64[i],
+                                              scorer) for i in range(I)])
+    ref, keep = np.stack(ref), np.stack(keep)
+    ok = ~bad & (keep >= 2.0 ** -20)
+    ulp = np.spacing(np.abs(ref[ok]).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got[ok].astype(np.float64) - ref[ok]) <= ulp)
+    assert np.all(fl[~bad] == np.where(keep[~bad] < 2.0 ** -7, 1, 0))
+
+
 @pytest.mark.parametrize("scorer", ["snapkv", "criticalkv", "laprox", "lava"])
 def test_causal_single_pass(gpu_lib, scorer):
     """The whole path scored from a prefill's causal statistic: corrected on
