@@ -186,7 +186,8 @@ adakv_status adakv_allocate(const adakv_shape* shape, const adakv_alloc* alloc, 
 }
 
 adakv_status adakv_lava_online_allocate(const adakv_shape* shape, int64_t total_budget, const float* score,
-                                        const int64_t* prev_sel_off, int32_t* budgets, int32_t* sel,
+                                        const int64_t* prev_sel_off, const int32_t* prev_budgets,
+                                        const int32_t* prev_sel, double* layer_ent, int32_t* budgets, int32_t* sel,
                                         int64_t* sel_off, void* ws, size_t ws_bytes, void* stream) {
   Geo g{};
   adakv_status st = check_shape(shape, g);
@@ -196,6 +197,9 @@ adakv_status adakv_lava_online_allocate(const adakv_shape* shape, int64_t total_
   if (!aligned16(score) || !aligned16(budgets) || !aligned16(sel_off) || !aligned16(ws)) return ADAKV_EINVAL;
   if (bp > 0 && !aligned16(sel)) return ADAKV_EINVAL;
   if (g.I > 1 && !aligned16(prev_sel_off)) return ADAKV_EINVAL;
+  if (layer_ent == nullptr || reinterpret_cast<uintptr_t>(layer_ent) % alignof(double) != 0) return ADAKV_EINVAL;
+  if ((prev_budgets == nullptr) != (prev_sel == nullptr)) return ADAKV_EINVAL;
+  if (g.I > 1 && prev_sel != nullptr && (!aligned16(prev_budgets) || !aligned16(prev_sel))) return ADAKV_EINVAL;
   if (g.I > 4096) return ADAKV_EUNSUPPORTED;
   if (bp > (int64_t)INT32_MAX) return ADAKV_EUNSUPPORTED;
   adakv_alloc a{};
@@ -205,7 +209,8 @@ adakv_status adakv_lava_online_allocate(const adakv_shape* shape, int64_t total_
   a.budget = total_budget;
   if (ws_bytes < alloc_ws_bytes(g, a)) return ADAKV_EWORKSPACE;
   return hip_status(launch_allocate(g, a, score, nullptr, budgets, sel, sel_off, static_cast<char*>(ws),
-                                   static_cast<hipStream_t>(stream), true, g.I > 1 ? prev_sel_off : nullptr));
+                                   static_cast<hipStream_t>(stream), true, g.I > 1 ? prev_sel_off : nullptr,
+                                   g.I > 1 ? prev_budgets : nullptr, g.I > 1 ? prev_sel : nullptr, layer_ent));
 }
 
 adakv_status adakv_lava_online_compact(const adakv_shape* shape, const void* k_new, const void* v_new,

@@ -42,11 +42,17 @@ hipError_t launch_lse_from_causal(const Geo& g, const void* q_win, const void* k
 
 // ---- allocation (select.hip)
 size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a);
-// prev_off: LAVa online prefill only (a LAVA_LAYERS call whose layer budgets are
-// capped by the previous step's; NULL at the first step), else unused.
+// LAVa online prefill only (online = true, a LAVA_LAYERS call whose layer
+// budgets are capped by the previous step's), else unused:
+//   prev_off       the previous step's sel_off (NULL at the first step)
+//   layer_ent      [I] each layer's entropy: 0..I-2 read, I-1 written
+//   prev_budgets, prev_sel  the previous step's outputs; with them the older
+//                  layers are re-selected from their previous entries
 hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* score, const float* score2,
                            int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st,
-                           bool online = false, const int64_t* prev_off = nullptr);
+                           bool online = false, const int64_t* prev_off = nullptr,
+                           const int32_t* prev_budgets = nullptr, const int32_t* prev_sel = nullptr,
+                           double* layer_ent = nullptr);
 
 // ---- compaction (compact.hip)
 hipError_t launch_compact(const Geo& g, int64_t retained_rows, const void* k, const void* v,

@@ -383,11 +383,15 @@ __device__ __forceinline__ double ln_float(uint32_t u, double v, const double* _
 }
 
 // First digit pass of the layer-wide top-k, kept per row (the row histograms
-// also serve each head's own top-k later).  For LAVa each chunk also leaves its
-// partial sums S = sum s and Q = sum s ln s (fp64) for the layer entropy.
+// also serve each head's own top-k later).  For LAVa each chunk from ent_chunk0
+// on also leaves its partial sums S = sum s and Q = sum s ln s (fp64) for the
+// layer entropy, at part[2 * (chunk - ent_chunk0)] (the online prefill takes
+// the older layers' entropies from its cache and sums the newest layer only).
 __global__ __launch_bounds__(SB) void layer_hist0_kernel(const float* __restrict__ score, int p, int cpr, int ntile,
-                                                         int vec, int lava, uint32_t* __restrict__ rowhist,
-                                                         double* __restrict__ part, uint32_t* __restrict__ flag) {
+                                                         int vec, int lava_in, int ent_chunk0,
+                                                         uint32_t* __restrict__ rowhist, double* __restrict__ part,
+                                                         uint32_t* __restrict__ flag) {
+  const bool lava = lava_in != 0 && (int)blockIdx.x >= ent_chunk0;   // uniform over the workgroup
   __shared__ uint32_t h[NBIN];
   __shared__ double dsh[2][SW];
   __shared__ double ltab[SB], itab[SB];   // ln(1 + k/256) and 1/(1 + k/256), k < 256 (LAVa)
@@ -427,8 +431,8 @@ __global__ __launch_bounds__(SB) void layer_hist0_kernel(const float* __restrict
   if (lava && threadIdx.x == 0) {
     double s2 = 0.0, q2 = 0.0;
     for (int i = 0; i < SW; ++i) { s2 += dsh[0][i]; q2 += dsh[1][i]; }
-    part[2 * (size_t)blockIdx.x] = s2;
-    part[2 * (size_t)blockIdx.x + 1] = q2;
+    part[2 * (size_t)(blockIdx.x - ent_chunk0)] = s2;
+    part[2 * (size_t)(blockIdx.x - ent_chunk0) + 1] = q2;
   }
   flush_hist(h, rowhist + (size_t)ch.r * NBIN, NBIN);
 }
@@ -479,10 +483,14 @@ __global__ __launch_bounds__(SB) void layer_pick0_kernel(const uint32_t* __restr
 // layer's budget is capped by its budget of the previous step, read from that
 // step's offsets prev_off [L] (layers 0..L-2; NULL when L == 1), and by its
 // prefix hkv * p; the newest layer (L-1) only by hkv * p.
+// Layers below `first` take e_l from ent (each layer's entropy as the step that
+// first saw it computed it); part holds the partials of layers first..L-1, and
+// their e_l are written to ent when it is given.
 __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restrict__ part, int L, int chunks_per_layer,
                                                          int hkv, int p, int64_t Bp, int online,
-                                                         const int64_t* __restrict__ prev_off,
-                                                         int64_t* __restrict__ klist, int64_t* __restrict__ sel_off) {
+                                                         const int64_t* __restrict__ prev_off, int first,
+                                                         double* __restrict__ ent, int64_t* __restrict__ klist,
+                                                         int64_t* __restrict__ sel_off) {
   extern __shared__ __align__(16) char smem[];
   double* rem = reinterpret_cast<double*>(smem);     // e_l first, then the remainders
   int64_t* fl = reinterpret_cast<int64_t*>(rem + L);
@@ -493,15 +501,23 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
   {
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
     for (int l = wv; l < L; l += SW) {
+      if (l < first) {                      // wave-uniform
+        if (lane == 0) rem[l] = ent[l];
+        continue;
+      }
       double S = 0.0, Q = 0.0;
-      const double* pl = part + 2 * (size_t)l * chunks_per_layer;
+      const double* pl = part + 2 * (size_t)(l - first) * chunks_per_layer;
       for (int c = lane; c < chunks_per_layer; c += WAVE) { S += pl[2 * c]; Q += pl[2 * c + 1]; }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
         S += __shfl_xor(S, off);
         Q += __shfl_xor(Q, off);
       }
-      if (lane == 0) rem[l] = (S > 0.0) ? (log(S) - Q / S) / ((double)hkv * (double)p) : 0.0;
+      if (lane == 0) {
+        const double e = (S > 0.0) ? (log(S) - Q / S) / ((double)hkv * (double)p) : 0.0;
+        rem[l] = e;
+        if (ent != nullptr) ent[l] = e;
+      }
     }
   }
   __syncthreads();
@@ -1270,7 +1286,8 @@ __device__ __forceinline__ RState row_pass(const uint32_t (&key)[RT_NPT], RState
   if (live) {
 #pragma unroll
     for (int j = 0; j < RT_NPT; ++j)
-      if (in_prefix(key[j], S.prefix, PS)) atomicAdd(h + digit_of(key[j], PS), 1u);
+      // padding (NONE) matches no prefix of a later pass; pass 0 skips it
+      if ((PS != 0 || key[j] != NONE) && in_prefix(key[j], S.prefix, PS)) atomicAdd(h + digit_of(key[j], PS), 1u);
   }
   __syncthreads();
   RState out = {NONE, 0};
@@ -1370,6 +1387,150 @@ __global__ __launch_bounds__(XB) void row_topk_kernel(const float* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- LAVa online: older layers
+// Layer j < I-1 of an online step keeps the top klist[j] of its kept entries
+// of the previous step (prev_sel from prev_off[j], heads one after another,
+// head g holding prev_budgets[j*hkv + g] indices in rising order).  The
+// previous step kept the first prev_off[j+1] - prev_off[j] >= klist[j] entries
+// of the same order (-score, flat index) over the same scores, so its first
+// klist[j] are the layer's first klist[j]: the same selection as a top-k over
+// all of the layer's scores, from at most RT_MAX entries instead of hkv * p.
+// The entries are already in flat-index order, so a tie goes to the earlier
+// entry.  One 1024-thread workgroup per older layer: the entries' scores are
+// gathered into registers (RT_NPT per thread), three digit passes into an LDS
+// histogram, kept entries emitted in order, head budgets counted in LDS.  The
+// host takes this route only when the previous step's older layers kept at
+// most RT_MAX entries in all; indices and counts read here are clamped into
+// range all the same.
+constexpr int RS_MAXH = 256;              // KV heads of a layer on this route
+
+__device__ __forceinline__ int rs_head_of(const int32_t* hstart, int hkv, int e) {
+  // the last head whose first entry is at most e (hstart[0] = 0)
+  int lo = 0, hi = hkv - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (hstart[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(XB) void lava_reselect_kernel(const float* __restrict__ score, int hkv, int p,
+                                                           const int32_t* __restrict__ prev_budgets,
+                                                           const int32_t* __restrict__ prev_sel,
+                                                           const int64_t* __restrict__ prev_off,
+                                                           const int64_t* __restrict__ klist,
+                                                           const int64_t* __restrict__ sel_off,
+                                                           int32_t* __restrict__ budgets, int32_t* __restrict__ sel,
+                                                           int64_t sel_total) {
+  __shared__ uint32_t h[NBIN];
+  __shared__ uint32_t sh[XW + 4];
+  __shared__ uint32_t res[2];
+  __shared__ int32_t stage[RT_STAGE];
+  __shared__ int32_t hstart[RS_MAXH + 1];
+  __shared__ uint32_t hcnt[RS_MAXH];
+  const int lay = blockIdx.x;
+  const int64_t in0 = prev_off[lay];
+  const int c = (int)min(max(prev_off[lay + 1] - in0, (int64_t)0), (int64_t)RT_MAX);
+  const int k = (int)min(max(klist[lay], (int64_t)0), (int64_t)c);
+  // first entry of every head: the scan of the previous budgets, clamped to c
+  {
+    const int t = threadIdx.x;
+    const uint32_t bprev = t < hkv ? (uint32_t)min(max(prev_budgets[(size_t)lay * hkv + t], 0), RT_MAX) : 0u;
+    uint32_t tot;
+    const uint32_t ex = xblock_excl_scan(bprev, sh, tot);
+    if (t < hkv) {
+      hstart[t] = (int32_t)min(ex, (uint32_t)c);
+      hcnt[t] = 0u;
+    }
+    if (t == 0) hstart[hkv] = c;
+  }
+  __syncthreads();
+  const int npt = ((c + XB - 1) / XB + 3) & ~3;   // <= RT_NPT
+  const int e0 = min(c, (int)threadIdx.x * npt);
+  const int n = min(npt, c - e0);
+  const int32_t* in = prev_sel + in0;
+  const float* lsc = score + (size_t)lay * hkv * p;
+  int32_t ix[RT_NPT];
+#pragma unroll
+  for (int j = 0; j < RT_NPT; ++j) ix[j] = (j < n) ? min(max(in[e0 + j], 0), p - 1) : 0;
+  uint32_t key[RT_NPT];
+  {
+    int hd = rs_head_of(hstart, hkv, e0);
+#pragma unroll
+    for (int j = 0; j < RT_NPT; ++j) {
+      while (hd + 1 < hkv && hstart[hd + 1] <= e0 + j) ++hd;
+      key[j] = (j < n) ? sel_key(lsc[(size_t)hd * p + ix[j]]) : NONE;
+    }
+  }
+  RState S = {0u, k};
+  S = row_pass<0>(key, S, h, sh, res);
+  S = row_pass<1>(key, S, h, sh, res);
+  S = row_pass<2>(key, S, h, sh, res);
+  // emission in entry order, as row_topk_kernel: kept scores and ties as bit
+  // masks, the thread's share of the ties, positions by a workgroup scan
+  const uint32_t quota = (S.prefix == NONE) ? 0u : (uint32_t)S.krem;
+  uint32_t m2 = 0u, m1 = 0u;
+#pragma unroll
+  for (int j = 0; j < RT_NPT; ++j) {
+    if ((j & 7) == 0) __builtin_amdgcn_sched_barrier(0);
+    const int kc = klass(key[j], key[j] != NONE, false, S.prefix);
+    m2 |= (kc == 2 ? 1u : 0u) << j;
+    m1 |= (kc == 1 ? 1u : 0u) << j;
+  }
+  const uint32_t n2 = __builtin_popcount(m2), n1 = __builtin_popcount(m1);
+  uint32_t tot;
+  const uint32_t ex = xblock_excl_scan(n2 | (n1 << 16), sh, tot);   // c <= 2^15: no carry between halves
+  const uint32_t cnt = (tot & 0xFFFFu) + ((tot >> 16) < quota ? (tot >> 16) : quota);
+  const uint32_t before = min(ex >> 16, quota);
+  const uint32_t take1 = min(n1, quota - before);
+  uint32_t mt = 0u, rest = m1;
+  for (uint32_t i = 0; i < take1; ++i) {
+    const uint32_t low = rest & (0u - rest);
+    mt |= low;
+    rest ^= low;
+  }
+  const uint32_t mk = m2 | mt;
+  const uint32_t loc0 = (ex & 0xFFFFu) + before;
+  // kept entries per head: a thread's entries are consecutive, so one LDS
+  // atomic per head run
+  {
+    int hd = rs_head_of(hstart, hkv, e0);
+    uint32_t run = 0u, rem = mk;
+    while (rem) {
+      const int j = __builtin_ctz(rem);
+      rem &= rem - 1u;
+      int h2 = hd;
+      while (h2 + 1 < hkv && hstart[h2 + 1] <= e0 + j) ++h2;
+      if (h2 != hd) {
+        if (run) atomicAdd(hcnt + hd, run);
+        run = 0u;
+        hd = h2;
+      }
+      ++run;
+    }
+    if (run) atomicAdd(hcnt + hd, run);
+  }
+  const int64_t base = sel_off[lay];
+  for (uint32_t w0 = 0; w0 < cnt; w0 += RT_STAGE) {
+    uint32_t rem = mk, loc = loc0;
+    while (rem) {
+      const int j = __builtin_ctz(rem);
+      rem &= rem - 1u;
+      if (loc >= w0 && loc - w0 < (uint32_t)RT_STAGE) stage[loc - w0] = min(max(in[e0 + j], 0), p - 1);
+      ++loc;
+    }
+    __syncthreads();
+    const uint32_t nw = min((uint32_t)RT_STAGE, cnt - w0);
+    for (uint32_t i = threadIdx.x; i < nw; i += XB) {
+      const uint32_t pos = w0 + i;
+      if (pos < (uint32_t)k && base + pos < sel_total) sel[base + pos] = stage[i];
+    }
+    __syncthreads();
+  }
+  __syncthreads();   // every head count is in (also when nothing was staged)
+  if ((int)threadIdx.x < hkv) budgets[(size_t)lay * hkv + threadIdx.x] = (int32_t)hcnt[threadIdx.x];
+}
+
 // ---------------------------------------------------------------- workspace plan
 struct AllocPlan {
   int R, cpr, ntile, nchunk;
@@ -1428,7 +1589,8 @@ size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a) { return plan_alloc(g,
 //   [StreamingLLM] one kernel writes budgets, offsets and indices; no scores.
 hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* score, const float* score2,
                            int32_t* budgets, int32_t* sel, int64_t* sel_off, char* ws, hipStream_t st, bool online,
-                           const int64_t* prev_off) {
+                           const int64_t* prev_off, const int32_t* prev_budgets, const int32_t* prev_sel,
+                           double* layer_ent) {
   const AllocPlan P = plan_alloc(g, a);
   uint32_t* flag = reinterpret_cast<uint32_t*>(ws + P.off_flag);
   uint32_t* rowhist = reinterpret_cast<uint32_t*>(ws + P.off_rowhist);
@@ -1537,14 +1699,45 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
                                           a.alpha_num, a.alpha_den, g.I, budgets, sel, sel_off, flag);
     return hipGetLastError();
   }
-  // Layer-wide top-k.
-  layer_hist0_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, lava ? 1 : 0, rowhist, part, flag);
-  if (lava) {
-    const int64_t Bp = a.budget - (int64_t)g.I * g.w * g.hkv;
-    const size_t sm = (size_t)g.I * (sizeof(double) + sizeof(int64_t));
-    lava_budget_kernel<<<1, SB, sm, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp, online ? 1 : 0, prev_off, klist,
-                                          sel_off);
+  // LAVa online prefill: the entropies of the older layers come from the
+  // caller's cache, so only the newest layer's are summed.
+  const int ent_first = (lava && online) ? g.I - 1 : 0;
+  const int64_t Bp_lava = lava ? a.budget - (int64_t)g.I * g.w * g.hkv : 0;
+  const size_t sm_lava = (size_t)g.I * (sizeof(double) + sizeof(int64_t));
+  if (lava && online && g.I > 1 && prev_budgets != nullptr && prev_sel != nullptr && hkv <= RS_MAXH &&
+      a.budget - (int64_t)(g.I - 1) * g.w * hkv <= RT_MAX) {
+    // Incremental step: the older layers kept at most RT_MAX entries in all at
+    // the previous step, and their new selections lie inside those.  The
+    // newest layer runs the layer-wide chain on its own rows (same chunking
+    // as the whole call, so its entropy sums are the ones the full route
+    // forms); every older layer is re-selected from its previous entries.
+    const int nc1 = hkv * cpr;
+    const size_t lay = (size_t)(g.I - 1) * hkv;
+    const float* s1 = score + lay * g.p;
+    layer_hist0_kernel<<<nc1, SB, 0, st>>>(s1, g.p, cpr, nt, vec1, 1, 0, rowhist, part, flag);
+    lava_budget_kernel<<<1, SB, sm_lava, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp_lava, 1, prev_off, ent_first,
+                                               layer_ent, klist, sel_off);
+    layer_pick0_kernel<<<1, SB, 0, st>>>(rowhist, hkv, 0, klist + (g.I - 1), segst);
+    for (int ps = 1; ps < 3; ++ps) {
+      radix_hist(nc1, st, s1, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist, flag);
+      radix_pick_kernel<<<1, SB, 0, st>>>(seghist, ps, nullptr, 0, segst);
+    }
+    layer_count_kernel<<<nc1, SB, 0, st>>>(s1, nullptr, g.p, cpr, nt, vec1, hkv, segst, cnt);
+    row_budget_kernel<<<hkv, SB, 0, st>>>(hkv, MODE_LAVA, 0, 0, 1, 0, 1, 1, nullptr, nullptr, segst, cnt, rowhist,
+                                          budgets + lay, rowbase, rowk2, rowst, sel_off + (g.I - 1));
+    chunk_count_kernel<<<nc1, SB, 0, st>>>(s1, nullptr, g.p, cpr, nt, vec1, rowst, cc);
+    emit_kernel<false, true><<<nc1, SB, 0, st>>>(s1, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets + lay,
+                                                 sel, sel_total, nullptr);
+    lava_reselect_kernel<<<g.I - 1, XB, 0, st>>>(score, hkv, g.p, prev_budgets, prev_sel, prev_off, klist, sel_off,
+                                                 budgets, sel, sel_total);
+    return hipGetLastError();
   }
+  // Layer-wide top-k.
+  layer_hist0_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, lava ? 1 : 0, ent_first * hkv * cpr, rowhist,
+                                        part, flag);
+  if (lava)
+    lava_budget_kernel<<<1, SB, sm_lava, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp_lava, online ? 1 : 0, prev_off,
+                                               ent_first, online ? layer_ent : nullptr, klist, sel_off);
   layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, (lava || preset) ? klist : nullptr, segst);
   for (int ps = 1; ps < 3; ++ps) {
     radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist, flag);

@@ -77,7 +77,8 @@ def load(path: Optional[str] = None):
     lib.adakv_decode_attn_noalloc.argtypes = [S, A, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                               ctypes.c_int32, _vp, _vp]
     lib.adakv_decode_attn_noalloc.restype = ctypes.c_int
-    lib.adakv_lava_online_allocate.argtypes = [S, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.adakv_lava_online_allocate.argtypes = [S, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               ctypes.c_size_t, _vp]
     lib.adakv_lava_online_allocate.restype = ctypes.c_int
     lib.adakv_lava_online_compact.argtypes = [S, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                               _vp, _vp, _vp, _vp, _vp]
@@ -177,9 +178,11 @@ def adakv_decode_attn_noalloc(shape, alloc, q, k_new, v_new, k_flat, v_flat, seg
     _check(st, "adakv_decode_attn_noalloc")
 
 
-def adakv_lava_online_allocate(shape, total_budget, score, prev_sel_off, budgets, sel, sel_off, ws, stream=None):
+def adakv_lava_online_allocate(shape, total_budget, score, prev_sel_off, prev_budgets, prev_sel, layer_ent, budgets,
+                               sel, sel_off, ws, stream=None):
     st = load().adakv_lava_online_allocate(ctypes.byref(shape), int(total_budget), _p(score), _p(prev_sel_off),
-                                           _p(budgets), _p(sel), _p(sel_off), _p(ws), _nbytes(ws), _stream(stream))
+                                           _p(prev_budgets), _p(prev_sel), _p(layer_ent), _p(budgets), _p(sel),
+                                           _p(sel_off), _p(ws), _nbytes(ws), _stream(stream))
     _check(st, "adakv_lava_online_allocate")
 
 

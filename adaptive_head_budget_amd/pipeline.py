@@ -185,7 +185,10 @@ class LavaOnline:
     is prefilled, score it, re-allocate every layer so far under the shared
     total, and rebuild the flat cache from the new layer's dense K/V and the
     previous flat cache (two buffers used in turn).  Only the newest layer's
-    dense cache is read at each step."""
+    dense cache is read at each step.  Each layer's entropy is kept from the
+    step that added it; with `incremental` (the default) the older layers are
+    re-selected from their previous kept entries, otherwise from their full
+    scores (the same result)."""
 
     def __init__(self, cfg: Workload, n: Optional[int] = None, total: Optional[int] = None, device="cuda"):
         import torch
@@ -216,13 +219,14 @@ class LavaOnline:
                 "seg_start": torch.empty((self.L * self.hkv + 1,), dtype=torch.int64, device=device),
                 "seg_len": torch.empty((self.L * self.hkv,), dtype=torch.int32, device=device),
             })
+        self.layer_ent = torch.zeros((self.L,), dtype=torch.float64, device=device)
         self.max_rows = rows
         self.layers_done = 0
 
     def current(self):
         return self.bufs[(self.layers_done - 1) % 2]
 
-    def step(self, q_win, k, v, stream=None):
+    def step(self, q_win, k, v, stream=None, incremental=True):
         """Prefill-time eviction after the next layer: q_win [hq, w, d],
         k, v [hkv, n, d] of that layer."""
         l = self.layers_done
@@ -232,8 +236,10 @@ class LavaOnline:
         lib.adakv_score(one, q_win, k, v, None, self.score[l], None, self.ws, stream)
         cur, prev = self.bufs[l % 2], self.bufs[(l + 1) % 2]
         sh = make_shape(self.cfg, l + 1, self.n)
+        inc = incremental and l > 0
         lib.adakv_lava_online_allocate(sh, self.total, self.score[:l + 1], prev["sel_off"] if l else None,
-                                       cur["budgets"], cur["sel"], cur["sel_off"], self.ws, stream)
+                                       prev["budgets"] if inc else None, prev["sel"] if inc else None,
+                                       self.layer_ent, cur["budgets"], cur["sel"], cur["sel_off"], self.ws, stream)
         old = (lambda key: prev[key] if l else None)
         lib.adakv_lava_online_compact(sh, k, v, old("k_flat"), old("v_flat"), old("seg_start"), old("sel"),
                                       old("sel_off"), cur["budgets"], cur["sel"], cur["sel_off"], self.max_rows,

@@ -313,20 +313,38 @@ adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, c
  * scores (no safeguard).  The budgets may sum to less than B'(l) where a cap
  * binds: sel_off[I] holds the count.
  *
+ * A layer's entropy e_j depends on its own scores only, so each is computed
+ * once, at the step that adds the layer, and kept by the caller in layer_ent.
+ * Because budgets never grow, the new top-B_j of an older layer is the first
+ * B_j of its previous kept entries (same order, same scores): given the
+ * previous step's budgets and sel, each older layer is re-selected from those
+ * entries and only the newest layer's full scores are read (taken when the
+ * previous step's older layers kept at most 32768 entries in all and hkv <=
+ * 256; otherwise every layer is re-selected from its full scores).  Both
+ * routes give the same outputs.
+ *
  *   shape.n_inst  I = layers prefilled so far; scorer/pool as for the scores
  *   score         [I, hkv, p] float32, the LAVa scores of layers 0..I-1 (each
  *                 layer's own, as adakv_score wrote them when it was prefilled)
  *   prev_sel_off  [I] int64: sel_off of the previous step (layers 0..I-2);
  *                 NULL when I == 1.  Must not overlap sel_off.
+ *   prev_budgets, prev_sel   the previous step's budgets and sel, both or
+ *                 neither (NULL: every layer from its full scores; ignored
+ *                 when I == 1).  Must not overlap budgets or sel.
+ *   layer_ent     [I] float64, 8-byte aligned, in/out: entries 0..I-2 as the
+ *                 earlier steps wrote them (read), entry I-1 written.  The
+ *                 caller keeps it from step to step.
  *   budgets [I, hkv] int32 out, sel int32 out (capacity total_budget - I*w*hkv,
  *   layout as adakv_allocate), sel_off [I+1] int64 out.
  *   ws            >= adakv_workspace_bytes(shape, LAVA_LAYERS alloc, 0) bytes;
  *                 its first int32 reports broken score preconditions as for
- *                 adakv_allocate.
+ *                 adakv_allocate, for the scores this call reads in full (the
+ *                 newest layer's alone on the incremental route).
  * Needs I <= 4096. */
 adakv_status adakv_lava_online_allocate(const adakv_shape* shape, int64_t total_budget, const float* score,
-                                        const int64_t* prev_sel_off, int32_t* budgets, int32_t* sel,
-                                        int64_t* sel_off, void* ws, size_t ws_bytes, void* stream);
+                                        const int64_t* prev_sel_off, const int32_t* prev_budgets,
+                                        const int32_t* prev_sel, double* layer_ent, int32_t* budgets,
+                                        int32_t* sel, int64_t* sel_off, void* ws, size_t ws_bytes, void* stream);
 
 /* The flat cache of layers 0..I-1 after an adakv_lava_online_allocate step:
  * the newest layer's rows (instance I-1) are gathered from its dense cache,

@@ -830,11 +830,31 @@ def test_laprox_full_sampled(gpu_lib):
 
 
 # ------------------------------------------------------------------ LAVa online prefill
-def run_online(cfg, n, total, label):
+def _same_step(a, b, l, I, what):
+    """Two LavaOnline runs after the same step: budgets, offsets, selections
+    and the flat cache identical."""
+    ca, cb = a.current(), b.current()
+    hkv = a.hkv
+    for key, m in (("budgets", I * hkv), ("sel_off", I + 1), ("seg_start", I * hkv + 1), ("seg_len", I * hkv)):
+        assert torch.equal(ca[key][:m], cb[key][:m]), f"{what} step {l}: {key} differs between the two routes"
+    tot = int(ca["sel_off"][I].item())
+    assert torch.equal(ca["sel"][:tot], cb["sel"][:tot]), f"{what} step {l}: sel differs between the two routes"
+    rows = int(ca["seg_start"][I * hkv].item())
+    for key in ("k_flat", "v_flat"):
+        assert torch.equal(ca[key][:rows].view(torch.int16 if ca[key].element_size() == 2 else torch.int32),
+                           cb[key][:rows].view(torch.int16 if cb[key].element_size() == 2 else torch.int32)), \
+            f"{what} step {l}: {key} differs between the two routes"
+    assert torch.equal(a.layer_ent[:I], b.layer_ent[:I]), f"{what} step {l}: cached entropies differ"
+
+
+def run_online(cfg, n, total, label, twin=True):
+    """Every step against the oracle's schedule; with twin, a second run that
+    re-selects every layer from its full scores must give identical outputs."""
     log(f"case {label}: {cfg.name} L={cfg.layers} n={n} total={total}")
     L, w, hkv, dt = cfg.layers, cfg.w, cfg.hkv, cfg.dtype
     insts = [synth.make_instance(cfg, l, n_override=n) for l in range(L)]
     on = pipeline.LavaOnline(cfg, n=n, total=total)
+    full = pipeline.LavaOnline(cfg, n=n, total=total) if twin else None
     k64 = [_w(x["k"], dt) for x in insts]
     v64 = [_w(x["v"], dt) for x in insts]
     prev_lb = np.zeros(0, dtype=np.int64)
@@ -843,7 +863,11 @@ def run_online(cfg, n, total, label):
         k = pipeline.to_device(insts[l]["k"], dt)
         v = pipeline.to_device(insts[l]["v"], dt)
         on.step(q, k, v)
+        if full is not None:
+            full.step(q, k, v, incremental=False)
         torch.cuda.synchronize()
+        if full is not None:
+            _same_step(on, full, l, l + 1, label)
         del q, k, v                                   # only the flat cache keeps this layer
         score = on.score[:l + 1].cpu().numpy().astype(np.float64)
         if l == 0:
@@ -884,6 +908,87 @@ def test_lava_online_prefill_caps(gpu_lib):
     cfg = scaled(configs.MISTRAL7B_LAVA, layers=3, name="lava_online_caps")
     n = 700
     run_online(cfg, n, 3 * 8 * 32 + 3 * 8 * (n - 32) // 2, "lava online caps L3 n700")
+
+
+def test_lava_online_route_switch(gpu_lib):
+    """The older layers' previous entries exceed 32768 at step 1 (every layer
+    re-selected from its full scores) and fit at step 2 (re-selected from
+    the previous entries); layer 0 keeps 32,944 entries after step 0."""
+    cfg = scaled(configs.MISTRAL7B_LAVA, layers=3, name="lava_online_switch")
+    n = 5032
+    total = 33200            # B'(0) = 32944, B'(1) = 32688 (hkv = 8, w = 32)
+    assert total - 1 * 32 * 8 > 32768 >= total - 2 * 32 * 8
+    run_online(cfg, n, total, "lava online route switch L3 n5032")
+
+
+def _online_alloc_direct(score_np, total, w, incremental):
+    """Every step of the online allocation on given scores [L, hkv, p],
+    through the C ABI alone (no scorer): per step budgets, sel_off, sel."""
+    L, hkv, p = score_np.shape
+    dev = "cuda"
+    score = torch.from_numpy(score_np.astype(np.float32)).to(dev)
+    lava = lib.AdakvAlloc(mode=lib.ADAKV_ALLOC_LAVA_LAYERS, alpha_num=0, alpha_den=1, ck_num=0, ck_den=1, sinks=0,
+                          budget=L * w * hkv)
+    shape = lambda I: lib.AdakvShape(n_inst=I, hq=hkv, hkv=hkv, d=128, n=p + w, w=w, pool=1,  # noqa: E731
+                                     dtype=lib.ADAKV_BF16, scorer=lib.ADAKV_SCORE_LAVA, hidden=0, eps=0.0,
+                                     reserved0=0)
+    ws = torch.empty(lib.adakv_workspace_bytes(shape(L), lava, 0), dtype=torch.uint8, device=dev)
+    ent = torch.zeros(L, dtype=torch.float64, device=dev)
+    cap = max(total - w * hkv, 4)
+    bufs = [{"budgets": torch.empty(L * hkv, dtype=torch.int32, device=dev),
+             "sel": torch.empty(cap, dtype=torch.int32, device=dev),
+             "sel_off": torch.empty(L + 1, dtype=torch.int64, device=dev)} for _ in range(2)]
+    out = []
+    for l in range(L):
+        cur, prev = bufs[l % 2], bufs[(l + 1) % 2]
+        inc = incremental and l > 0
+        lib.adakv_lava_online_allocate(shape(l + 1), total, score[:l + 1], prev["sel_off"] if l else None,
+                                       prev["budgets"] if inc else None, prev["sel"] if inc else None, ent,
+                                       cur["budgets"], cur["sel"], cur["sel_off"], ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0, "scores flagged as breaking the precondition"
+        off = cur["sel_off"][:l + 2].cpu().numpy()
+        out.append((cur["budgets"][:(l + 1) * hkv].cpu().numpy().reshape(l + 1, hkv), off,
+                    cur["sel"][:int(off[-1])].cpu().numpy()))
+    return out
+
+
+@pytest.mark.parametrize("case", ["ties", "dominant_layer"])
+def test_lava_online_allocate_given_scores(gpu_lib, case):
+    """The online allocation alone on crafted scores, every step against the
+    oracle and the two routes against each other: scores on a grid of 17
+    values (ties across every threshold, zeros), and a layer whose mass sits
+    on a few entries (low entropy: its budget falls to a handful)."""
+    rng = np.random.default_rng(2024 if case == "ties" else 77)
+    L, hkv, p, w = 6, 4, 1000, 32
+    s = rng.integers(0, 17, size=(L, hkv, p)).astype(np.float64) / 16.0
+    if case == "dominant_layer":
+        s = rng.random((L, hkv, p))
+        s[2] = 1e-6
+        s[2, 1, 10:13] = 1.0
+    s = s.astype(np.float32).astype(np.float64)
+    total = L * w * hkv + 1500
+    got_inc = _online_alloc_direct(s, total, w, True)
+    got_full = _online_alloc_direct(s, total, w, False)
+    prev_lb = np.zeros(0, dtype=np.int64)
+    for l in range(L):
+        (b, off, sel), (bf, offf, self_) = got_inc[l], got_full[l]
+        assert np.array_equal(b, bf) and np.array_equal(off, offf) and np.array_equal(sel, self_), \
+            f"{case} step {l}: the two routes differ"
+        ref = allocation.lava_online_step(s[:l + 1], total, w, prev_lb)
+        lb = np.diff(off)
+        if not check_lava_layer_budgets(lb, ref["layer_budgets"], ref["entropy"], ref["Bp"], f"{case} step {l}",
+                                        same_sum=False):
+            rb, rsel = allocation.layer_top_select(s[:l + 1], lb)
+            ref = {"budgets": rb, "sel": rsel}
+        for j in range(l + 1):
+            pos, heads = int(off[j]), []
+            for g in range(hkv):
+                heads.append(sel[pos:pos + int(b[j, g])])
+                pos += int(b[j, g])
+            check_selection(b[j], int(off[j]), heads, ref["budgets"][j], ref["sel"][j], f"{case} step {l} layer {j}")
+        prev_lb = lb
+        log(f"  {case} step {l}: layer budgets {lb.tolist()}; both routes and the oracle agree")
 
 
 # ------------------------------------------------------------------ limits of the supported shapes
