@@ -262,6 +262,20 @@ __device__ __forceinline__ RState pick_and_clear(uint32_t* hs, int ps, RState st
   return out;
 }
 
+// The pick of pass ps from a complete histogram hs that stays as it is: every
+// workgroup of the launch after a digit pass forms the same pick itself, so no
+// launch of its own is needed for it.  st is the state before the pass.
+__device__ __forceinline__ RState pick_keep(const uint32_t* __restrict__ hs, int ps, RState st, uint32_t* sh) {
+  RState out = {NONE, 0};
+  if (st.krem > 0 && st.prefix != NONE) {   // uniform
+    uint32_t d, above;
+    block_pick([&](int b) { return hs[b]; }, pass_bins(ps), (uint32_t)st.krem, sh, d, above);
+    out.prefix = st.prefix | (d << digit_shift(ps));
+    out.krem = st.krem - (int32_t)above;
+  }
+  return out;
+}
+
 // ---------------------------------------------------------------- zero fill
 __global__ __launch_bounds__(SB) void sel_zero_kernel(u32x4* __restrict__ p, size_t n16) {
   const u32x4 z = {0u, 0u, 0u, 0u};
@@ -283,15 +297,20 @@ __device__ __forceinline__ void flush_hist(const uint32_t* h, uint32_t* hg, int 
 // continue from st[segment].  With member flags (USE_M), flagged scores are not
 // candidates.  The pass and the flags are compile-time: with them at run time
 // the per-score loop compiles to a chain of divergent branches that costs more
-// than the chunk's load.
+// than the chunk's load.  pick_hist (later passes): st is the state before the
+// previous pass, whose digit every workgroup picks from pick_hist (that pass's
+// complete histograms); the segment's first chunk stores the result in st_out.
 template <int PS, bool USE_M>
 __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict__ score,
                                                         const uint8_t* __restrict__ member, int p, int cpr,
                                                         int ntile, int vec, int seg_rows,
                                                         const int32_t* __restrict__ kinit, int kconst,
                                                         const RState* __restrict__ st, uint32_t* __restrict__ hist,
-                                                        uint32_t* __restrict__ flag) {
+                                                        uint32_t* __restrict__ flag,
+                                                        const uint32_t* __restrict__ pick_hist,
+                                                        RState* __restrict__ st_out) {
   __shared__ uint32_t h[NBIN];
+  __shared__ uint32_t sh[SW + 4];
   const Chunk ch = chunk_of(cpr, ntile, p);
   const int s = ch.r / seg_rows;
   ChunkKeys K;
@@ -305,6 +324,10 @@ __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict_
     cur.krem = kinit ? kinit[s] : kconst;
   } else {
     cur = st[s];
+    if (pick_hist != nullptr) {
+      cur = pick_keep(pick_hist + (size_t)s * NBIN, PS - 1, cur, sh);
+      if (threadIdx.x == 0 && ch.r % seg_rows == 0 && ch.c == 0) st_out[s] = cur;
+    }
   }
   if (cur.krem <= 0 || cur.prefix == NONE) return;
   constexpr int nb = PS == 2 ? 512 : NBIN;
@@ -334,10 +357,10 @@ __global__ __launch_bounds__(SB) void radix_hist_kernel(const float* __restrict_
 // Launches the digit pass ps (0..2) with or without member flags.
 void radix_hist(int nc, hipStream_t stream, const float* score, const uint8_t* member, int p, int cpr, int ntile,
                 int vec, int seg_rows, int ps, const int32_t* kinit, int kconst, const RState* st, uint32_t* hist,
-                uint32_t* flag) {
+                uint32_t* flag, const uint32_t* pick_hist = nullptr, RState* st_out = nullptr) {
 #define RH(PSV, M)                                                                                       \
   radix_hist_kernel<PSV, M><<<nc, SB, 0, stream>>>(score, member, p, cpr, ntile, vec, seg_rows, kinit, kconst, st, hist, \
-                                                   flag)
+                                                   flag, pick_hist, st_out)
   if (member != nullptr) {
     if (ps == 0) RH(0, true); else if (ps == 1) RH(1, true); else RH(2, true);
   } else {
@@ -440,19 +463,16 @@ __global__ __launch_bounds__(SB) void layer_hist0_kernel(const float* __restrict
 // First digit pick of every layer-wide top-k (one workgroup per instance) from
 // the sum of its rows' histograms, with k = kP, or klist[instance] for LAVa.
 // The row histograms are kept.
-__global__ __launch_bounds__(SB) void layer_pick0_kernel(const uint32_t* __restrict__ rowhist, int hkv, int kP,
-                                                         const int64_t* __restrict__ klist, RState* __restrict__ seg) {
+__device__ __forceinline__ void layer_pick0_of(const uint32_t* __restrict__ h0, int hkv, int k,
+                                               RState* __restrict__ out) {
   __shared__ uint32_t sh[SW + 4];
-  const int inst = blockIdx.x;
-  const int k = klist ? (int)klist[inst] : kP;
-  if (k <= 0) {
-    if (threadIdx.x == 0) { RState none = {NONE, 0}; seg[inst] = none; }
+  if (k <= 0) {                                  // uniform
+    if (threadIdx.x == 0) { RState none = {NONE, 0}; *out = none; }
     return;
   }
   // the instance's pass-0 histogram: its rows' histograms added bin by bin,
   // 32 independent loads in flight per thread, into LDS
   __shared__ uint32_t hsum[NBIN];
-  const uint32_t* h0 = rowhist + (size_t)inst * hkv * NBIN;
   uint32_t t[NBIN / SB];
 #pragma unroll
   for (int j = 0; j < NBIN / SB; ++j) t[j] = 0u;
@@ -473,7 +493,13 @@ __global__ __launch_bounds__(SB) void layer_pick0_kernel(const uint32_t* __restr
   __syncthreads();
   uint32_t d, above;
   block_pick([&](int b) { return hsum[b]; }, NBIN, (uint32_t)k, sh, d, above);
-  if (threadIdx.x == 0) { RState x = {d << 20, k - (int32_t)above}; seg[inst] = x; }
+  if (threadIdx.x == 0) { RState x = {d << 20, k - (int32_t)above}; *out = x; }
+}
+
+__global__ __launch_bounds__(SB) void layer_pick0_kernel(const uint32_t* __restrict__ rowhist, int hkv, int kP,
+                                                         const int64_t* __restrict__ klist, RState* __restrict__ seg) {
+  const int inst = blockIdx.x;
+  layer_pick0_of(rowhist + (size_t)inst * hkv * NBIN, hkv, klist ? (int)klist[inst] : kP, seg + inst);
 }
 
 // LAVa: per layer, S and Q from the chunk partials in a fixed order,
@@ -490,12 +516,14 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
                                                          int hkv, int p, int64_t Bp, int online,
                                                          const int64_t* __restrict__ prev_off, int first,
                                                          double* __restrict__ ent, int64_t* __restrict__ klist,
-                                                         int64_t* __restrict__ sel_off) {
+                                                         int64_t* __restrict__ sel_off,
+                                                         const uint32_t* __restrict__ pick_rowhist,
+                                                         RState* __restrict__ pick_out) {
   extern __shared__ __align__(16) char smem[];
   double* rem = reinterpret_cast<double*>(smem);     // e_l first, then the remainders
   int64_t* fl = reinterpret_cast<int64_t*>(rem + L);
   __shared__ double Esh;
-  __shared__ int64_t def;
+  __shared__ int64_t def, klast;
   // one wave per layer: lane-strided sums over the layer's chunk partials,
   // then a fixed butterfly (the same order on every run)
   {
@@ -553,6 +581,7 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
       k = min(k, cap);
     }
     klist[l] = k;
+    if (l == L - 1) klast = k;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -560,6 +589,9 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
     for (int i = 0; i < L; ++i) { sel_off[i] = s; s += klist[i]; }
     sel_off[L] = s;
   }
+  // with pick_rowhist (a call that selects in the newest layer alone): that
+  // layer's first digit, from its rows' pass-0 histograms
+  if (pick_rowhist != nullptr) layer_pick0_of(pick_rowhist, hkv, (int)klast, pick_out);
 }
 
 // ---------------------------------------------------------------- layer counts and budgets
@@ -567,19 +599,36 @@ enum { MODE_ADA = 0, MODE_LAVA = 1, MODE_CK = 2 };
 
 // Per row: entries above its segment's threshold T and equal to it (a segment
 // is seg_rows consecutive rows: one instance, or every row of the call).  With
-// member flags, flagged entries are not counted.
+// member flags, flagged entries are not counted.  pick_hist: seg is the state
+// before the last digit pass, whose digit every workgroup picks from pick_hist
+// (the complete last-pass histograms); the segment's first chunk stores the
+// final state in seg_out.  cc_out: the chunk's own two counts as well (what
+// chunk_count_kernel gives for rows that keep the segment's threshold).
 __global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict__ score,
                                                          const uint8_t* __restrict__ member, int p, int cpr,
                                                          int ntile, int vec, int seg_rows,
-                                                         const RState* __restrict__ seg, uint32_t* __restrict__ cnt) {
+                                                         const RState* __restrict__ seg, uint32_t* __restrict__ cnt,
+                                                         const uint32_t* __restrict__ pick_hist,
+                                                         RState* __restrict__ seg_out, uint32_t* __restrict__ cc_out) {
   __shared__ uint32_t sh[SW + 4];
   const Chunk ch = chunk_of(cpr, ntile, p);
   ChunkKeys K;
   uint8_t m[NK];
   load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
   if (member) load_member(member + (size_t)ch.r * p, ch, ntile, vec != 0, K, m);
-  const RState L = seg[ch.r / seg_rows];
-  if (L.prefix == NONE) return;
+  const int sg = ch.r / seg_rows;
+  RState L = seg[sg];
+  if (pick_hist != nullptr) {
+    L = pick_keep(pick_hist + (size_t)sg * NBIN, 2, L, sh);
+    if (threadIdx.x == 0 && ch.r % seg_rows == 0 && ch.c == 0) seg_out[sg] = L;
+  }
+  if (L.prefix == NONE) {                      // uniform
+    if (cc_out != nullptr && threadIdx.x == 0) {
+      cc_out[2 * (size_t)blockIdx.x] = 0u;
+      cc_out[2 * (size_t)blockIdx.x + 1] = 0u;
+    }
+    return;
+  }
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
@@ -591,6 +640,10 @@ __global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict
   if (threadIdx.x == 0) {
     if (both & 0xFFFFu) atomicAdd(cnt + 2 * (size_t)ch.r, both & 0xFFFFu);
     if (both >> 16) atomicAdd(cnt + 2 * (size_t)ch.r + 1, both >> 16);
+    if (cc_out != nullptr) {
+      cc_out[2 * (size_t)blockIdx.x] = both & 0xFFFFu;
+      cc_out[2 * (size_t)blockIdx.x + 1] = both >> 16;
+    }
   }
 }
 
@@ -814,18 +867,17 @@ __global__ __launch_bounds__(SB) void chunk_count_kernel(const float* __restrict
 }
 
 // Writes the kept scores of the chunk in index order: as token indices at
-// sel[rowbase[r] + position] (TO_SEL: at most cap[r] of them, never past
-// sel_total), or as member flags.  USE_M: flagged scores count as kept.
+// sel[base + position] (TO_SEL: at most lim of them, never past sel_total), or
+// as member flags.  S is the row's state (threshold, ties it keeps).  USE_M:
+// flagged scores count as kept.
 template <bool USE_M, bool TO_SEL>
-__global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ score, const uint8_t* __restrict__ member,
-                                                  int p, int cpr, int ntile, int vec, const RState* __restrict__ rowst,
-                                                  const uint32_t* __restrict__ cc, const int64_t* __restrict__ rowbase,
-                                                  const int32_t* __restrict__ cap, int32_t* __restrict__ sel,
-                                                  int64_t sel_total, uint8_t* __restrict__ member_out) {
+__device__ __forceinline__ void emit_chunk(const float* __restrict__ score, const uint8_t* __restrict__ member, int p,
+                                           int cpr, int ntile, int vec, const Chunk& ch, const RState S,
+                                           const uint32_t* __restrict__ cc, const int64_t base, const uint32_t lim,
+                                           int32_t* __restrict__ sel, int64_t sel_total,
+                                           uint8_t* __restrict__ member_out) {
   __shared__ uint32_t sh[SW + 4];
   __shared__ uint32_t before_sh[2][SW];
-  const Chunk ch = chunk_of(cpr, ntile, p);
-  const RState S = rowst[ch.r];
   ChunkKeys K;
   uint8_t m[NK];
   load_chunk(score + (size_t)ch.r * p, ch, ntile, vec != 0, K);
@@ -847,8 +899,6 @@ __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ scor
   // ties kept by earlier chunks, and what is left (no subtraction under a condition)
   const uint32_t qrem = quota - min(quota, B1);
   const uint32_t pos0 = B2 + min(quota, B1);
-  const int64_t base = TO_SEL ? rowbase[ch.r] : 0;
-  const uint32_t lim = TO_SEL ? (uint32_t)cap[ch.r] : 0u;
 
   int kc[NK];
   uint32_t n2 = 0, n1 = 0;
@@ -900,6 +950,62 @@ __global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ scor
         if (j < K.n) mo[K.e0 + j] = take[j];
     }
   }
+}
+
+template <bool USE_M, bool TO_SEL>
+__global__ __launch_bounds__(SB) void emit_kernel(const float* __restrict__ score, const uint8_t* __restrict__ member,
+                                                  int p, int cpr, int ntile, int vec, const RState* __restrict__ rowst,
+                                                  const uint32_t* __restrict__ cc, const int64_t* __restrict__ rowbase,
+                                                  const int32_t* __restrict__ cap, int32_t* __restrict__ sel,
+                                                  int64_t sel_total, uint8_t* __restrict__ member_out) {
+  const Chunk ch = chunk_of(cpr, ntile, p);
+  emit_chunk<USE_M, TO_SEL>(score, member, p, cpr, ntile, vec, ch, rowst[ch.r], cc, TO_SEL ? rowbase[ch.r] : 0,
+                            TO_SEL ? (uint32_t)cap[ch.r] : 0u, sel, sel_total, member_out);
+}
+
+// LAVa: rows keep their layer's threshold T with a share of its ties in head
+// order, so each workgroup forms its row's budget B_g = above + share and its
+// offset in sel from the heads' counts itself (the chunk counts of T come
+// from layer_count_kernel), then emits; the row's first chunk writes B_g.
+// hkv <= 256.
+__global__ __launch_bounds__(SB) void lava_emit_kernel(const float* __restrict__ score, int p, int cpr, int ntile,
+                                                       int vec, int hkv, const RState* __restrict__ seg,
+                                                       const uint32_t* __restrict__ cnt,
+                                                       const uint32_t* __restrict__ cc,
+                                                       const int64_t* __restrict__ sel_off,
+                                                       int32_t* __restrict__ budgets, int32_t* __restrict__ sel,
+                                                       int64_t sel_total) {
+  __shared__ uint32_t gt_sh[256], eq_sh[256];
+  __shared__ int64_t base_sh;
+  __shared__ uint32_t f_sh, q_sh;
+  const Chunk ch = chunk_of(cpr, ntile, p);
+  const int inst = ch.r / hkv, g = ch.r - inst * hkv;
+  const RState L = seg[inst];
+  for (int j = threadIdx.x; j < hkv; j += SB) {
+    gt_sh[j] = cnt[2 * ((size_t)inst * hkv + j)];
+    eq_sh[j] = cnt[2 * ((size_t)inst * hkv + j) + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // ties shared out in head order, as row_budget_kernel does (a layer's
+    // counts stay below 2^31)
+    const int64_t quota = (L.prefix == NONE) ? 0 : L.krem;
+    int64_t before = 0, base = sel_off[inst];
+    for (int j = 0; j < g; ++j) {
+      const int64_t share = min(max(quota - before, (int64_t)0), (int64_t)eq_sh[j]);
+      base += (int64_t)gt_sh[j] + share;
+      before += eq_sh[j];
+    }
+    const int64_t share = min(max(quota - before, (int64_t)0), (int64_t)eq_sh[g]);
+    base_sh = base;
+    f_sh = gt_sh[g] + (uint32_t)share;
+    q_sh = (uint32_t)share;
+  }
+  __syncthreads();
+  RState S = {L.prefix, (int32_t)q_sh};
+  if (L.prefix == NONE) S.krem = 0;
+  if (threadIdx.x == 0 && ch.c == 0) budgets[ch.r] = (int32_t)f_sh;
+  emit_chunk<false, true>(score, nullptr, p, cpr, ntile, vec, ch, S, cc, base_sh, f_sh, sel, sel_total, nullptr);
 }
 
 // ---------------------------------------------------------------- one workgroup per instance
@@ -1534,8 +1640,9 @@ __global__ __launch_bounds__(XB) void lava_reselect_kernel(const float* __restri
 // ---------------------------------------------------------------- workspace plan
 struct AllocPlan {
   int R, cpr, ntile, nchunk;
-  size_t off_flag, off_rowhist, off_seghist, off_cnt, zero_end;
-  size_t off_seg, off_row, off_row2, off_rowk2, off_rowbase, off_cc, off_member, off_part, off_klist, off_kbase, total;
+  size_t off_flag, off_rowhist, off_seghist, off_seghist2, off_cnt, zero_end;
+  size_t off_seg, off_seg1, off_seg2, off_row, off_row2, off_rowk2, off_rowbase, off_cc, off_member, off_part,
+      off_klist, off_kbase, total;
 };
 
 AllocPlan plan_alloc(const Geo& g, const adakv_alloc& a) {
@@ -1550,9 +1657,12 @@ AllocPlan plan_alloc(const Geo& g, const adakv_alloc& a) {
   P.off_flag = off;     off = 256;   // int32: a score broke the precondition
   P.off_rowhist = off;  off = align_up(off + (size_t)P.R * NBIN * 4, 256);
   P.off_seghist = off;  off = align_up(off + (size_t)g.I * NBIN * 4, 256);
+  P.off_seghist2 = off; off = align_up(off + (size_t)g.I * NBIN * 4, 256);   // the layer-wide pass 2
   P.off_cnt = off;      off = align_up(off + (size_t)P.R * 8, 256);
   P.zero_end = off;
   P.off_seg = off;      off = align_up(off + (size_t)g.I * sizeof(RState), 256);
+  P.off_seg1 = off;     off = align_up(off + (size_t)g.I * sizeof(RState), 256);
+  P.off_seg2 = off;     off = align_up(off + (size_t)g.I * sizeof(RState), 256);
   P.off_row = off;      off = align_up(off + (size_t)P.R * sizeof(RState), 256);
   P.off_row2 = off;     off = align_up(off + (size_t)P.R * sizeof(RState), 256);
   P.off_rowk2 = off;    off = align_up(off + (size_t)P.R * 4, 256);
@@ -1576,10 +1686,17 @@ size_t alloc_ws_bytes(const Geo& g, const adakv_alloc& a) { return plan_alloc(g,
 // Launch order (every kernel on `st`, nothing waits on the host):
 //   zero histograms and counts
 //   layer-wide top-k: pass-0 row histograms [LAVa: + entropy partials, layer budgets],
-//     pick 0, then (histogram, pick) for passes 1 and 2
-//   layer counts per row -> per-row budgets, offsets and first pick of the head's top-k
-//   [Ada-KV / CriticalKV] (histogram, pick) for passes 1 and 2 of every head's top-k
-//   per-chunk counts -> emission in index order
+//     pick 0, histograms of passes 1 and 2 (the pass-2 launch picks the digit of
+//     pass 1 itself), layer counts per row (picking the digit of pass 2 itself)
+//   [LAVa] emission in index order; each workgroup forms its row's budget and
+//     offset from the counts (rows keep the layer threshold)
+//   [LAVa online, older layers re-selected] the newest layer's chain as above
+//     (its first pick inside the layer-budget launch), then one workgroup per
+//     older layer re-selects among its previous entries
+//   per-row budgets, offsets and first pick of the head's top-k
+//   [Ada-KV, rows of at most RT_MAX scores] each head's top-k and emission in
+//     one launch, else (histogram, pick) for passes 1 and 2 of every head's
+//     top-k, per-chunk counts, emission in index order
 //   [CriticalKV] stage 1 emits member flags; stage 2 runs the head top-k again on the
 //     composite score over non-members and emits the union.
 //   [model-wide] one segment of all rows: (histogram, pick) x 3, counts per row,
@@ -1595,8 +1712,11 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   uint32_t* flag = reinterpret_cast<uint32_t*>(ws + P.off_flag);
   uint32_t* rowhist = reinterpret_cast<uint32_t*>(ws + P.off_rowhist);
   uint32_t* seghist = reinterpret_cast<uint32_t*>(ws + P.off_seghist);
+  uint32_t* seghist2 = reinterpret_cast<uint32_t*>(ws + P.off_seghist2);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + P.off_cnt);
   RState* segst = reinterpret_cast<RState*>(ws + P.off_seg);
+  RState* segst1 = reinterpret_cast<RState*>(ws + P.off_seg1);
+  RState* segst2 = reinterpret_cast<RState*>(ws + P.off_seg2);
   RState* rowst = reinterpret_cast<RState*>(ws + P.off_row);
   RState* rowst2 = reinterpret_cast<RState*>(ws + P.off_row2);
   int32_t* rowk2 = reinterpret_cast<int32_t*>(ws + P.off_rowk2);
@@ -1650,7 +1770,8 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
       radix_hist(nc, st, score, member, g.p, cpr, nt, vec1, hkv, ps, nullptr, k2, segst, seghist, flag);
       radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, k2, segst);
     }
-    layer_count_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, hkv, segst, cnt);
+    layer_count_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, hkv, segst, cnt, nullptr, nullptr,
+                                          nullptr);
     segment_budget_kernel<<<g.I, SB, 0, st>>>(hkv, hkv, g.I, f0, (int64_t)kP, segst, cnt, budgets, rowbase, rowst2,
                                               sel_off);
     chunk_count_kernel<<<nc, SB, 0, st>>>(score, member, g.p, cpr, nt, vec1, rowst2, cc);
@@ -1666,7 +1787,8 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
       radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, R, ps, nullptr, Bp, segst, seghist, flag);
       radix_pick_kernel<<<1, SB, 0, st>>>(seghist, ps, nullptr, Bp, segst);
     }
-    layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, segst, cnt);
+    layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, R, segst, cnt, nullptr, nullptr,
+                                          nullptr);
     segment_budget_kernel<<<1, SB, 0, st>>>(R, hkv, g.I, 0, 0, segst, cnt, budgets, rowbase, rowst, sel_off);
     chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
     emit_kernel<false, true><<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets, sel, (int64_t)Bp,
@@ -1716,18 +1838,12 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
     const float* s1 = score + lay * g.p;
     layer_hist0_kernel<<<nc1, SB, 0, st>>>(s1, g.p, cpr, nt, vec1, 1, 0, rowhist, part, flag);
     lava_budget_kernel<<<1, SB, sm_lava, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp_lava, 1, prev_off, ent_first,
-                                               layer_ent, klist, sel_off);
-    layer_pick0_kernel<<<1, SB, 0, st>>>(rowhist, hkv, 0, klist + (g.I - 1), segst);
-    for (int ps = 1; ps < 3; ++ps) {
-      radix_hist(nc1, st, s1, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist, flag);
-      radix_pick_kernel<<<1, SB, 0, st>>>(seghist, ps, nullptr, 0, segst);
-    }
-    layer_count_kernel<<<nc1, SB, 0, st>>>(s1, nullptr, g.p, cpr, nt, vec1, hkv, segst, cnt);
-    row_budget_kernel<<<hkv, SB, 0, st>>>(hkv, MODE_LAVA, 0, 0, 1, 0, 1, 1, nullptr, nullptr, segst, cnt, rowhist,
-                                          budgets + lay, rowbase, rowk2, rowst, sel_off + (g.I - 1));
-    chunk_count_kernel<<<nc1, SB, 0, st>>>(s1, nullptr, g.p, cpr, nt, vec1, rowst, cc);
-    emit_kernel<false, true><<<nc1, SB, 0, st>>>(s1, nullptr, g.p, cpr, nt, vec1, rowst, cc, rowbase, budgets + lay,
-                                                 sel, sel_total, nullptr);
+                                               layer_ent, klist, sel_off, rowhist, segst);
+    radix_hist(nc1, st, s1, nullptr, g.p, cpr, nt, vec1, hkv, 1, nullptr, 0, segst, seghist, flag);
+    radix_hist(nc1, st, s1, nullptr, g.p, cpr, nt, vec1, hkv, 2, nullptr, 0, segst, seghist2, flag, seghist, segst1);
+    layer_count_kernel<<<nc1, SB, 0, st>>>(s1, nullptr, g.p, cpr, nt, vec1, hkv, segst1, cnt, seghist2, segst2, cc);
+    lava_emit_kernel<<<nc1, SB, 0, st>>>(s1, g.p, cpr, nt, vec1, hkv, segst2, cnt, cc, sel_off + (g.I - 1),
+                                         budgets + lay, sel, sel_total);
     lava_reselect_kernel<<<g.I - 1, XB, 0, st>>>(score, hkv, g.p, prev_budgets, prev_sel, prev_off, klist, sel_off,
                                                  budgets, sel, sel_total);
     return hipGetLastError();
@@ -1737,29 +1853,33 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
                                         part, flag);
   if (lava)
     lava_budget_kernel<<<1, SB, sm_lava, st>>>(part, g.I, hkv * cpr, hkv, g.p, Bp_lava, online ? 1 : 0, prev_off,
-                                               ent_first, online ? layer_ent : nullptr, klist, sel_off);
+                                               ent_first, online ? layer_ent : nullptr, klist, sel_off, nullptr,
+                                               nullptr);
   layer_pick0_kernel<<<g.I, SB, 0, st>>>(rowhist, hkv, kP, (lava || preset) ? klist : nullptr, segst);
-  for (int ps = 1; ps < 3; ++ps) {
-    radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, hkv, ps, nullptr, 0, segst, seghist, flag);
-    radix_pick_kernel<<<g.I, SB, 0, st>>>(seghist, ps, nullptr, 0, segst);
+  // passes 1 and 2; the digits of passes 1 and 2 are picked by the launch after each
+  radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, hkv, 1, nullptr, 0, segst, seghist, flag);
+  radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, hkv, 2, nullptr, 0, segst, seghist2, flag, seghist, segst1);
+  // Head budgets (LAVa: the emission forms them from the counts itself).
+  layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, hkv, segst1, cnt, seghist2, segst2,
+                                        lava ? cc : nullptr);
+  if (lava) {
+    lava_emit_kernel<<<nc, SB, 0, st>>>(score, g.p, cpr, nt, vec1, hkv, segst2, cnt, cc, sel_off, budgets, sel,
+                                        sel_total);
+    return hipGetLastError();
   }
-  // Head budgets.
-  layer_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, hkv, segst, cnt);
   row_budget_kernel<<<R, SB, 0, st>>>(hkv, mode, kP, a.alpha_num, a.alpha_den, a.ck_num, a.ck_den, g.I,
-                                      preset ? klist : nullptr, preset ? kbase : nullptr, segst, cnt, rowhist, budgets,
-                                      rowbase, rowk2, rowst, sel_off);
-  if (!lava && !ck && g.p <= RT_MAX) {
+                                      preset ? klist : nullptr, preset ? kbase : nullptr, segst2, cnt, rowhist,
+                                      budgets, rowbase, rowk2, rowst, sel_off);
+  if (!ck && g.p <= RT_MAX) {
     // every head's own top-k and the emission, one workgroup per row: one
     // launch and one read of the scores instead of six and four
     row_topk_kernel<<<R, XB, 0, st>>>(score, g.p, vec1 ? 1 : 0, rowst, rowbase, budgets, sel, sel_total);
     return hipGetLastError();
   }
-  // Every head's own top-k (LAVa keeps the layer threshold).
-  if (!lava) {
-    for (int ps = 1; ps < 3; ++ps) {
-      radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, 0, rowst, rowhist, flag);
-      radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, 0, rowst);
-    }
+  // Every head's own top-k.
+  for (int ps = 1; ps < 3; ++ps) {
+    radix_hist(nc, st, score, nullptr, g.p, cpr, nt, vec1, 1, ps, nullptr, 0, rowst, rowhist, flag);
+    radix_pick_kernel<<<R, SB, 0, st>>>(rowhist, ps, nullptr, 0, rowst);
   }
   chunk_count_kernel<<<nc, SB, 0, st>>>(score, nullptr, g.p, cpr, nt, vec1, rowst, cc);
   if (!ck) {
