@@ -101,9 +101,12 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(const char* __restric
       const int B = budgets[s];
       int64_t tok;
       if (j < B) {
+        // budgets that sum past the instance's span of sel (not an allocate
+        // output) leave the rows past it unwritten instead of reading beyond
         const int s0 = inst * hkv;
         const int64_t head_off = packed_s - packed(s0) - (int64_t)g * w;
-        tok = sel[sel_off[inst] + head_off + j];
+        const int64_t si = sel_off[inst] + head_off + j;
+        tok = si < sel_off[inst + 1] ? sel[si] : -1;
       } else {
         tok = (int64_t)p + (j - B);
       }
@@ -146,7 +149,9 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(const char* __restric
 // (no reserve rows), where every kept token still is: a prefix token is
 // found by binary search in the head's previous ascending selection, a window
 // token at its fixed place after it.  Rows past the device total or the
-// buffer, and tokens missing from the previous cache, are skipped.
+// buffer, and tokens missing from the previous cache, are skipped; reads stay
+// inside each layer's span of sel and sel_old and inside max_rows rows of the
+// previous cache even when budgets and offsets disagree.
 template <int ROWB>
 __global__ __launch_bounds__(256) void online_copy_kernel(
     const char* __restrict__ k_new, const char* __restrict__ v_new, const char* __restrict__ k_old,
@@ -187,8 +192,13 @@ __global__ __launch_bounds__(256) void online_copy_kernel(
       const int64_t j = r - seg_start[s];
       const int B = budgets[s];
       int64_t tok;
-      if (j < B) tok = sel[sel_off[inst] + (seg_start[s] - seg_start[s0] - (int64_t)g * w) + j];
-      else tok = (int64_t)p + (j - B);
+      if (j < B) {
+        // never past the layer's span of sel, whatever the budgets add up to
+        const int64_t si = sel_off[inst] + (seg_start[s] - seg_start[s0] - (int64_t)g * w) + j;
+        tok = si < sel_off[inst + 1] ? sel[si] : -1;
+      } else {
+        tok = (int64_t)p + (j - B);
+      }
       if (inst == S / hkv - 1) {
         if (tok >= 0 && tok < n) {
           const int64_t row = (int64_t)g * n + tok;
@@ -201,17 +211,21 @@ __global__ __launch_bounds__(256) void online_copy_kernel(
         int64_t pos = -1;
         if (tok >= p) {
           pos = bold + (tok - p);
-        } else {
-          const int32_t* hs = sel_old + sel_off_old[inst] + (ob - seg_start_old[s0] - (int64_t)g * w);
-          int64_t lo = 0, hi = bold;             // first index with hs[index] >= tok
+        } else if (tok >= 0) {
+          const int64_t h0 = sel_off_old[inst] + (ob - seg_start_old[s0] - (int64_t)g * w);
+          // the head's previous selection, kept inside the layer's span of sel_old
+          const int64_t hn = min(bold, sel_off_old[inst + 1] - h0);
+          const int32_t* hs = sel_old + h0;
+          int64_t lo = 0, hi = hn;               // first index with hs[index] >= tok
           while (lo < hi) {
             const int64_t mid = (lo + hi) >> 1;
             if (hs[mid] < tok) lo = mid + 1;
             else hi = mid;
           }
-          if (lo < bold && hs[lo] == tok) pos = lo;
+          if (lo < hn && hs[lo] == tok) pos = lo;
         }
-        if (pos >= 0 && pos < bold + w) {
+        // rows of the previous cache past the buffer (max_rows, as this one) are not read
+        if (pos >= 0 && pos < bold + w && ob + pos < flat_rows) {
           sk = k_old + (ob + pos) * ROWB;
           sv = v_old + (ob + pos) * ROWB;
         }

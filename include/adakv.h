@@ -354,9 +354,13 @@ adakv_status adakv_lava_online_allocate(const adakv_shape* shape, int64_t total_
  * rows.  The copy is bit-exact.
  *
  *   k_new, v_new     [hkv, n, d] dtype: the dense cache of layer I-1
- *   k_old, v_old     previous flat cache (layers 0..I-2), seg_start_old
- *                    [(I-1)*hkv+1], sel_old and sel_off_old [I] of the previous
- *                    step; all NULL when I == 1
+ *   k_old, v_old     previous flat cache (layers 0..I-2), at least max_rows
+ *                    rows like k_flat (rows at or past max_rows are not read),
+ *                    seg_start_old [(I-1)*hkv+1], sel_old and sel_off_old [I]
+ *                    of the previous step; all NULL when I == 1.  Reads of
+ *                    sel and sel_old stay inside each layer's span of its
+ *                    offsets even where budgets disagree with them (rows left
+ *                    unwritten then).
  *   budgets, sel, sel_off   this step's adakv_lava_online_allocate outputs
  *   max_rows         rows of k_flat / v_flat; rows past it are not written
  *                    (B'(l) + I*hkv*w always suffices)

@@ -1188,3 +1188,87 @@ def test_decode_reserve_larger_than_compacted(gpu_lib):
     diff = (out_app - out_none).abs().max().item()
     assert diff <= 1e-5, f"a dropped append changed the output (max-abs {diff:.2e})"
     log("  reserve larger than compacted: the append is dropped, cache untouched, output = no-append output")
+
+
+# ------------------------------------------------------------------ compaction against budgets that disagree with the offsets
+def _rows_bf16(nrows, d, first_value):
+    """Rows whose every element is one small integer (exact in bf16): row r holds first_value + r."""
+    vals = torch.arange(first_value, first_value + nrows, dtype=torch.float32, device="cuda")
+    return vals[:, None].expand(nrows, d).contiguous().to(torch.bfloat16)
+
+
+def test_compact_budgets_past_offsets(gpu_lib):
+    """adakv_compact given budgets that sum past the instance's span of sel
+    (never an allocate output): the rows whose sel position lies past the span
+    are left unwritten and nothing past the flat buffer's rows is touched.
+    Every buffer is large enough that even unchecked reads would stay inside."""
+    hkv, w, n, d = 2, 4, 40, 128
+    p = n - w
+    shape = lib.AdakvShape(n_inst=1, hq=hkv, hkv=hkv, d=d, n=n, w=w, pool=1, dtype=lib.ADAKV_BF16,
+                           scorer=lib.ADAKV_SCORE_SNAPKV, hidden=0, eps=0.0, reserved0=0)
+    alloc = lib.AdakvAlloc(mode=lib.ADAKV_ALLOC_ADA, alpha_num=1, alpha_den=5, ck_num=0, ck_den=1, sinks=0,
+                           budget=8 + w * hkv, inst_budget=None)          # 8 selected rows, 16 retained
+    k = _rows_bf16(hkv * n, d, 1).reshape(1, hkv, n, d)
+    v = _rows_bf16(hkv * n, d, 101).reshape(1, hkv, n, d)       # all values below 256: exact in bf16
+    budgets = torch.tensor([6, 6], dtype=torch.int32, device="cuda")        # 12 > the span of 8
+    sel_off = torch.tensor([0, 8], dtype=torch.int64, device="cuda")
+    sel = torch.tensor([1, 3, 5, 7, 9, 11, 2, 4, 6, 8, 10, 12] + [0] * 52, dtype=torch.int32, device="cuda")
+    sentinel = -7.0
+    kf = torch.full((64, d), sentinel, dtype=torch.bfloat16, device="cuda")
+    vf = torch.full((64, d), sentinel, dtype=torch.bfloat16, device="cuda")
+    seg_start = torch.empty(hkv + 1, dtype=torch.int64, device="cuda")
+    seg_len = torch.empty(hkv, dtype=torch.int32, device="cuda")
+    lib.adakv_compact(shape, alloc, k, v, budgets, sel, sel_off, 0, kf, vf, seg_start, seg_len)
+    torch.cuda.synchronize()
+    assert seg_start.tolist() == [0, 10, 20] and seg_len.tolist() == [10, 10]
+    kv0 = kf[:, 0].float().cpu().numpy()
+    tok_h0 = [1, 3, 5, 7, 9, 11, p, p + 1, p + 2, p + 3]
+    want = [1 + t for t in tok_h0] + [1 + n + 2, 1 + n + 4] + [sentinel] * (64 - 12)
+    assert kv0.tolist() == [float(x) for x in want], kv0[:20]
+    assert (vf[:, 0].float().cpu().numpy()[:12] == np.array(want[:12]) + 100).all()
+    log("  budgets past the offsets: rows past the span of sel unwritten, nothing past the flat buffer")
+
+
+def test_online_compact_budgets_past_offsets(gpu_lib):
+    """adakv_lava_online_compact given a layer whose budgets sum past its span
+    of sel and a previous segment start past the previous cache's rows (never
+    outputs of the library): those rows are left unwritten, every other row
+    is the right one.  The previous cache has 64 rows, so even unchecked reads
+    would stay inside it; max_rows is 24."""
+    hkv, w, n, d = 2, 2, 20, 128
+    p = n - w
+    shape = lib.AdakvShape(n_inst=2, hq=hkv, hkv=hkv, d=d, n=n, w=w, pool=1, dtype=lib.ADAKV_BF16,
+                           scorer=lib.ADAKV_SCORE_LAVA, hidden=0, eps=0.0, reserved0=0)
+    dev = "cuda"
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)   # noqa: E731
+    i64 = lambda x: torch.tensor(x, dtype=torch.int64, device=dev)   # noqa: E731
+    # every value below 256, so exact in bf16
+    k_old, v_old = _rows_bf16(64, d, 1), _rows_bf16(64, d, 65)
+    k_new = _rows_bf16(hkv * n, d, 129).reshape(hkv, n, d)
+    v_new = _rows_bf16(hkv * n, d, 169).reshape(hkv, n, d)
+    sel_old, sel_off_old = i32([1, 5, 9, 2, 4, 6] + [0] * 10), i64([0, 6])
+    seg_start_old = i64([0, 5, 30])        # head 1's true end is 10
+    budgets = i32([2, 3, 3, 3])             # layer 0 sums to 5 over a span of 4
+    sel_off = i64([0, 4, 10])
+    sel = i32([1, 9, 4, 6, 0, 3, 7, 1, 2, 8] + [0] * 6)
+    sentinel = -7.0
+    kf = torch.full((24, d), sentinel, dtype=torch.bfloat16, device=dev)
+    vf = torch.full((24, d), sentinel, dtype=torch.bfloat16, device=dev)
+    seg_start = torch.empty(2 * hkv + 1, dtype=torch.int64, device=dev)
+    seg_len = torch.empty(2 * hkv, dtype=torch.int32, device=dev)
+    lib.adakv_lava_online_compact(shape, k_new, v_new, k_old, v_old, seg_start_old, sel_old, sel_off_old, budgets,
+                                  sel, sel_off, 24, kf, vf, seg_start, seg_len)
+    torch.cuda.synchronize()
+    assert seg_start.tolist() == [0, 4, 9, 14, 19]
+    old_row = lambda r: 1 + r                        # noqa: E731
+    new_row = lambda g, t: 129 + g * n + t           # noqa: E731
+    want = ([old_row(r) for r in (0, 2, 3, 4)] + [old_row(6), old_row(7)] + [sentinel] * 3 +
+            [new_row(0, t) for t in (0, 3, 7, p, p + 1)] + [new_row(1, t) for t in (1, 2, 8, p, p + 1)] +
+            [sentinel] * 5)
+    got = kf[:, 0].float().cpu().numpy()
+    assert got.tolist() == [float(x) for x in want], got
+    gv = vf[:, 0].float().cpu().numpy()
+    for r, x in enumerate(want):
+        if x != sentinel:
+            assert gv[r] == x + (64 if x < 129 else 40), (r, gv[r], x)
+    log("  online compact: a layer's budgets past its span and a previous segment past the previous cache skipped")
