@@ -1272,3 +1272,83 @@ def test_online_compact_budgets_past_offsets(gpu_lib):
         if x != sentinel:
             assert gv[r] == x + (64 if x < 129 else 40), (r, gv[r], x)
     log("  online compact: a layer's budgets past its span and a previous segment past the previous cache skipped")
+
+
+# ------------------------------------------------------------------ LAVa selection on given scores: head counts and ragged rows
+def _lava_scores(rng, L, hkv, p, grid):
+    """Scores on a grid of `grid` + 1 values in [0, 1] (ties across every
+    threshold, zeros), one layer with its mass on a few entries."""
+    s = rng.integers(0, grid + 1, size=(L, hkv, p)).astype(np.float64) / grid
+    s[L // 2] = 1e-6
+    s[L // 2, 0, 1:4] = 1.0
+    return s.astype(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("L,hkv,p", [(40, 1, 301), (5, 3, 1003), (3, 16, 257)])
+def test_lava_allocate_given_scores(gpu_lib, L, hkv, p):
+    """The offline LAVa allocation through the C ABI alone (no scorer) on
+    crafted scores, against the oracle: one KV head, an odd head count and
+    row length (scalar score loads), many heads per layer."""
+    rng = np.random.default_rng(L * 1000 + hkv * 10 + p)
+    w = 32
+    s = _lava_scores(rng, L, hkv, p, 16)
+    total = L * w * hkv + min(hkv * p, (L * hkv * p) // 7)
+    shape = lib.AdakvShape(n_inst=L, hq=hkv, hkv=hkv, d=128, n=p + w, w=w, pool=1, dtype=lib.ADAKV_BF16,
+                           scorer=lib.ADAKV_SCORE_LAVA, hidden=0, eps=0.0, reserved0=0)
+    alloc = lib.AdakvAlloc(mode=lib.ADAKV_ALLOC_LAVA_LAYERS, alpha_num=0, alpha_den=1, ck_num=0, ck_den=1, sinks=0,
+                           budget=total)
+    score = torch.from_numpy(s.astype(np.float32)).cuda()
+    ws = torch.empty(lib.adakv_workspace_bytes(shape, alloc, 0), dtype=torch.uint8, device="cuda")
+    Bp = total - L * w * hkv
+    budgets = torch.empty(L * hkv, dtype=torch.int32, device="cuda")
+    sel = torch.empty(max(Bp, 4), dtype=torch.int32, device="cuda")
+    sel_off = torch.empty(L + 1, dtype=torch.int64, device="cuda")
+    lib.adakv_allocate(shape, alloc, score, None, budgets, sel, sel_off, ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0
+    b = budgets.cpu().numpy().reshape(L, hkv)
+    off = sel_off.cpu().numpy()
+    hs = sel[:Bp].cpu().numpy()
+    ref = allocation.lava_allocate(s, total, w)
+    lb = np.diff(off)
+    if not check_lava_layer_budgets(lb, ref["layer_budgets"], ref["entropy"], Bp, f"L{L} hkv{hkv} p{p}"):
+        ref = allocation.lava_allocate(s, total, w, layer_budgets=lb)
+    for l in range(L):
+        pos, heads = int(off[l]), []
+        for g in range(hkv):
+            heads.append(hs[pos:pos + int(b[l, g])])
+            pos += int(b[l, g])
+        check_selection(b[l], int(off[l]), heads, ref["budgets"][l], ref["sel"][l], f"L{L} hkv{hkv} p{p} layer {l}")
+    log(f"  LAVa L={L} hkv={hkv} p={p}: layer budgets {lb.tolist()[:8]}...; selections exact")
+
+
+@pytest.mark.parametrize("L,hkv,p", [(40, 1, 301), (6, 3, 1003)])
+def test_lava_online_allocate_head_counts(gpu_lib, L, hkv, p):
+    """The online allocation on crafted scores with one KV head over 40 layers
+    (small older sets, a low-entropy layer) and with three KV heads on odd
+    rows: both routes identical at every step and equal to the oracle."""
+    rng = np.random.default_rng(L * 7 + hkv + p)
+    w = 32
+    s = _lava_scores(rng, L, hkv, p, 16)
+    total = L * w * hkv + min(hkv * p, 1500)
+    got_inc = _online_alloc_direct(s, total, w, True)
+    got_full = _online_alloc_direct(s, total, w, False)
+    prev_lb = np.zeros(0, dtype=np.int64)
+    for l in range(L):
+        (b, off, sel), (bf, offf, self_) = got_inc[l], got_full[l]
+        assert np.array_equal(b, bf) and np.array_equal(off, offf) and np.array_equal(sel, self_), \
+            f"step {l}: the two routes differ"
+        ref = allocation.lava_online_step(s[:l + 1], total, w, prev_lb)
+        lb = np.diff(off)
+        if not check_lava_layer_budgets(lb, ref["layer_budgets"], ref["entropy"], ref["Bp"], f"step {l}",
+                                        same_sum=False):
+            rb, rsel = allocation.layer_top_select(s[:l + 1], lb)
+            ref = {"budgets": rb, "sel": rsel}
+        for j in range(l + 1):
+            pos, heads = int(off[j]), []
+            for g in range(hkv):
+                heads.append(sel[pos:pos + int(b[j, g])])
+                pos += int(b[j, g])
+            check_selection(b[j], int(off[j]), heads, ref["budgets"][j], ref["sel"][j], f"step {l} layer {j}")
+        prev_lb = lb
+    log(f"  online L={L} hkv={hkv} p={p}: {L} steps, both routes and the oracle agree")
