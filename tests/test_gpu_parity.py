@@ -1352,3 +1352,43 @@ def test_lava_online_allocate_head_counts(gpu_lib, L, hkv, p):
             check_selection(b[j], int(off[j]), heads, ref["budgets"][j], ref["sel"][j], f"step {l} layer {j}")
         prev_lb = lb
     log(f"  online L={L} hkv={hkv} p={p}: {L} steps, both routes and the oracle agree")
+
+
+@pytest.mark.parametrize("I,hkv,p,frac,alpha", [(4, 2, 3000, 0.3, (1, 5)), (3, 8, 5000, 0.2, (1, 5)),
+                                                (2, 3, 20001, 0.1, (4, 5)), (1, 16, 40000, 0.05, (1, 5))])
+def test_ada_allocate_given_scores(gpu_lib, I, hkv, p, frac, alpha):
+    """The Ada-KV allocation through the C ABI alone on scores from a grid of
+    17 values (ties at the layer threshold shared across heads in head order,
+    ties inside each head), on each route: one workgroup per instance (4x2x3000),
+    the one-launch head top-k (8x5000, 3x20001 with odd rows), and rows longer
+    than 32768 on the chunked per-row passes (16x40000)."""
+    rng = np.random.default_rng(I * 100003 + hkv * 101 + p)
+    w = 32
+    s = (rng.integers(0, 17, size=(I, hkv, p)).astype(np.float64) / 16.0).astype(np.float32)
+    s[:, 0] *= np.float32(0.25)             # one sparse head per instance (the safeguard matters)
+    P = int(frac * hkv * p)
+    budget = w * hkv + P
+    shape = lib.AdakvShape(n_inst=I, hq=hkv, hkv=hkv, d=128, n=p + w, w=w, pool=1, dtype=lib.ADAKV_BF16,
+                           scorer=lib.ADAKV_SCORE_SNAPKV, hidden=0, eps=0.0, reserved0=0)
+    alloc = lib.AdakvAlloc(mode=lib.ADAKV_ALLOC_ADA, alpha_num=alpha[0], alpha_den=alpha[1], ck_num=0, ck_den=1,
+                           sinks=0, budget=budget)
+    score = torch.from_numpy(s).cuda()
+    ws = torch.empty(lib.adakv_workspace_bytes(shape, alloc, 0), dtype=torch.uint8, device="cuda")
+    budgets = torch.empty(I * hkv, dtype=torch.int32, device="cuda")
+    sel = torch.empty(I * P, dtype=torch.int32, device="cuda")
+    sel_off = torch.empty(I + 1, dtype=torch.int64, device="cuda")
+    lib.adakv_allocate(shape, alloc, score, None, budgets, sel, sel_off, ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0
+    b = budgets.cpu().numpy().reshape(I, hkv)
+    off = sel_off.cpu().numpy()
+    hs = sel.cpu().numpy()
+    assert off.tolist() == [i * P for i in range(I + 1)]
+    for i in range(I):
+        r = allocation.ada_allocate(s[i].astype(np.float64), budget, w, alpha)
+        pos, heads = int(off[i]), []
+        for g in range(hkv):
+            heads.append(hs[pos:pos + int(b[i, g])])
+            pos += int(b[i, g])
+        check_selection(b[i], int(off[i]), heads, r["budgets"], r["sel"], f"ada {I}x{hkv}x{p} instance {i}")
+    log(f"  Ada-KV {I}x{hkv}x{p} alpha {alpha}: budgets {b[0].tolist()[:8]}; selections exact")
