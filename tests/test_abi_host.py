@@ -286,3 +286,28 @@ def test_floor_and_streaming_rejects(L):
     assert st == lib.ADAKV_EINVAL
     assert lib.adakv_workspace_bytes(s, _alloc(mode=lib.ADAKV_ALLOC_ADA_FLOOR), 0) > \
         lib.adakv_workspace_bytes(s, _alloc(mode=lib.ADAKV_ALLOC_ADA), 0) - 1
+
+
+def online_status(L, shape, total, layer_ent=FAKE, prev_budgets=FAKE, prev_sel=FAKE, prev_off=FAKE,
+                  ws_bytes=1 << 40):
+    return L.adakv_lava_online_allocate(ctypes.byref(shape), total, FAKE, prev_off, prev_budgets, prev_sel,
+                                        layer_ent, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_lava_online_allocate_rejects(L):
+    """The online allocation's own arguments: the per-layer entropy array is
+    required and 8-byte aligned, the previous budgets and selection come
+    together and aligned, the previous offsets are aligned, the windows fit
+    the total, and the workspace is large enough (every case is refused before
+    anything is launched)."""
+    s = _shape(n_inst=2, scorer=lib.ADAKV_SCORE_LAVA)
+    total = 2 * s.w * s.hkv + 500
+    assert online_status(L, s, total, layer_ent=None) == lib.ADAKV_EINVAL
+    assert online_status(L, s, total, layer_ent=FAKE + 4) == lib.ADAKV_EINVAL
+    assert online_status(L, s, total, prev_sel=None) == lib.ADAKV_EINVAL
+    assert online_status(L, s, total, prev_budgets=None) == lib.ADAKV_EINVAL
+    assert online_status(L, s, total, prev_sel=FAKE + 4) == lib.ADAKV_EINVAL
+    assert online_status(L, s, total, prev_budgets=FAKE + 8) == lib.ADAKV_EINVAL
+    assert online_status(L, s, total, prev_off=FAKE + 8) == lib.ADAKV_EINVAL
+    assert online_status(L, s, 2 * s.w * s.hkv - 1) == lib.ADAKV_EINVAL
+    assert online_status(L, s, total, ws_bytes=16) == lib.ADAKV_EWORKSPACE
