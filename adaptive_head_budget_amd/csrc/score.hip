@@ -156,6 +156,41 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2)
   m = M;
 }
 
+// The partial row statistics of a launch merged once per window row: part
+// holds nsub (max, sum) pairs per row, [instance][KV head][partial][G*w];
+// merged gets one per row, [instance][KV head][G*w], formed in partial order.
+// Calls that split a head over many chunks (one long instance) run it before
+// pass 2, whose every workgroup would otherwise merge all nsub pairs of its
+// rows in its prologue.
+constexpr int MERGE_MIN = 64;   // partials per row above which the merge runs on its own
+// One wave per row: lane L merges partials L, L+64, ... in order, then a
+// butterfly over the 64 lanes (a fixed order, the same on every run).
+__global__ __launch_bounds__(256) void merge_part_kernel(const float2* __restrict__ part, float2* __restrict__ merged,
+                                                         int rows, int Gw, int nsub) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= rows) return;                          // uniform across the wave
+  const int head = t / Gw, j = t - head * Gw;
+  const float2* pr = part + (size_t)head * nsub * Gw + j;
+  float m = -INFINITY, l = 0.f;
+  for (int c0 = lane; c0 < nsub; c0 += 4 * WAVE) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * WAVE;
+      v[u] = c < nsub ? pr[(size_t)c * Gw] : make_float2(-INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) merge_ml(m, l, v[u].x, v[u].y);
+  }
+#pragma unroll
+  for (int mask = 1; mask < WAVE; mask <<= 1) {
+    const float om = shfl_xor(m, mask), ol = shfl_xor(l, mask);
+    merge_ml(m, l, om, ol);
+  }
+  if (lane == 0) merged[t] = make_float2(m, l);
+}
+
 // Sum 32 per-lane values across the 16 lanes of a lane group (lanes sharing
 // lane/16); afterwards lane c of the group holds the totals of entries 2c, 2c+1.
 // A butterfly of four DPP involutions (mirror, half mirror, quad ^2, quad ^1):
@@ -1381,7 +1416,7 @@ struct ScorePlan {
   int ib;        // instances per batch
   int nchunk;    // stats chunks per head
   int kend;      // end of the widest row domain
-  size_t off_part, off_heads, off_vbar, off_fac, off_smax, total;
+  size_t off_part, off_heads, off_vbar, off_fac, off_smax, off_pmerge, total;
 };
 
 ScorePlan plan_score(const Geo& g) {
@@ -1409,6 +1444,8 @@ ScorePlan plan_score(const Geo& g) {
   P.off_smax = off;   // LAVa on the register-K path: unpooled group maxima of a batch
   if (g.scorer == ADAKV_SCORE_LAVA && kr_geometry(g))
     off = align_up(off + (size_t)P.ib * g.hkv * lava_keys(g) * sizeof(float), 256);
+  P.off_pmerge = off;   // one merged (max, sum) pair per window row of a batch
+  off = align_up(off + (size_t)P.ib * g.hkv * Gw * sizeof(float2), 256);
   P.total = off;
   return P;
 }
@@ -1504,6 +1541,18 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
     else
       score_stats_kernel<T, D, NB, false><<<g1, threads, lds_stats, st>>>(qt, kt, part, i0, g.hq, g.hkv, g.G, g.n,
                                                                           g.w, g.p, P.kend, nchunk, kpw, c2);
+    // pass 2 reads one merged (max, sum) pair per row where a head's keys
+    // were split over many chunks (a long instance alone in its batch)
+    const float2* part_e = part;
+    int nsub_e = nchunk;
+    if (row_lse == nullptr && nchunk > MERGE_MIN) {
+      float2* pm = reinterpret_cast<float2*>(ws + P.off_pmerge);
+      const int Gw = g.G * g.w;
+      const int rows = ni * g.hkv * Gw;
+      merge_part_kernel<<<(rows + 3) / 4, 256, 0, st>>>(part, pm, rows, Gw, nchunk);
+      part_e = pm;
+      nsub_e = 1;
+    }
     const long tiles_total = (long)ntiles * g.hkv * ni;
     int tpw = (int)std::max<long>(1, (tiles_total + target - 1) / target);
     if (tpw > ntiles) tpw = ntiles;
@@ -1512,17 +1561,17 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
   do {                                                                                                       \
     if (lava)                                                                                                \
       score_emit_kernel<T, D, NB, POOLV, EMIT_LAVA><<<g2, threads, lds_emit, st>>>(                          \
-          qt, kt, part, row_lse, vpart, nvblk, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
+          qt, kt, part_e, row_lse, vpart, nvblk, score, nullptr, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nsub_e, tpw, c2);              \
     else                                                                                                     \
       score_emit_kernel<T, D, NB, POOLV, EMIT_SNAP><<<g2, threads, lds_emit, st>>>(                          \
-          qt, kt, part, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);              \
+          qt, kt, part_e, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nsub_e, tpw, c2);              \
   } while (0)
     if (krl != nullptr) {
       float* smax = reinterpret_cast<float*>(ws + P.off_smax);
       const int kpw_l = kr_keys_per_wg((long)((ke + KB - 1) / KB) * g.hkv * ni, krl_res, KR_WAVES * KB);
       krl<<<dim3((ke + kpw_l - 1) / kpw_l, g.hkv, ni), KR_WAVES * WAVE, kr_lds_e, st>>>(
-          reinterpret_cast<const uint16_t*>(qt), reinterpret_cast<const uint16_t*>(kt), part, row_lse, smax, i0,
-          g.hq, g.hkv, g.n, g.w, g.p, ke, nchunk, kpw_l, c2);
+          reinterpret_cast<const uint16_t*>(qt), reinterpret_cast<const uint16_t*>(kt), part_e, row_lse, smax, i0,
+          g.hq, g.hkv, g.n, g.w, g.p, ke, nsub_e, kpw_l, c2);
       const dim3 gp((g.p + LP_KEYS - 1) / LP_KEYS, g.hkv, ni);
       switch (g.pool) {
         case 1: lava_pool_kernel<0><<<gp, 256, 0, st>>>(smax, vpart, nvblk, score, i0, g.hkv, g.p, ke, g.w); break;
@@ -1533,12 +1582,12 @@ hipError_t run_score(const Geo& g, const ScorePlan& P, const void* q, const void
     } else if (kre != nullptr && heads == nullptr) {
       const int kpw_e = kr_keys_per_wg((long)((g.p + KB - 1) / KB) * g.hkv * ni, kre_res, KR_WAVES * KB);
       kre<<<dim3((g.p + kpw_e - 1) / kpw_e, g.hkv, ni), KR_WAVES * WAVE, kr_lds_e, st>>>(
-          reinterpret_cast<const uint16_t*>(qt), reinterpret_cast<const uint16_t*>(kt), part, row_lse, score, i0,
-          g.hq, g.hkv, g.n, g.w, g.p, nchunk, kpw_e, c2);
+          reinterpret_cast<const uint16_t*>(qt), reinterpret_cast<const uint16_t*>(kt), part_e, row_lse, score, i0,
+          g.hq, g.hkv, g.n, g.w, g.p, nsub_e, kpw_e, c2);
     } else if (laprox) {
       if constexpr (sizeof(T) == 2 && D == 128)   // the only LaProx geometry the ABI accepts
         score_emit_kernel<T, D, NB, 1, EMIT_SQ><<<g2, threads, lds_emit, st>>>(
-            qt, kt, part, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nchunk, tpw, c2);
+            qt, kt, part_e, row_lse, vpart, nvblk, score, heads, i0, g.hq, g.hkv, g.G, g.n, g.w, g.p, nsub_e, tpw, c2);
       else
         return hipErrorInvalidValue;
     } else switch (g.pool) {
