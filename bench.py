@@ -186,7 +186,11 @@ def cpu_baseline(cfg, target_s: float = 10.0):
         return time.perf_counter() - t0, kh, vh
 
     spent, done, dec_s = 0.0, 0, 0.0
+    last = time.perf_counter()
     while done < cfg.instances and (done == 0 or spent < target_s):
+        if time.perf_counter() - last > 20.0:
+            print(f"[bench] oracle: {done} of {cfg.instances} instances, {spent:.1f} s", file=sys.stderr, flush=True)
+            last = time.perf_counter()
         inst = synth.make_instance(cfg, done)
         dt_s, kh, vh = evict_one(inst)
         spent += dt_s
@@ -254,6 +258,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama3.1-8b_32L_b4_n32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0,
+                    help="oracle work timed for cpu_baseline before it stops (a large value: every instance)")
     ap.add_argument("--row-lse", action="store_true",
                     help="score with adakv_score_lse: the window rows' log-sum-exp is supplied (prepared before "
                          "timing), so the keys are read once")
@@ -461,7 +467,7 @@ def main():
         out["measured_peaks"] = measured
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_baseline_seconds)
     print(json.dumps(out), flush=True)
 
 
