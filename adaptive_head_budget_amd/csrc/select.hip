@@ -595,7 +595,7 @@ __global__ __launch_bounds__(SB) void lava_budget_kernel(const double* __restric
 }
 
 // ---------------------------------------------------------------- layer counts and budgets
-enum { MODE_ADA = 0, MODE_LAVA = 1, MODE_CK = 2 };
+enum { MODE_ADA = 0, MODE_CK = 2 };   // the row budget kernel's two kinds of row
 
 // Per row: entries above its segment's threshold T and equal to it (a segment
 // is seg_rows consecutive rows: one instance, or every row of the call).  With
@@ -647,15 +647,14 @@ __global__ __launch_bounds__(SB) void layer_count_kernel(const float* __restrict
   }
 }
 
-// One workgroup per row r (head g of instance i).  From the counts of the
-// instance's rows: the heads' layer counts f_g (ties shared out in flat index
-// order), then
-//  * Ada-KV / CriticalKV: the budget B_g by the safeguard, the row's offset in
-//    sel, the row's k for its own top-k (B_g, or b'_g = floor(B_g * ck_num /
-//    ck_den) for CriticalKV stage 1, b''_g = B_g - b'_g kept for stage 2) and
-//    the first digit pick of that top-k from the row's pass-0 histogram;
-//  * LAVa: B_g = f_g; the row keeps the layer threshold with its share of the ties.
-// Every workgroup of an instance computes the same head values.
+// One workgroup per row r (head g of instance i), Ada-KV and CriticalKV.  From
+// the counts of the instance's rows: the heads' layer counts f_g (ties shared
+// out in flat index order), the budget B_g by the safeguard, the row's offset
+// in sel, the row's k for its own top-k (B_g, or b'_g = floor(B_g * ck_num /
+// ck_den) for CriticalKV stage 1, b''_g = B_g - b'_g kept for stage 2) and the
+// first digit pick of that top-k from the row's pass-0 histogram.  (LAVa rows
+// keep the layer threshold: lava_emit_kernel forms their budgets.)  Every
+// workgroup of an instance computes the same head values.
 __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int kP0, int alpha_num, int alpha_den,
                                                         int ck_num, int ck_den, int n_inst,
                                                         const int64_t* __restrict__ klist,
@@ -687,22 +686,9 @@ __global__ __launch_bounds__(SB) void row_budget_kernel(int hkv, int mode, int k
       share = share < 0 ? 0 : (share > eq_sh[j] ? eq_sh[j] : share);
       before += eq_sh[j];
       f_sh[j] = gt_sh[j] + share;
-      q_sh[j] = share;
     }
   }
   __syncthreads();
-  if (mode == MODE_LAVA) {
-    if (threadIdx.x == 0) {
-      int64_t base = sel_off[inst];
-      for (int j = 0; j < g; ++j) base += f_sh[j];
-      budgets[r] = (int32_t)f_sh[g];
-      rowbase[r] = base;
-      RState x = {L.prefix, (int32_t)q_sh[g]};
-      if (L.prefix == NONE) { x.prefix = NONE; x.krem = 0; }
-      rowst[r] = x;
-    }
-    return;
-  }
   // Safeguard in exact integers: N_g = a*h*f_g + (b-a)*P over Den = b*h, floors
   // plus one unit to the P - sum(floor) largest remainders (lower head first).
   const int64_t a = alpha_num, b = alpha_den, h = hkv;
@@ -1732,7 +1718,7 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   const int nc = P.nchunk, cpr = P.cpr, nt = P.ntile, hkv = g.hkv, R = P.R;
   const bool lava = a.mode == ADAKV_ALLOC_LAVA_LAYERS;
   const bool ck = a.mode == ADAKV_ALLOC_ADA_CRITICALKV;
-  const int mode = lava ? MODE_LAVA : (ck ? MODE_CK : MODE_ADA);
+  const int mode = ck ? MODE_CK : MODE_ADA;
   const bool preset = a.inst_budget != nullptr;   // per-instance budgets (Ada-KV mode only)
   const int kP = (lava || preset) ? 0 : (int)(a.budget - (int64_t)g.w * g.hkv);
   int64_t sel_total = lava ? a.budget - (int64_t)g.I * g.w * g.hkv : (int64_t)g.I * kP;
