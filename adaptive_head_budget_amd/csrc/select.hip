@@ -1495,6 +1495,10 @@ __global__ __launch_bounds__(XB) void row_topk_kernel(const float* __restrict__ 
 // most RT_MAX entries in all; indices and counts read here are clamped into
 // range all the same.
 constexpr int RS_MAXH = 256;              // KV heads of a layer on this route
+// Each older layer is re-selected by one workgroup, so while the older layers
+// keep more than this many entries each on average, the layer-wide chain over
+// their full scores (spread over the chip) is the faster route.
+constexpr int64_t RS_AVG_MAX = 8192;
 
 __device__ __forceinline__ int rs_head_of(const int32_t* hstart, int hkv, int e) {
   // the last head whose first entry is at most e (hstart[0] = 0)
@@ -1813,9 +1817,11 @@ hipError_t launch_allocate(const Geo& g, const adakv_alloc& a, const float* scor
   const int64_t Bp_lava = lava ? a.budget - (int64_t)g.I * g.w * g.hkv : 0;
   const size_t sm_lava = (size_t)g.I * (sizeof(double) + sizeof(int64_t));
   if (lava && online && g.I > 1 && prev_budgets != nullptr && prev_sel != nullptr && hkv <= RS_MAXH &&
-      a.budget - (int64_t)(g.I - 1) * g.w * hkv <= RT_MAX) {
+      a.budget - (int64_t)(g.I - 1) * g.w * hkv <= RT_MAX &&
+      a.budget - (int64_t)(g.I - 1) * g.w * hkv <= RS_AVG_MAX * (g.I - 1)) {
     // Incremental step: the older layers kept at most RT_MAX entries in all at
-    // the previous step, and their new selections lie inside those.  The
+    // the previous step (at most RS_AVG_MAX each on average), and their new
+    // selections lie inside those.  The
     // newest layer runs the layer-wide chain on its own rows (same chunking
     // as the whole call, so its entropy sums are the ones the full route
     // forms); every older layer is re-selected from its previous entries.

@@ -319,9 +319,9 @@ adakv_status adakv_compact(const adakv_shape* shape, const adakv_alloc* alloc, c
  * B_j of its previous kept entries (same order, same scores): given the
  * previous step's budgets and sel, each older layer is re-selected from those
  * entries and only the newest layer's full scores are read (taken when the
- * previous step's older layers kept at most 32768 entries in all and hkv <=
- * 256; otherwise every layer is re-selected from its full scores).  Both
- * routes give the same outputs.
+ * previous step's older layers kept at most 32768 entries in all, at most 8192
+ * each on average, and hkv <= 256; otherwise every layer is re-selected from
+ * its full scores).  Both routes give the same outputs.
  *
  *   shape.n_inst  I = layers prefilled so far; scorer/pool as for the scores
  *   score         [I, hkv, p] float32, the LAVa scores of layers 0..I-1 (each

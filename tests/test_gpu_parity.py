@@ -913,14 +913,19 @@ def test_lava_online_prefill_caps(gpu_lib):
 
 
 def test_lava_online_route_switch(gpu_lib):
-    """The older layers' previous entries exceed 32768 at step 1 (every layer
-    re-selected from its full scores) and fit at step 2 (re-selected from
-    the previous entries); layer 0 keeps 32,944 entries after step 0."""
-    cfg = scaled(configs.MISTRAL7B_LAVA, layers=3, name="lava_online_switch")
+    """Both bounds of the incremental route: at step 1 the older layer's
+    previous entries exceed 32768 in all (layer 0 keeps 32,944 after step 0),
+    at steps 2 and 3 they fit but average more than 8192 per older layer, so
+    every layer is re-selected from its full scores; from step 4 on they are
+    re-selected from their previous entries."""
+    cfg = scaled(configs.MISTRAL7B_LAVA, layers=6, name="lava_online_switch")
     n = 5032
-    total = 33200            # B'(0) = 32944, B'(1) = 32688 (hkv = 8, w = 32)
-    assert total - 1 * 32 * 8 > 32768 >= total - 2 * 32 * 8
-    run_online(cfg, n, total, "lava online route switch L3 n5032")
+    total = 33200            # B'(l) = 33200 - (l + 1) * 256 (hkv = 8, w = 32)
+    bprev = lambda I: total - (I - 1) * 32 * 8          # noqa: E731
+    assert bprev(2) > 32768
+    assert all(bprev(I) > 8192 * (I - 1) for I in (3, 4))
+    assert all(bprev(I) <= min(32768, 8192 * (I - 1)) for I in (5, 6))
+    run_online(cfg, n, total, "lava online route switch L6 n5032")
 
 
 def _online_alloc_direct(score_np, total, w, incremental):
